@@ -1,0 +1,409 @@
+"""CPU oracle of the online MR-GPTQ-style FP4 path.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run this module. The
+product (the HIP library and its Python binding) never does. The oracle and
+the HIP path share no code; only the seeded input generators feed both.
+
+It is plain, slow and written to be checked against the pages by eye: NumPy
+only, float64 wherever the pages leave the precision open, float32 where a
+step is defined in float32 (the rotation and the NVFP4 element step).
+
+Pages (cited by title and section):
+
+* [BRIDGE-de]  "Bridging the Gap Between Promise and Performance for
+  Microscaling FP4 Quantization" (gist.science, German),
+  "Technische Zusammenfassung": §1 Problemstellung; §2 Methodik und Analyse
+  ("Theoretische Analyse der Fehler", "Einführung von MR-GPTQ",
+  "GPU-Kernel-Unterstützung (QuTLASS)").
+* [BRIDGE-en]  the same paper on chatpaper.ai, English abstract.
+* [BRIDGE-es]  the same paper (gist.science, Spanish), "Resumen técnico":
+  §2 Metodología (A. Análisis de Error, B. MR-GPTQ, C. QuTLASS).
+* [UNVEIL-nl]  "Unveiling the Potential of Quantization with MXFP4:
+  Strategies for Quantization Error Reduction" (gist.science, Dutch),
+  "Technische samenvatting": Probleemstelling; Methodologie
+  (1. Overflow-Aware Scaling).
+* [TORQ-de]    "TORQ: Two-Level Orthogonal Rotation for MXFP4 Quantization"
+  (gist.science, German), "Technische Zusammenfassung": 1. Problemstellung.
+
+What the method computes, step by step (the online path):
+
+1. widen bf16 X to float32 (exact);
+2. rotate each row by a block-diagonal Hadamard matrix, blocks of ``b``
+   along K, applied to weights and activations alike ([BRIDGE-de] §2
+   "Einführung von MR-GPTQ", item 1; [BRIDGE-es] §2.B item 1);
+3. per group of 32 (MXFP4) or 16 (NVFP4) elements take the absolute maximum
+   and derive the shared scale ([BRIDGE-de] §1; [UNVEIL-nl] Probleemstelling);
+4. round every element to nearest onto the E2M1 grid (RTN, [BRIDGE-de] §2
+   "Theoretische Analyse der Fehler"; E2M1 codebook [TORQ-de] 1.);
+5. pack two 4-bit codes per byte;
+6. multiply the dequantized operands: Y = dq(Xq) dq(Wq)^T ([BRIDGE-de] §2
+   "GPU-Kernel-Unterstützung (QuTLASS)", 4-bit matmul).
+
+Readings taken where the pages are silent (each is listed in the design doc):
+
+R1  Blocks and groups are contiguous and aligned from k = 0; the Hadamard
+    block b and the scale group g are independent (b in {16,32,64,128}).
+R2  The Hadamard matrix is the plain Sylvester one, H[i,j] = (-1)^popcount(i&j),
+    normalised by 1/sqrt(b) so that the rotation is orthogonal.
+R3  The rotation is computed in float32 as the fast Walsh-Hadamard transform in
+    ascending stride order (h = 1, 2, 4, ..., b/2; pair (i, i+h) with bit h of i
+    clear -> (x_i + x_{i+h}, x_i - x_{i+h})), then one float32 multiply by
+    c_b = fl32(1/sqrt(b)). Fixing this order makes the float32 result unique.
+R4  MXFP4 scale: the smallest power of two 2^e with alpha_max <= 6 * 2^e, so
+    that the block maximum lands in (3, 6] ([UNVEIL-nl] Methodologie, 1. OAS,
+    which describes this mapping as the standard MXFP4 one). E8M0 code e + 127,
+    e clamped to [-127, 127]; an all-zero group gets code 0.
+R5  NVFP4 tensor scale s_t = fl32(T / (6 * 448)) with T the absolute maximum of
+    the whole rotated tensor, recomputed on every call ([BRIDGE-es] §2.B item 2
+    speaks of group and tensor scales). The E4M3 group code is the nearest
+    E4M3FN value to alpha_max / (6 s_t) (ties to even, saturating at 448),
+    decided exactly. s_t == 0 makes the whole tensor zero.
+R6  NVFP4 element step in float32, as the kernel computes it:
+    S = fl32(d * s_t), R = fl32(1 / S), u = fl32(y * R); a group with
+    S < 2^-126 (including d == 0) is all signed zeros.
+R7  E2M1 rounding is round-to-nearest, ties to the even code, saturating at
+    +-6, keeping the sign of the input (so -0 and small negatives give 0x8).
+    Codes: bit 3 = sign, bits 2..0 index {0, .5, 1, 1.5, 2, 3, 4, 6}.
+R8  Packing: byte j of a row holds element 2j in its low nibble and element
+    2j+1 in its high nibble; scales are row-major [rows, K/g].
+R9  The GEMM reference is the exact product of the dequantized operands,
+    formed in float64: Y64 = dq(Xq) @ dq(Wq)^T, no bias.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "E2M1_MAGNITUDES",
+    "E4M3_MAX",
+    "NV_TENSOR_DIVISOR",
+    "widen_bf16",
+    "sylvester_hadamard",
+    "hadamard_constant",
+    "rotate_fwht_f32",
+    "rotate_exact_f64",
+    "e2m1_rne",
+    "e2m1_value",
+    "e4m3_value",
+    "e4m3_rne_sat",
+    "mx_shared_exponent",
+    "quantize_mxfp4",
+    "quantize_nvfp4",
+    "pack_nibbles",
+    "unpack_nibbles",
+    "rotate_quantize",
+    "dequantize",
+    "linear_f64",
+    "bf16_rne_f64",
+    "near_boundary_flags",
+]
+
+# E2M1 magnitudes indexed by the 3 low bits of a code ([TORQ-de] 1.: the
+# geometrically progressive e2m1 codebook; [UNVEIL-nl] OAS: formal limit 6.0).
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+_E2M1_MIDPOINTS = (E2M1_MAGNITUDES[:-1] + E2M1_MAGNITUDES[1:]) / 2.0  # 7 rounding boundaries
+
+E2M1_MAX = 6.0
+E4M3_MAX = 448.0
+NV_TENSOR_DIVISOR = E2M1_MAX * E4M3_MAX  # 2688: maps T onto the largest (E4M3 x E2M1) product
+
+MX_GROUP = 32  # [BRIDGE-de] §1: 32 elements share one scale in MXFP4
+NV_GROUP = 16  # [BRIDGE-de] §1: 16 elements share one scale in NVFP4
+
+
+# --------------------------------------------------------------------------
+# step 1: bf16 -> float32
+# --------------------------------------------------------------------------
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float32, exactly (bf16 is the top half)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32)
+    return (b << np.uint32(16)).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# step 2: block-wise Hadamard rotation ([BRIDGE-de] §2 MR-GPTQ item 1)
+# --------------------------------------------------------------------------
+def sylvester_hadamard(b: int) -> np.ndarray:
+    """H_b[i, j] = (-1)^popcount(i & j) (reading R2), as int64 +-1."""
+    if b < 1 or b & (b - 1):
+        raise ValueError("Hadamard size must be a power of two")
+    i = np.arange(b)
+    pc = np.zeros((b, b), dtype=np.int64)
+    a = i[:, None] & i[None, :]
+    while np.any(a):
+        pc += a & 1
+        a = a >> 1
+    return np.where(pc % 2 == 0, 1, -1).astype(np.int64)
+
+
+def hadamard_constant(b: int) -> np.float32:
+    """c_b = fl32(1/sqrt(b)) (reading R3)."""
+    return np.float32(1.0 / np.sqrt(np.float64(b)))
+
+
+def rotate_fwht_f32(x32: np.ndarray, b: int) -> np.ndarray:
+    """Rotate rows by blocks of b along the last axis, in float32 (reading R3).
+
+    x32: float32 [..., K] with K % b == 0. Returns a new float32 array.
+    """
+    x32 = np.asarray(x32, dtype=np.float32)
+    K = x32.shape[-1]
+    if K % b:
+        raise ValueError("K must be a multiple of the Hadamard block")
+    v = np.array(x32, dtype=np.float32, copy=True).reshape(-1, b)
+    h = 1
+    while h < b:
+        w = v.reshape(v.shape[0], b // (2 * h), 2, h)
+        lo = w[:, :, 0, :].copy()  # x_i, bit h of i clear
+        hi = w[:, :, 1, :].copy()  # x_{i+h}
+        w[:, :, 0, :] = lo + hi
+        w[:, :, 1, :] = lo - hi
+        h *= 2
+    v = v * hadamard_constant(b)
+    return v.reshape(x32.shape)
+
+
+def rotate_exact_f64(x: np.ndarray, b: int) -> np.ndarray:
+    """The same rotation as a dense product in float64: y = (H_b x) / sqrt(b) per block."""
+    x = np.asarray(x, dtype=np.float64)
+    H = sylvester_hadamard(b).astype(np.float64)
+    v = x.reshape(-1, b) @ H.T / np.sqrt(np.float64(b))
+    return v.reshape(x.shape)
+
+
+# --------------------------------------------------------------------------
+# element formats
+# --------------------------------------------------------------------------
+def e2m1_rne(u: np.ndarray) -> np.ndarray:
+    """Round to the nearest E2M1 value, ties to the even code, saturate (reading R7).
+
+    u: float array (the element already divided by its scale). Returns uint8
+    codes 0..15 (bit 3 = sign of u).
+    """
+    u = np.asarray(u, dtype=np.float64)
+    mag = np.abs(u)
+    i = np.searchsorted(_E2M1_MIDPOINTS, mag, side="left")  # midpoints strictly below mag
+    at = np.minimum(i, len(_E2M1_MIDPOINTS) - 1)
+    tie = (i < len(_E2M1_MIDPOINTS)) & (mag == _E2M1_MIDPOINTS[at])
+    i = np.where(tie & (i % 2 == 1), i + 1, i)
+    sign = np.signbit(u).astype(np.int64)
+    return (i | (sign << 3)).astype(np.uint8)
+
+
+def e2m1_value(codes: np.ndarray) -> np.ndarray:
+    """Decode E2M1 codes (uint8 0..15) to float64."""
+    c = np.asarray(codes, dtype=np.uint8)
+    v = E2M1_MAGNITUDES[c & 7]
+    return np.where(c & 8, -v, v)
+
+
+def _e4m3_table() -> np.ndarray:
+    """Values of the finite non-negative E4M3FN codes 0x00..0x7E ([UNVEIL-nl]
+    Probleemstelling: 4 exponent bits, 3 mantissa bits; bias 7, subnormals,
+    no infinity, 0x7F is NaN)."""
+    vals = []
+    for c in range(0x7F):
+        e, m = c >> 3, c & 7
+        vals.append(m * 2.0 ** -9 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(vals, dtype=np.float64)
+
+
+_E4M3_VALUES = _e4m3_table()
+_E4M3_MIDPOINTS = (_E4M3_VALUES[:-1] + _E4M3_VALUES[1:]) / 2.0  # exact in float64
+
+
+def e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """Decode non-negative E4M3FN codes 0..126 to float64."""
+    c = np.asarray(codes, dtype=np.int64)
+    if np.any((c < 0) | (c > 0x7E)):
+        raise ValueError("E4M3 scale code out of the non-negative finite range")
+    return _E4M3_VALUES[c]
+
+
+def e4m3_rne_sat(q: np.ndarray) -> np.ndarray:
+    """Nearest non-negative E4M3FN code to q >= 0, ties to even, saturating at 448."""
+    q = np.asarray(q, dtype=np.float64)
+    if np.any(q < 0) or np.any(np.isnan(q)):
+        raise ValueError("E4M3 scale input must be a non-negative number")
+    i = np.searchsorted(_E4M3_MIDPOINTS, q, side="left")
+    at = np.minimum(i, len(_E4M3_MIDPOINTS) - 1)
+    tie = (i < len(_E4M3_MIDPOINTS)) & (q == _E4M3_MIDPOINTS[at])
+    i = np.where(tie & (i % 2 == 1), i + 1, i)
+    return np.minimum(i, 0x7E).astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
+# step 3-4, MXFP4 ([BRIDGE-de] §1: 32 elements, E8M0 power-of-two scale)
+# --------------------------------------------------------------------------
+def mx_shared_exponent(alpha_max: np.ndarray) -> np.ndarray:
+    """e = ceil(log2(alpha_max / 6)), clamped to [-127, 127]; 0 -> -127 (reading R4).
+
+    Written via frexp: alpha_max = f * 2^E with f in [0.5, 1); then
+    alpha_max / 2^(E-3) = 8f lies in [4, 6] when f <= 0.75, and
+    alpha_max / 2^(E-2) = 4f lies in (3, 4) when f > 0.75.
+    """
+    a = np.asarray(alpha_max, dtype=np.float64)
+    f, E = np.frexp(a)
+    e = E.astype(np.int64) - 3 + (f > 0.75)
+    e = np.where(a == 0, -127, e)
+    return np.clip(e, -127, 127)
+
+
+def quantize_mxfp4(y32: np.ndarray):
+    """MXFP4 codes and E8M0 scale codes of rotated float32 rows y32 [rows, K]."""
+    rows, K = y32.shape
+    grp = np.asarray(y32, dtype=np.float32).reshape(rows, K // MX_GROUP, MX_GROUP)
+    alpha_max = np.max(np.abs(grp), axis=2)  # exact
+    e = mx_shared_exponent(alpha_max)
+    # u = y / 2^e is exact (power-of-two scaling in float64)
+    u = grp.astype(np.float64) * np.ldexp(1.0, -e)[..., None]
+    codes = e2m1_rne(u).reshape(rows, K)
+    scales = (e + 127).astype(np.uint8)
+    return codes, scales
+
+
+# --------------------------------------------------------------------------
+# step 3-4, NVFP4 ([BRIDGE-de] §1: 16 elements; [UNVEIL-nl] E4M3 scale;
+# [BRIDGE-es] §2.B: group and tensor scales)
+# --------------------------------------------------------------------------
+def quantize_nvfp4(y32: np.ndarray, tensor_amax: np.float32 | None = None):
+    """NVFP4 codes, E4M3 scale codes and the float32 tensor scale (readings R5, R6).
+
+    tensor_amax: the absolute maximum over the whole rotated tensor; computed
+    from y32 when None (pass it in when y32 holds only some rows).
+    """
+    rows, K = y32.shape
+    y32 = np.asarray(y32, dtype=np.float32)
+    T = np.float32(np.max(np.abs(y32))) if tensor_amax is None else np.float32(tensor_amax)
+    s_t = np.float32(T / np.float32(NV_TENSOR_DIVISOR))  # float32 division, rounded once
+    grp = y32.reshape(rows, K // NV_GROUP, NV_GROUP)
+    alpha_max = np.max(np.abs(grp), axis=2)
+    if s_t == 0:
+        scales = np.zeros(alpha_max.shape, dtype=np.uint8)
+        codes = (np.signbit(grp).astype(np.uint8) << 3).reshape(rows, K)
+        return codes, scales, s_t
+    q = alpha_max.astype(np.float64) / (6.0 * np.float64(s_t))  # decided exactly (see R5)
+    scales = e4m3_rne_sat(q)
+    d = e4m3_value(scales).astype(np.float32)
+    S = (d * s_t).astype(np.float32)
+    zero_group = S < np.float32(2.0 ** -126)
+    S_safe = np.where(zero_group, np.float32(1.0), S)
+    R = (1.0 / S_safe.astype(np.float64)).astype(np.float32)  # = fl32(1/S)
+    u = (grp * R[..., None]).astype(np.float32)
+    codes = e2m1_rne(u)
+    codes = np.where(zero_group[..., None], np.signbit(grp).astype(np.uint8) << 3, codes)
+    return codes.reshape(rows, K).astype(np.uint8), scales, s_t
+
+
+# --------------------------------------------------------------------------
+# step 5: packing (reading R8)
+# --------------------------------------------------------------------------
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+# --------------------------------------------------------------------------
+# the whole online step: rotate + quantize + pack
+# --------------------------------------------------------------------------
+def rotate_quantize(x_bits: np.ndarray, block: int, fmt: str, tensor_amax=None):
+    """bf16 X [rows, K] -> (packed codes [rows, K/2], scale codes [rows, K/g], s_t or None)."""
+    x32 = widen_bf16(x_bits)
+    if x32.ndim != 2:
+        raise ValueError("X must be 2-D")
+    y32 = rotate_fwht_f32(x32, block)
+    if fmt == "mxfp4":
+        codes, scales = quantize_mxfp4(y32)
+        return pack_nibbles(codes), scales, None
+    if fmt == "nvfp4":
+        codes, scales, s_t = quantize_nvfp4(y32, tensor_amax)
+        return pack_nibbles(codes), scales, s_t
+    raise ValueError(fmt)
+
+
+# --------------------------------------------------------------------------
+# step 6: dequantize and multiply (reading R9)
+# --------------------------------------------------------------------------
+def dequantize(packed: np.ndarray, scales: np.ndarray, fmt: str, s_t=None) -> np.ndarray:
+    """Exact float64 values of a quantized tensor [rows, K]."""
+    codes = unpack_nibbles(packed)
+    rows, K = codes.shape
+    vals = e2m1_value(codes)
+    if fmt == "mxfp4":
+        sc = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)
+        return (vals.reshape(rows, K // MX_GROUP, MX_GROUP) * sc[..., None]).reshape(rows, K)
+    if fmt == "nvfp4":
+        sc = e4m3_value(scales) * np.float64(s_t)
+        return (vals.reshape(rows, K // NV_GROUP, NV_GROUP) * sc[..., None]).reshape(rows, K)
+    raise ValueError(fmt)
+
+
+def linear_f64(xq, xs, wq, ws, fmt: str, x_ts=None, w_ts=None) -> np.ndarray:
+    """Y64 = dq(Xq) @ dq(Wq)^T in float64 ([BRIDGE-de] §2 QuTLASS: the 4-bit matmul)."""
+    a = dequantize(xq, xs, fmt, x_ts)
+    b = dequantize(wq, ws, fmt, w_ts)
+    return a @ b.T
+
+
+def bf16_rne_f64(y: np.ndarray) -> np.ndarray:
+    """Round float64 values to bfloat16 (nearest, ties to even), returned as float64.
+
+    Used only to form the reference of a bf16-output GEMM: the output dtype
+    fixes the reference.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    m, e = np.frexp(y)  # y = m 2^e, |m| in [0.5, 1): 8 significant bits -> m * 2^8 integer
+    r = np.ldexp(np.round(np.ldexp(m, 8)), e - 8)  # np.round rounds half to even
+    return r
+
+
+# --------------------------------------------------------------------------
+# parity support: elements and groups next to a rounding boundary
+# --------------------------------------------------------------------------
+def near_boundary_flags(y32: np.ndarray, scales: np.ndarray, fmt: str, s_t=None, rel=1e-6):
+    """Elements whose float32 rotated value lies within ``rel`` (relative) of a
+    rounding boundary: an E2M1 midpoint times the group scale, or, for the whole
+    group, an MX exponent threshold 6*2^k / an E4M3 midpoint of the group scale.
+
+    Returns a bool array [rows, K]. Used only to report (never to excuse)
+    differences: the parity rule still demands bit equality everywhere else.
+    """
+    rows, K = y32.shape
+    g = MX_GROUP if fmt == "mxfp4" else NV_GROUP
+    grp = np.abs(np.asarray(y32, dtype=np.float64)).reshape(rows, K // g, g)
+    if fmt == "mxfp4":
+        scale = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)
+    else:
+        scale = e4m3_value(scales) * np.float64(s_t)
+    flags = np.zeros(grp.shape, dtype=bool)
+    for t in _E2M1_MIDPOINTS:
+        bnd = t * scale[..., None]
+        flags |= np.abs(grp - bnd) <= rel * bnd
+    amax = grp.max(axis=2)
+    if fmt == "mxfp4":
+        # exponent thresholds alpha_max = 6 * 2^k
+        with np.errstate(divide="ignore"):
+            k = np.round(np.log2(np.where(amax > 0, amax, 1.0) / 6.0))
+        thr = 6.0 * np.ldexp(1.0, k.astype(np.int64))
+        gflag = (amax > 0) & (np.abs(amax - thr) <= rel * thr)
+    else:
+        if s_t == 0:
+            gflag = np.zeros(amax.shape, dtype=bool)
+        else:
+            q = amax / (6.0 * np.float64(s_t))
+            j = np.clip(np.searchsorted(_E4M3_MIDPOINTS, q), 0, len(_E4M3_MIDPOINTS) - 1)
+            gflag = np.zeros(amax.shape, dtype=bool)
+            for jj in (j - 1, j):
+                m = _E4M3_MIDPOINTS[np.clip(jj, 0, len(_E4M3_MIDPOINTS) - 1)]
+                gflag |= np.abs(q - m) <= rel * m
+    flags |= gflag[..., None]
+    return flags.reshape(rows, K)

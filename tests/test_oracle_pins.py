@@ -1,0 +1,412 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a library
+routine (scipy's Hadamard matrix, torch's float8_e4m3fn), a brute-force search,
+exact rational arithmetic, a closed form or an invariant. A plausible mistake
+(dropped butterfly stage, wrong sign, wrong scale rounding direction, wrong tie
+rule, transposed GEMM operand, swapped nibbles) fails at least one of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+from oracle import fp4_oracle as O
+from microscaling_fp4_quantized_amd import workloads as WL
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "format_facts.json")
+BLOCKS = (16, 32, 64, 128)
+
+
+def facts():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------
+# Hadamard rotation
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("b", BLOCKS)
+def test_sylvester_matches_scipy_and_is_orthogonal(b):
+    H = O.sylvester_hadamard(b)
+    assert np.array_equal(H, scipy.linalg.hadamard(b))  # library construction
+    assert np.array_equal(H, H.T)
+    assert np.array_equal(H @ H.T, b * np.eye(b, dtype=np.int64))
+
+
+@pytest.mark.parametrize("b", BLOCKS)
+def test_hadamard_constant_is_correctly_rounded(b):
+    c = O.hadamard_constant(b)
+    cf = Fraction(float(c))
+    ulp = Fraction(2) ** (math.frexp(float(c))[1] - 24)
+    # |c - 1/sqrt(b)| <= ulp/2  <=>  (c - ulp/2)^2 <= 1/b <= (c + ulp/2)^2
+    assert (cf - ulp / 2) ** 2 <= Fraction(1, b) <= (cf + ulp / 2) ** 2
+
+
+@pytest.mark.parametrize("b", BLOCKS)
+def test_fwht_exact_on_small_integers(b):
+    # all partial sums are small integers -> the float32 transform is exact
+    x = rng(b).integers(-512, 513, size=(7, 4 * b)).astype(np.float32)
+    y = O.rotate_fwht_f32(x, b)
+    z = (x.astype(np.int64).reshape(-1, b) @ scipy.linalg.hadamard(b).T).reshape(x.shape)
+    expect = z.astype(np.float32) * O.hadamard_constant(b)
+    assert np.array_equal(y, expect)
+
+
+@pytest.mark.parametrize("b", BLOCKS)
+def test_fwht_f32_within_rounding_bound_of_exact(b):
+    x = O.widen_bf16(WL.bf16_bits_from_f32(rng(b + 1).standard_t(3, size=(64, 8 * b)).astype(np.float32)))
+    y32 = O.rotate_fwht_f32(x, b).astype(np.float64)
+    y64 = O.rotate_exact_f64(x, b)
+    H = scipy.linalg.hadamard(b).astype(np.float64)
+    y64_lib = (x.astype(np.float64).reshape(-1, b) @ H) / math.sqrt(b)
+    assert np.allclose(y64.reshape(-1, b), y64_lib, rtol=0, atol=1e-12 * np.abs(x).max())
+    # per block: each of log2(b) stages and the final multiply round once (<= 2^-24 relative)
+    err = np.linalg.norm((y32 - y64).reshape(-1, b), axis=1)
+    nrm = np.linalg.norm(x.astype(np.float64).reshape(-1, b), axis=1)
+    assert np.all(err <= (math.log2(b) + 2) * 2.0 ** -24 * nrm * 1.01)
+
+
+@pytest.mark.parametrize("b", BLOCKS)
+def test_rotation_preserves_norm_and_is_linear_odd(b):
+    x = O.widen_bf16(WL.bf16_bits_from_f32(rng(3 * b).standard_normal((32, 4 * b)).astype(np.float32)))
+    y = O.rotate_fwht_f32(x, b)
+    nx = np.linalg.norm(x.astype(np.float64), axis=1)
+    ny = np.linalg.norm(y.astype(np.float64), axis=1)
+    assert np.all(np.abs(ny - nx) <= 1e-6 * nx)
+    yn = O.rotate_fwht_f32(-x, b)
+    nz = y != 0
+    assert np.array_equal(yn[nz], -y[nz])
+
+
+def test_rotation_fused_into_weights_keeps_product():
+    # (X R)(W R)^T = X W^T for the block-diagonal orthogonal R (rotation folded into W)
+    x = rng(5).standard_normal((6, 256))
+    w = rng(6).standard_normal((10, 256))
+    for b in BLOCKS:
+        lhs = O.rotate_exact_f64(x, b) @ O.rotate_exact_f64(w, b).T
+        assert np.allclose(lhs, x @ w.T, rtol=0, atol=1e-12 * np.abs(x @ w.T).max())
+
+
+# --------------------------------------------------------------------------
+# E2M1 elements
+# --------------------------------------------------------------------------
+def test_e2m1_grid_from_format_definition():
+    f = facts()
+    eb, mb = f["e2m1_element_format"]["exponent_bits"], f["e2m1_element_format"]["mantissa_bits"]
+    bias = 2 ** (eb - 1) - 1
+    vals = []
+    for e in range(2 ** eb):
+        for m in range(2 ** mb):
+            if e == 0:
+                vals.append(m / 2 ** mb * 2.0 ** (1 - bias))
+            else:
+                vals.append((1 + m / 2 ** mb) * 2.0 ** (e - bias))
+    assert vals == list(O.E2M1_MAGNITUDES)
+    assert max(vals) == f["e2m1_max"]["value"]
+
+
+def _e2m1_brute(u):
+    grid = [Fraction(float(g)) for g in O.E2M1_MAGNITUDES]
+    out = np.empty(u.shape, dtype=np.uint8)
+    for idx, v in np.ndenumerate(u):
+        av = abs(Fraction(float(v)))
+        d = [abs(av - g) for g in grid]
+        best = min(d)
+        cands = [i for i, di in enumerate(d) if di == best]
+        c = cands[0] if len(cands) == 1 else [i for i in cands if i % 2 == 0][0]
+        out[idx] = c | (8 if math.copysign(1.0, v) < 0 else 0)
+    return out
+
+
+def test_e2m1_rne_brute_force_all_bf16_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):
+        u = WL.f32_from_bf16_bits(bits).astype(np.float64)
+    ok = np.isfinite(u)
+    u = u[ok]
+    assert np.array_equal(O.e2m1_rne(u), _e2m1_brute(u))
+
+
+def test_e2m1_ties_and_signs():
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    # ties to the even code: 0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0
+    assert list(O.e2m1_rne(ties)) == [0, 2, 2, 4, 4, 6, 6]
+    assert list(O.e2m1_rne(-ties)) == [8, 10, 10, 12, 12, 14, 14]
+    assert list(O.e2m1_rne(np.array([0.0, -0.0, -1e-30, 7.0, 1e30, -1e30]))) == [0, 8, 8, 7, 7, 15]
+    nb = np.nextafter(ties, np.inf)
+    assert list(O.e2m1_rne(nb)) == [1, 2, 3, 4, 5, 6, 7]
+
+
+# --------------------------------------------------------------------------
+# E4M3 scales
+# --------------------------------------------------------------------------
+def test_e4m3_values_match_torch_float8():
+    codes = torch.arange(0x7F, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(O.e4m3_value(np.arange(0x7F)), ref)
+    f = facts()["nv_scale_format"]
+    assert (f["exponent_bits"], f["mantissa_bits"]) == (4, 3)
+    assert O.e4m3_value(np.array([0x7E]))[0] == O.E4M3_MAX
+
+
+def _e4m3_brute(q):
+    vals = [Fraction(float(v)) for v in O.e4m3_value(np.arange(0x7F))]
+    out = []
+    for x in q:
+        xf = Fraction(float(x))
+        if xf >= vals[-1]:
+            out.append(0x7E)
+            continue
+        d = [abs(xf - v) for v in vals]
+        best = min(d)
+        cands = [i for i, di in enumerate(d) if di == best]
+        out.append(cands[0] if len(cands) == 1 else [i for i in cands if i % 2 == 0][0])
+    return np.array(out, dtype=np.uint8)
+
+
+def test_e4m3_rne_sat_brute_force_and_torch():
+    vals = O.e4m3_value(np.arange(0x7F))
+    mids = (vals[:-1] + vals[1:]) / 2
+    q = np.concatenate([
+        vals, mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf),
+        [448.0, 460.0, 464.0, 1e6, 0.0, 2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -11],
+        rng(7).uniform(0, 500, 300), np.exp(rng(8).uniform(-12, 6, 300)),
+    ])
+    got = O.e4m3_rne_sat(q)
+    assert np.array_equal(got, _e4m3_brute(q))
+    # torch's cast (round to nearest even) for float32-representable in-range inputs
+    q32 = q[(q < 464.0)].astype(np.float32)
+    ref = torch.from_numpy(q32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_rne_sat(q32.astype(np.float64)), ref)
+
+
+# --------------------------------------------------------------------------
+# MXFP4 scale rule
+# --------------------------------------------------------------------------
+def _mx_exp_brute(a):
+    if a == 0:
+        return -127
+    e = -200
+    while not (Fraction(float(a)) <= 6 * Fraction(2) ** e):
+        e += 1
+    return max(-127, min(127, e))
+
+
+def test_mx_exponent_brute_force():
+    a = np.concatenate([
+        6.0 * np.ldexp(1.0, np.arange(-130, 120)),  # thresholds: exactly 6*2^k
+        np.nextafter(6.0 * np.ldexp(1.0, np.arange(-120, 120)), np.inf),
+        np.nextafter(6.0 * np.ldexp(1.0, np.arange(-120, 120)), 0),
+        3.0 * np.ldexp(1.0, np.arange(-20, 20)),
+        np.exp(rng(9).uniform(-100, 80, 500)),
+        [0.0, 1e-45, 2.0 ** -149, 3.4e38],
+    ]).astype(np.float32)
+    got = O.mx_shared_exponent(a)
+    ref = np.array([_mx_exp_brute(v) for v in a])
+    assert np.array_equal(got, ref)
+
+
+def test_mx_scale_rounds_up_like_the_example():
+    f = facts()["scale_rounding_direction_example"]
+    # an ideal scale of 3.5 with power-of-two marks 2 and 4 must become 4
+    e = O.mx_shared_exponent(np.array([6.0 * f["value"]], dtype=np.float32))[0]
+    assert 2.0 ** e == f["must_round_to"]
+
+
+@pytest.mark.parametrize("b", (32, 128))
+def test_mx_block_max_lands_in_3_6(b):
+    f = facts()
+    lo, hi = f["mx_block_max_range"]["low_exclusive"], f["mx_block_max_range"]["high_inclusive"]
+    g = f["mx_group_size"]["value"]
+    x = WL.draw_x(WL.WORKLOADS["tiny"])
+    xp, sc, _ = O.rotate_quantize(x, b, "mxfp4")
+    y = O.rotate_fwht_f32(O.widen_bf16(x), b)
+    amax = np.abs(y.astype(np.float64)).reshape(y.shape[0], -1, g).max(axis=2)
+    r = amax / np.ldexp(1.0, sc.astype(np.int64) - 127)
+    assert sc.shape == (x.shape[0], x.shape[1] // g)
+    assert np.all((r > lo) & (r <= hi))
+    # and the largest code magnitude of each group is 3, 4 or 6 (from (3, 6] and RTN)
+    codes = O.unpack_nibbles(xp).reshape(x.shape[0], -1, g)
+    mx = O.E2M1_MAGNITUDES[(codes & 7).max(axis=2)]
+    assert set(np.unique(mx)) <= {3.0, 4.0, 6.0}
+
+
+def test_mx_power_of_two_equivariance_and_sign_symmetry():
+    x = WL.draw_x(WL.WORKLOADS["tiny"])
+    x32 = O.widen_bf16(x)
+    p0, s0, _ = O.rotate_quantize(x, 32, "mxfp4")
+    for k in (-20, -3, 5, 30):
+        xk = WL.bf16_bits_from_f32(x32 * np.float32(2.0 ** k))  # exact scaling
+        pk, sk, _ = O.rotate_quantize(xk, 32, "mxfp4")
+        assert np.array_equal(pk, p0)
+        assert np.array_equal(sk.astype(int), s0.astype(int) + k)
+    xn = WL.bf16_bits_from_f32(-x32)
+    pn, sn, _ = O.rotate_quantize(xn, 32, "mxfp4")
+    assert np.array_equal(sn, s0)
+    y = O.rotate_fwht_f32(x32, 32)
+    c0, cn = O.unpack_nibbles(p0), O.unpack_nibbles(pn)
+    assert np.array_equal(cn[y != 0], c0[y != 0] ^ 8)
+
+
+def test_mx_conditional_idempotence():
+    # requantizing dq(codes) without rotation returns the same codes and scale
+    # exactly when the group's largest code magnitude is 4 or 6; with 3 the scale halves
+    x = WL.draw_x(WL.WORKLOADS["tiny"])
+    p, s, _ = O.rotate_quantize(x, 32, "mxfp4")
+    dq = O.dequantize(p, s, "mxfp4").astype(np.float32)  # exact in float32
+    c2, s2 = O.quantize_mxfp4(dq)
+    codes = O.unpack_nibbles(p).reshape(x.shape[0], -1, 32)
+    top = O.E2M1_MAGNITUDES[(codes & 7).max(axis=2)]
+    same = s2 == s
+    assert np.array_equal(same, top >= 4.0)
+    assert np.all(s2[top == 3.0].astype(int) == s[top == 3.0].astype(int) - 1)
+    g2 = c2.reshape(codes.shape)
+    assert np.array_equal(g2[same], codes[same])
+
+
+def test_mx_zero_group_and_scale_codes_are_powers_of_two():
+    x = np.zeros((2, 64), dtype=np.uint16)
+    x[1, 32:] = WL.bf16_bits_from_f32(np.linspace(-3, 3, 32).astype(np.float32))
+    p, s, _ = O.rotate_quantize(x, 32, "mxfp4")
+    assert list(s[0]) == [0, 0] and s[1, 0] == 0
+    assert np.all(O.unpack_nibbles(p)[0] == 0)
+    f = facts()["mx_scale_format"]
+    assert (f["exponent_bits"], f["mantissa_bits"]) == (8, 0)
+
+
+# --------------------------------------------------------------------------
+# NVFP4
+# --------------------------------------------------------------------------
+def test_nv_quantizer_properties():
+    f = facts()
+    x = WL.draw_x(WL.WORKLOADS["tiny"])
+    for b in (16, 32, 128):
+        p, sc, s_t = O.rotate_quantize(x, b, "nvfp4")
+        y = O.rotate_fwht_f32(O.widen_bf16(x), b).astype(np.float64)
+        g = f["nv_group_size"]["value"]
+        assert sc.shape == (x.shape[0], x.shape[1] // g)
+        T = np.abs(y).max()
+        assert s_t == np.float32(np.float32(T) / np.float32(2688))
+        grp = np.abs(y).reshape(x.shape[0], -1, g)
+        amax = grp.max(axis=2)
+        # group code: brute-force nearest E4M3 to amax/(6 s_t)
+        q = amax / (6.0 * float(s_t))
+        assert np.array_equal(sc.ravel(), _e4m3_brute(q.ravel()))
+        # the largest group scale is 448 (the tensor max maps to 6 * 448)
+        assert O.e4m3_value(sc).max() == 448.0
+        # elements: nearest grid point of y / (d s_t) unless within 1e-6 of a boundary
+        d = O.e4m3_value(sc) * float(s_t)
+        u = (y.reshape(x.shape[0], -1, g) / d[..., None]).reshape(y.shape)
+        codes = O.unpack_nibbles(p)
+        exact = O.e2m1_rne(u)
+        flags = O.near_boundary_flags(y.astype(np.float32), sc, "nvfp4", s_t)
+        assert np.array_equal(codes[~flags], exact[~flags])
+        assert flags.mean() < 1e-3
+
+
+def test_nv_equivariance_and_zero_tensor():
+    x = WL.draw_x(WL.WORKLOADS["tiny"])
+    x32 = O.widen_bf16(x)
+    p0, s0, t0 = O.rotate_quantize(x, 16, "nvfp4")
+    for k in (-7, 9):
+        pk, sk, tk = O.rotate_quantize(WL.bf16_bits_from_f32(x32 * np.float32(2.0 ** k)), 16, "nvfp4")
+        assert np.array_equal(pk, p0) and np.array_equal(sk, s0)
+        assert tk == np.float32(t0 * np.float32(2.0 ** k))
+    z = np.zeros((3, 32), dtype=np.uint16)
+    p, s, t = O.rotate_quantize(z, 16, "nvfp4")
+    assert t == 0 and np.all(s == 0) and np.all(p == 0)
+
+
+# --------------------------------------------------------------------------
+# packing, dequantization and the product
+# --------------------------------------------------------------------------
+def test_pack_low_nibble_first():
+    assert list(O.pack_nibbles(np.array([1, 2, 3, 4, 15, 0], dtype=np.uint8))) == [0x21, 0x43, 0x0F]
+    c = rng(10).integers(0, 16, size=(5, 64)).astype(np.uint8)
+    assert np.array_equal(O.unpack_nibbles(O.pack_nibbles(c)), c)
+
+
+def _frac_linear(xq, xs, wq, ws, fmt, xts=None, wts=None):
+    g = 32 if fmt == "mxfp4" else 16
+    grid = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+            Fraction(4), Fraction(6)]
+
+    def val(packed, scales, r, k, ts):
+        byte = int(packed[r, k // 2])
+        c = byte & 0xF if k % 2 == 0 else byte >> 4
+        v = grid[c & 7] * (-1 if c & 8 else 1)
+        s = int(scales[r, k // g])
+        if fmt == "mxfp4":
+            return v * Fraction(2) ** (s - 127)
+        e, m = s >> 3, s & 7
+        d = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+        return v * d * Fraction(float(ts))
+
+    M, N, K = xq.shape[0], wq.shape[0], 2 * xq.shape[1]
+    Y = np.empty((M, N))
+    for m in range(M):
+        for n in range(N):
+            Y[m, n] = float(sum(val(xq, xs, m, k, xts) * val(wq, ws, n, k, wts) for k in range(K)))
+    return Y
+
+
+@pytest.mark.parametrize("fmt", ("mxfp4", "nvfp4"))
+def test_linear_matches_exact_rational_product(fmt):
+    x = WL.draw_normal_bf16((3, 64), 1.0, 1)
+    w = WL.draw_normal_bf16((5, 64), 0.02, 2)
+    b = 16 if fmt == "nvfp4" else 32
+    xq, xs, xt = O.rotate_quantize(x, b, fmt)
+    wq, ws, wt = O.rotate_quantize(w, b, fmt)
+    Y = O.linear_f64(xq, xs, wq, ws, fmt, xt, wt)
+    assert Y.shape == (3, 5)
+    assert np.allclose(Y, _frac_linear(xq, xs, wq, ws, fmt, xt, wt), rtol=1e-15, atol=0)
+
+
+def test_linear_unit_scales_exact_multiples_of_quarter():
+    c = rng(11).integers(0, 16, size=(4, 256)).astype(np.uint8)
+    d = rng(12).integers(0, 16, size=(6, 256)).astype(np.uint8)
+    xs = np.full((4, 8), 127, np.uint8)
+    ws = np.full((6, 8), 127, np.uint8)
+    Y = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "mxfp4")
+    ref = O.e2m1_value(c) @ O.e2m1_value(d).T
+    assert np.array_equal(Y, ref) and np.all(np.round(Y * 4) == Y * 4)
+
+
+def test_bf16_rounding_matches_generator_rounding():
+    y = rng(13).standard_normal(10000).astype(np.float32) * np.float32(37.0)
+    ref = WL.f32_from_bf16_bits(WL.bf16_bits_from_f32(y)).astype(np.float64)
+    assert np.array_equal(O.bf16_rne_f64(y.astype(np.float64)), ref)
+
+
+# --------------------------------------------------------------------------
+# statistical sanity (not parity): rotation helps MXFP4 on heavy tails
+# ([BRIDGE-de] §2 "Theoretische Analyse der Fehler")
+# --------------------------------------------------------------------------
+def test_rotation_lowers_mxfp4_error_on_laplace_data():
+    x32 = rng(14).laplace(size=(256, 1024)).astype(np.float32)
+    x32[:, rng(15).choice(1024, 8, replace=False)] *= 20
+    x = WL.bf16_bits_from_f32(x32)
+    xw = O.widen_bf16(x).astype(np.float64)
+
+    def rel_mse(rotated):
+        if rotated:
+            y = O.rotate_fwht_f32(O.widen_bf16(x), 32)
+        else:
+            y = O.widen_bf16(x)
+        c, s = O.quantize_mxfp4(y)
+        dq = O.dequantize(O.pack_nibbles(c), s, "mxfp4")
+        ref = y.astype(np.float64)
+        return np.sum((dq - ref) ** 2) / np.sum(ref ** 2)
+
+    assert rel_mse(True) < rel_mse(False)
+    assert np.isfinite(xw).all()
