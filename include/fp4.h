@@ -1,0 +1,143 @@
+/*
+ * fp4.h - C ABI of the MI355X (gfx950) online FP4 inference path.
+ *
+ * Three calls, matching the method's statement of the problem:
+ *
+ *   fp4_rotate_quantize   online: block-wise Hadamard rotation of bf16
+ *                         activations fused with microscaled FP4 quantization.
+ *   fp4_quantize_weights  offline: the same rotation and quantization applied
+ *                         to a weight matrix, so the rotation is folded into W.
+ *   fp4_linear            the W4A4 product Y = dq(Xq) dq(Wq)^T.
+ *
+ * Sources: "Bridging the Gap Between Promise and Performance for Microscaling
+ * FP4 Quantization" (gist.science, German edition), Technische Zusammenfassung
+ * §2 "Einführung von MR-GPTQ" (block-wise Hadamard rotations of weights and
+ * activations) and §2 "GPU-Kernel-Unterstützung (QuTLASS)" (fused online
+ * rotation + quantization kernel, 4-bit matmul); the same paper's English
+ * abstract on chatpaper.ai (rotation fused into the weights, fast online
+ * computation of the activations); §1 Problemstellung (MXFP4: 32 elements per
+ * scale, NVFP4: 16).
+ *
+ * Conventions shared by every call:
+ *  - Pointers named as device pointers must point to device memory of the
+ *    current HIP device. The caller owns and allocates every buffer; the library
+ *    allocates nothing and keeps no state besides a thread-local error string.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
+ *    asynchronously; no call synchronises the host.
+ *  - All arguments are validated before anything is launched. On a non-OK
+ *    status nothing has been launched and no output has been written; the
+ *    message is available from fp4_last_error().
+ *  - bf16 X / W values must be finite, with |value| <= 2^100 (larger values may
+ *    overflow inside the float32 rotation); NaN/Inf are outside the contract.
+ */
+#ifndef FP4_MI355X_H
+#define FP4_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4_API __attribute__((visibility("default")))
+
+/* Formats. MXFP4: groups of 32 E2M1 elements share one E8M0 (power-of-two)
+ * scale. NVFP4: groups of 16 share one E4M3 scale, plus one float32 scale for
+ * the whole tensor ("Unveiling the Potential of Quantization with MXFP4",
+ * gist.science, Dutch edition, Technische samenvatting, Probleemstelling). */
+enum { FP4_MXFP4 = 0, FP4_NVFP4 = 1 };
+
+/* Output dtypes of fp4_linear. */
+enum { FP4_OUT_F32 = 0, FP4_OUT_BF16 = 1 };
+
+/* Status codes (every call returns one). */
+enum {
+  FP4_OK = 0,
+  FP4_E_NULLPTR = -1, /* a required pointer is NULL, or a forbidden one is not     */
+  FP4_E_SHAPE = -2,   /* M, N or K out of range, K not a multiple of what is needed */
+  FP4_E_BLOCK = -3,   /* Hadamard block not in {16, 32, 64, 128}                  */
+  FP4_E_FORMAT = -4,  /* unknown format or output dtype                            */
+  FP4_E_ALIGN = -5,   /* a pointer or leading dimension breaks the alignment rule  */
+  FP4_E_HIP = -6      /* the HIP runtime reported an error at launch               */
+};
+
+/*
+ * fp4_rotate_quantize - rotate every row of X by the block-diagonal Hadamard
+ * matrix (blocks of `block` along K) and quantize it to MXFP4 or NVFP4.
+ *
+ * Per row, per aligned block of `block` elements: y = H_block x / sqrt(block),
+ * computed in float32 as the fast Walsh-Hadamard transform with strides 1, 2,
+ * 4, ... block/2 in that order (pairs (i, i+h) -> (x_i + x_{i+h}, x_i - x_{i+h}))
+ * followed by one float32 multiply by fl32(1/sqrt(block)).
+ * Then per group of g elements (g = 32 MXFP4, 16 NVFP4), with alpha = max |y|:
+ *  MXFP4: e = smallest integer with alpha <= 6 * 2^e (the group maximum lands
+ *         in (3, 6]), clamped to [-127, 127]; scale code = e + 127.
+ *  NVFP4: T = max |y| over all of X; s_t = fl32(T / 2688) is written to
+ *         *tensor_scale; scale code = nearest E4M3FN value to alpha / (6 s_t)
+ *         (ties to even, saturating at 448); elements use u = fl32(y * R) with
+ *         R = fl32(1 / fl32(d * s_t)), d the decoded group scale; a group with
+ *         d * s_t < 2^-126 stores signed zeros; T == 0 stores all zeros, s_t = 0.
+ * Element code: round-to-nearest-even of u = y / scale onto the E2M1 grid
+ * {0, .5, 1, 1.5, 2, 3, 4, 6}, saturating at 6, bit 3 = sign of y.
+ *
+ *  X            device, bf16 [M, ldx] row-major; columns 0..K-1 are used.
+ *               16-byte aligned; ldx >= K and ldx % 8 == 0.
+ *  M            rows, M >= 1.   K: columns, K >= 1, K % block == 0, K % 32 == 0.
+ *  block        16, 32, 64 or 128.
+ *  fmt          FP4_MXFP4 or FP4_NVFP4.
+ *  codes        device, uint8 [M, K/2]: byte j of a row holds element 2j in
+ *               its low nibble, element 2j+1 in its high nibble. 16-byte aligned.
+ *  scales       device, uint8 [M, K/g] row-major (E8M0 or E4M3FN codes).
+ *               NVFP4: 2-byte aligned.
+ *  tensor_scale NVFP4: device float[1]; receives s_t (it also serves as the
+ *               pass-1 maximum while the call runs). MXFP4: must be NULL.
+ *  stream       hipStream_t or NULL.
+ * MXFP4 is one kernel launch; NVFP4 is four (clear, tensor maximum, quantize,
+ * finish the tensor scale), all on `stream`.
+ */
+FP4_API int fp4_rotate_quantize(const void *X, int64_t M, int64_t K, int64_t ldx, int block, int fmt,
+                        uint8_t *codes, uint8_t *scales, float *tensor_scale, void *stream);
+
+/*
+ * fp4_quantize_weights - the same rotation and quantization on a weight matrix
+ * W [N, K] (offline), so that the rotation cancels in the product:
+ * (X R)(W R)^T = X W^T for the orthogonal block-diagonal R. Arguments as for
+ * fp4_rotate_quantize with (W, N, ldw) in place of (X, M, ldx); the same
+ * `block` and `fmt` must be used for X and W.
+ */
+FP4_API int fp4_quantize_weights(const void *W, int64_t N, int64_t K, int64_t ldw, int block, int fmt,
+                         uint8_t *codes, uint8_t *scales, float *tensor_scale, void *stream);
+
+/*
+ * fp4_linear - Y[m, n] = sum_k dq(Xq)[m, k] * dq(Wq)[n, k], float32 accumulation.
+ *  MXFP4: dq = e2m1(code) * 2^(scale - 127); runs on gfx950 scaled MFMA with
+ *         the E8M0 scales consumed by the instruction.
+ *  NVFP4: dq = e2m1(code) * e4m3(scale) * s_t; the E4M3 group scale is folded
+ *         into an exact bf16 operand in the kernel prologue (E4M3 scales have no
+ *         native MFMA form on gfx950), x_ts * w_ts is applied in the epilogue.
+ *
+ *  Xq  device uint8 [M, K/2], Xs device uint8 [M, K/g]  (fp4_rotate_quantize output)
+ *  Wq  device uint8 [N, K/2], Ws device uint8 [N, K/g]  (fp4_quantize_weights output)
+ *  x_ts, w_ts  NVFP4: device float[1] tensor scales; MXFP4: must be NULL.
+ *  M, N >= 1; K >= 128 and K % 128 == 0.
+ *  Xq, Wq 16-byte aligned; Xs, Ws 4-byte aligned.
+ *  Y   device [M, N] row-major, float32 (FP4_OUT_F32) or bf16 (FP4_OUT_BF16,
+ *      round-to-nearest-even); 16-byte aligned.
+ * No bias, no activation. One kernel launch on `stream`.
+ */
+FP4_API int fp4_linear(const uint8_t *Xq, const uint8_t *Xs, const float *x_ts,
+               const uint8_t *Wq, const uint8_t *Ws, const float *w_ts,
+               int64_t M, int64_t N, int64_t K, int fmt,
+               void *Y, int y_dtype, void *stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+FP4_API const char *fp4_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+FP4_API int fp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4_MI355X_H */

@@ -1,0 +1,140 @@
+"""Thin Python binding of libfp4.so (include/fp4.h), same names as the C calls.
+
+Argument marshalling only: every step of the path runs in the HIP kernels behind
+the C ABI. torch supplies device memory (outputs are allocated with
+``torch.empty`` on the input's device) and the current stream. There is no
+fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "FP4_MXFP4",
+    "FP4_NVFP4",
+    "Fp4Error",
+    "library_path",
+    "load_library",
+    "fp4_rotate_quantize",
+    "fp4_quantize_weights",
+    "fp4_linear",
+    "fp4_abi_version",
+    "group_size",
+]
+
+FP4_MXFP4 = 0
+FP4_NVFP4 = 1
+_FMT = {"mxfp4": FP4_MXFP4, "nvfp4": FP4_NVFP4, FP4_MXFP4: FP4_MXFP4, FP4_NVFP4: FP4_NVFP4}
+_STATUS = {0: "OK", -1: "NULLPTR", -2: "SHAPE", -3: "BLOCK", -4: "FORMAT", -5: "ALIGN", -6: "HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class Fp4Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{_STATUS.get(status, status)}] {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libfp4.so")
+
+
+def load_library() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; build it with `python -m microscaling_fp4_quantized_amd.build` "
+            "(there is no fallback path)")
+    lib = ctypes.CDLL(path)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    q_args = [vp, i64, i64, i64, i32, i32, vp, vp, vp, vp]
+    for name in ("fp4_rotate_quantize", "fp4_quantize_weights"):
+        f = getattr(lib, name)
+        f.argtypes = q_args
+        f.restype = i32
+    lib.fp4_linear.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32, vp]
+    lib.fp4_linear.restype = i32
+    lib.fp4_last_error.argtypes = []
+    lib.fp4_last_error.restype = ctypes.c_char_p
+    lib.fp4_abi_version.argtypes = []
+    lib.fp4_abi_version.restype = i32
+    _LIB = lib
+    return lib
+
+
+def group_size(fmt) -> int:
+    return 32 if _FMT[fmt] == FP4_MXFP4 else 16
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check(status: int):
+    if status != 0:
+        raise Fp4Error(status, load_library().fp4_last_error().decode())
+
+
+def _quantize(name: str, x: torch.Tensor, block: int, fmt, out=None):
+    lib = load_library()
+    f = _FMT[fmt]
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError(f"{name}: expects a 2-D bf16 CUDA tensor with unit column stride")
+    M, K = x.shape
+    g = group_size(f)
+    if out is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((M, K // g), dtype=torch.uint8, device=x.device)
+        ts = torch.empty((1,), dtype=torch.float32, device=x.device) if f == FP4_NVFP4 else None
+    else:
+        codes, scales, ts = out
+    _check(getattr(lib, name)(_ptr(x), M, K, x.stride(0), int(block), f, _ptr(codes), _ptr(scales),
+                              _ptr(ts), _stream(x.device)))
+    return codes, scales, ts
+
+
+def fp4_rotate_quantize(x: torch.Tensor, block: int, fmt="mxfp4", out=None):
+    """Online block-Hadamard rotation + FP4 quantization of bf16 activations.
+
+    Returns (codes [M, K/2] uint8, scales [M, K/g] uint8, tensor_scale [1] float32 or None).
+    ``out`` may pass preallocated (codes, scales, tensor_scale).
+    """
+    return _quantize("fp4_rotate_quantize", x, block, fmt, out)
+
+
+def fp4_quantize_weights(w: torch.Tensor, block: int, fmt="mxfp4", out=None):
+    """Offline rotation + quantization of a weight matrix [N, K] (same contract)."""
+    return _quantize("fp4_quantize_weights", w, block, fmt, out)
+
+
+def fp4_linear(xq, xs, wq, ws, fmt="mxfp4", x_ts=None, w_ts=None, out_dtype=torch.float32, out=None):
+    """Y = dq(Xq) dq(Wq)^T, [M, N] in float32 or bf16."""
+    lib = load_library()
+    f = _FMT[fmt]
+    M, N, K = xq.shape[0], wq.shape[0], 2 * xq.shape[1]
+    for t in (xq, xs, wq, ws):
+        if not t.is_cuda or t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("fp4_linear: codes and scales must be contiguous uint8 CUDA tensors")
+    if wq.shape[1] * 2 != K:
+        raise ValueError("fp4_linear: X and W disagree on K")
+    ydt = {torch.float32: 0, torch.bfloat16: 1}[out_dtype]
+    y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    _check(lib.fp4_linear(_ptr(xq), _ptr(xs), _ptr(x_ts), _ptr(wq), _ptr(ws), _ptr(w_ts), M, N, K, f,
+                          _ptr(y), ydt, _stream(xq.device)))
+    return y
+
+
+def fp4_abi_version() -> int:
+    return load_library().fp4_abi_version()

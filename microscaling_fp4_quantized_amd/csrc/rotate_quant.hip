@@ -1,0 +1,278 @@
+// Online block-Hadamard rotation fused with MXFP4 / NVFP4 quantization (gfx950).
+//
+// Method: "Bridging the Gap Between Promise and Performance for Microscaling FP4
+// Quantization" (gist.science, German edition), Technische Zusammenfassung §2
+// "Einführung von MR-GPTQ" item 1 (block-wise Hadamard rotations of weights and
+// activations) and §2 "GPU-Kernel-Unterstützung (QuTLASS)" (the activation
+// rotation is fused into a lightweight quantization kernel computed online).
+// Scale rule: "Unveiling the Potential of Quantization with MXFP4" (gist.science,
+// Dutch edition), Methodologie, 1. Overflow-Aware Scaling: standard MXFP4 maps
+// the block maximum into (3, 6].
+//
+// Work decomposition: one lane owns one 32-element chunk of a row (64 bytes of
+// bf16 in, 16 bytes of packed codes out). A Hadamard block of b <= 32 lives in
+// one lane's registers; b = 64 / 128 spans 2 / 4 adjacent lanes of a quad and
+// its last stages exchange values with DPP quad permutes. The transform follows
+// one fixed order (strides 1, 2, 4, ... then one multiply by fl32(1/sqrt(b)))
+// so its float32 result is unique. The whole path is HBM-bound: every byte of X
+// is read once, every code and scale byte written once.
+#include "common.hpp"
+
+namespace fp4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct RowMap {
+  // chunk -> (row, chunk-in-row) via multiply-high division by chunks_per_row
+  uint32_t cpr;    // chunks (32 elements) per row
+  uint32_t magic;  // see make_rowmap
+  uint32_t shift;
+  uint32_t pow2;   // cpr is a power of two: shift only
+};
+
+__device__ __forceinline__ uint32_t row_of(uint32_t gc, const RowMap& rm) {
+  if (rm.pow2) return gc >> rm.shift;
+  uint32_t t = __umulhi(gc, rm.magic);
+  return (t + ((gc - t) >> 1)) >> (rm.shift - 1);
+}
+
+// Load the lane's 32 bf16 values and widen them to float32 (exact).
+__device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ X, int64_t ldx, uint32_t gc,
+                                           const RowMap& rm, bool contiguous, float v[32]) {
+  const uint16_t* p;
+  if (contiguous) {
+    p = X + (size_t)gc * 32;
+  } else {
+    uint32_t row = row_of(gc, rm);
+    uint32_t kc = gc - row * rm.cpr;
+    p = X + (size_t)row * (size_t)ldx + (size_t)kc * 32;
+  }
+  const v4u* q = reinterpret_cast<const v4u*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v4u w = __builtin_nontemporal_load(q + j);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      v[8 * j + 2 * t] = bf16_lo(w[t]);
+      v[8 * j + 2 * t + 1] = bf16_hi(w[t]);
+    }
+  }
+}
+
+// Fast Walsh-Hadamard transform of the Hadamard block, unnormalised.
+template <int B>
+__device__ __forceinline__ void fwht(float v[32]) {
+  constexpr int IN_LANE = B < 32 ? B : 32;
+#pragma unroll
+  for (int h = 1; h < IN_LANE; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (!(i & h)) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+  // stride 32 (lane ^ 1) and 64 (lane ^ 2): the lower lane keeps x + partner,
+  // the upper lane partner - x (its own value with the sign bit flipped).
+  if constexpr (B >= 64) {
+    const unsigned flip = (threadIdx.x & 1) ? 0x80000000u : 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = quad_xor<1>(v[i]) + __uint_as_float(__float_as_uint(v[i]) ^ flip);
+  }
+  if constexpr (B >= 128) {
+    const unsigned flip = (threadIdx.x & 2) ? 0x80000000u : 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = quad_xor<2>(v[i]) + __uint_as_float(__float_as_uint(v[i]) ^ flip);
+  }
+}
+
+// Eight float32 values -> one dword of eight E2M1 codes (element 2j in the low
+// nibble of byte j), dividing by 2^(exponent field of `scale` - 127) exactly and
+// rounding to nearest, ties to even, saturating at 6, keeping the sign.
+__device__ __forceinline__ unsigned cvt8(const float* v, float scale) {
+  unsigned w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], scale, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], scale, 3);
+  return w;
+}
+
+__device__ __forceinline__ unsigned sign_codes8(const float* v) {
+  unsigned w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= ((__float_as_uint(v[i]) >> 31) << 3) << (4 * i);
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4: one kernel. E8M0 code = max(0, biased_exp(alpha) - 2 + [mantissa > 0.5]),
+// i.e. e = ceil(log2(alpha / 6)) clamped to [-127, 127] (alpha = 0 -> code 0).
+// ---------------------------------------------------------------------------
+template <int B>
+__global__ __launch_bounds__(kThreads) void rotate_quant_mx(const uint16_t* __restrict__ X, int64_t ldx,
+                                                            RowMap rm, uint32_t total, int contiguous,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  const uint32_t gc = blockIdx.x * kThreads + threadIdx.x;
+  if (gc >= total) return;  // whole quads leave together (total % (B/32) == 0)
+  float v[32];
+  load_chunk(X, ldx, gc, rm, contiguous != 0, v);
+  fwht<B>(v);
+  const float c = __uint_as_float(hadamard_constant_bits(B));
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    v[i] *= c;
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  const unsigned ab = __float_as_uint(amax);
+  int code = (int)(ab >> 23) - 2 + ((ab & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+  code = code < 0 ? 0 : code;
+  const float sc = __uint_as_float((unsigned)code << 23);
+  v4u out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[j] = cvt8(v + 8 * j, sc);
+  __builtin_nontemporal_store(out, reinterpret_cast<v4u*>(codes) + gc);
+  scales[gc] = (uint8_t)code;
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 pass 1: T = max |y| over the tensor, accumulated with an integer
+// atomic max on the float bits (non-negative floats order like their bits).
+// max |fl32(z c)| = fl32(max|z| c) since rounding is monotone, so the final
+// multiply is applied once per lane.
+// ---------------------------------------------------------------------------
+__global__ void clear_word(unsigned* p) {
+  if (threadIdx.x == 0) *p = 0u;
+}
+
+template <int B>
+__global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restrict__ X, int64_t ldx,
+                                                        RowMap rm, uint32_t total, int contiguous,
+                                                        unsigned* __restrict__ amax_bits) {
+  const uint32_t gc = blockIdx.x * kThreads + threadIdx.x;
+  float m = 0.f;
+  if (gc < total) {
+    float v[32];
+    load_chunk(X, ldx, gc, rm, contiguous != 0, v);
+    fwht<B>(v);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+    m *= __uint_as_float(hadamard_constant_bits(B));
+  }
+  // wave reduction, then one atomic per wave
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) atomicMax(amax_bits, __float_as_uint(m));
+}
+
+// NVFP4 pass 2: group scales and codes given T.
+template <int B>
+__global__ __launch_bounds__(kThreads) void rotate_quant_nv(const uint16_t* __restrict__ X, int64_t ldx,
+                                                            RowMap rm, uint32_t total, int contiguous,
+                                                            const unsigned* __restrict__ amax_bits,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  const uint32_t gc = blockIdx.x * kThreads + threadIdx.x;
+  if (gc >= total) return;
+  float v[32];
+  load_chunk(X, ldx, gc, rm, contiguous != 0, v);
+  fwht<B>(v);
+  const float c = __uint_as_float(hadamard_constant_bits(B));
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] *= c;
+  const float T = __uint_as_float(*amax_bits);
+  const float s_t = (float)((double)T / 2688.0);  // = fl32(T / 2688)
+  v4u out;
+  unsigned sc2 = 0;
+  if (s_t == 0.f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = sign_codes8(v + 8 * j);
+  } else {
+    const double den = 6.0 * (double)s_t;  // exact
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[16 * g + i]));
+      const unsigned code = e4m3_rne_sat((double)a / den);
+      const float S = e4m3_value(code) * s_t;
+      sc2 |= code << (8 * g);
+      if (S < 1.17549435e-38f) {  // 2^-126: the group stores signed zeros
+        out[2 * g] = sign_codes8(v + 16 * g);
+        out[2 * g + 1] = sign_codes8(v + 16 * g + 8);
+      } else {
+        const float R = (float)(1.0 / (double)S);  // = fl32(1 / S)
+        float u[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) u[i] = v[16 * g + i] * R;
+        out[2 * g] = cvt8(u, 1.0f);
+        out[2 * g + 1] = cvt8(u + 8, 1.0f);
+      }
+    }
+  }
+  __builtin_nontemporal_store(out, reinterpret_cast<v4u*>(codes) + gc);
+  reinterpret_cast<uint16_t*>(scales)[gc] = (uint16_t)sc2;
+}
+
+// NVFP4 pass 3: replace T by s_t = fl32(T / 2688) in the caller's tensor-scale word.
+__global__ void finish_tensor_scale(float* ts) {
+  if (threadIdx.x == 0) {
+    const float T = __uint_as_float(*reinterpret_cast<unsigned*>(ts));
+    *ts = (float)((double)T / 2688.0);
+  }
+}
+
+RowMap make_rowmap(uint32_t cpr) {
+  RowMap rm{cpr, 0, 0, 0};
+  if ((cpr & (cpr - 1)) == 0) {
+    rm.pow2 = 1;
+    while ((1u << rm.shift) < cpr) ++rm.shift;
+    return rm;
+  }
+  uint32_t l = 0;
+  while ((1ull << l) < cpr) ++l;  // l = ceil(log2 cpr) >= 2
+  rm.magic = (uint32_t)((((1ull << l) - cpr) << 32) / cpr + 1);
+  rm.shift = l;
+  return rm;
+}
+
+template <int B>
+hipError_t launch_b(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int fmt, uint8_t* codes,
+                    uint8_t* scales, float* ts, hipStream_t st) {
+  const uint32_t cpr = (uint32_t)(K / 32);
+  const uint32_t total = (uint32_t)(M * (K / 32));
+  const RowMap rm = make_rowmap(cpr);
+  const int contiguous = ldx == K;
+  const dim3 grid((total + kThreads - 1) / kThreads), block(kThreads);
+  if (fmt == 0) {
+    hipLaunchKernelGGL(rotate_quant_mx<B>, grid, block, 0, st, X, ldx, rm, total, contiguous, codes,
+                       scales);
+    return hipGetLastError();
+  }
+  unsigned* amax = reinterpret_cast<unsigned*>(ts);
+  hipLaunchKernelGGL(clear_word, dim3(1), dim3(64), 0, st, amax);
+  hipLaunchKernelGGL(rotate_amax<B>, grid, block, 0, st, X, ldx, rm, total, contiguous, amax);
+  hipLaunchKernelGGL(rotate_quant_nv<B>, grid, block, 0, st, X, ldx, rm, total, contiguous, amax, codes,
+                     scales);
+  hipLaunchKernelGGL(finish_tensor_scale, dim3(1), dim3(64), 0, st, ts);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace fp4
+
+hipError_t fp4_launch_rotate_quantize(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int block,
+                                      int fmt, uint8_t* codes, uint8_t* scales, float* ts,
+                                      hipStream_t st) {
+  switch (block) {
+    case 16: return fp4::launch_b<16>(X, M, K, ldx, fmt, codes, scales, ts, st);
+    case 32: return fp4::launch_b<32>(X, M, K, ldx, fmt, codes, scales, ts, st);
+    case 64: return fp4::launch_b<64>(X, M, K, ldx, fmt, codes, scales, ts, st);
+    default: return fp4::launch_b<128>(X, M, K, ldx, fmt, codes, scales, ts, st);
+  }
+}

@@ -1,0 +1,95 @@
+"""The C-ABI library loads and exports every symbol include/fp4.h declares, and
+argument validation rejects bad calls before anything touches the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from microscaling_fp4_quantized_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4.h")
+
+
+def declared_symbols():
+    with open(HEADER) as f:
+        text = f.read()
+    return re.findall(r"FP4_API\s+[\w\s\*]+?\b(fp4_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        pytest.skip("libfp4.so not built")
+    return binding.load_library()
+
+
+def test_header_declares_the_three_calls():
+    syms = declared_symbols()
+    for s in ("fp4_rotate_quantize", "fp4_quantize_weights", "fp4_linear", "fp4_last_error"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for s in declared_symbols():
+        assert s in exported, s
+        assert hasattr(lib, s)
+    # nothing else with C linkage leaks out
+    assert {s for s in exported if s.startswith("fp4_")} == set(declared_symbols())
+    assert lib.fp4_abi_version() == 100
+
+
+A16 = 0x10000  # a 16-byte aligned fake address: never dereferenced, validation fails first
+
+
+def q(lib, X=A16, M=4, K=64, ldx=64, block=32, fmt=0, codes=A16, scales=A16, ts=None):
+    return lib.fp4_rotate_quantize(X, M, K, ldx, block, fmt, codes, scales, ts, None)
+
+
+def test_rotate_quantize_validation(lib):
+    assert q(lib, fmt=2, X=None) == -4
+    assert q(lib, block=8) == -3
+    assert q(lib, block=256) == -3
+    assert q(lib, X=None) == -1
+    assert q(lib, codes=None) == -1
+    assert q(lib, fmt=1, ts=None) == -1            # NVFP4 needs the tensor-scale buffer
+    assert q(lib, fmt=0, ts=A16, X=None) == -1
+    assert q(lib, ts=A16) == -1                    # MXFP4 forbids it
+    assert q(lib, M=0, X=None, codes=None) == -1   # pointer checks come first
+    assert q(lib, M=0) == -2
+    assert q(lib, K=48, block=16) == -2            # K % 32
+    assert q(lib, K=96, block=64) == -2            # K % block
+    assert q(lib, ldx=32) == -2
+    assert q(lib, X=A16 + 2) == -5
+    assert q(lib, ldx=68) == -5
+    assert q(lib, codes=A16 + 8) == -5
+    assert q(lib, fmt=1, ts=A16, scales=A16 + 1) == -5
+    assert b"multiple of 32" in lib.fp4_last_error() or lib.fp4_last_error()
+    assert lib.fp4_quantize_weights(None, 4, 64, 64, 32, 0, A16, A16, None, None) == -1
+    assert b"fp4_quantize_weights" in lib.fp4_last_error()
+
+
+def lin(lib, Xq=A16, Xs=A16, xts=None, Wq=A16, Ws=A16, wts=None, M=4, N=4, K=128, fmt=0, Y=A16, ydt=0):
+    return lib.fp4_linear(Xq, Xs, xts, Wq, Ws, wts, M, N, K, fmt, Y, ydt, None)
+
+
+def test_linear_validation(lib):
+    assert lin(lib, fmt=3) == -4
+    assert lin(lib, ydt=5) == -4
+    assert lin(lib, Y=None) == -1
+    assert lin(lib, Ws=None) == -1
+    assert lin(lib, fmt=1) == -1                   # NVFP4 needs both tensor scales
+    assert lin(lib, fmt=1, xts=A16) == -1
+    assert lin(lib, xts=A16) == -1                 # MXFP4 forbids them
+    assert lin(lib, K=64) == -2
+    assert lin(lib, K=192) == -2
+    assert lin(lib, M=0) == -2
+    assert lin(lib, Xq=A16 + 4) == -5
+    assert lin(lib, Xs=A16 + 2) == -5
+    assert lin(lib, Y=A16 + 8) == -5
+    assert b"fp4_linear" in lib.fp4_last_error()

@@ -1,0 +1,144 @@
+"""GPU parity of fp4_linear (W4A4 GEMM) against the float64 oracle product.
+
+The reference is always built from oracle-quantized operands. Small cases are
+compared in full; the prefill and large workloads run at their full sizes and
+are compared on sampled rows and columns of Y.
+"""
+import numpy as np
+import pytest
+import torch
+
+from microscaling_fp4_quantized_amd import binding as B
+from microscaling_fp4_quantized_amd import workloads as WL
+from oracle import fp4_oracle as O
+from parity import (GEMM_REL_FRO_TOL, assert_quant_parity, compare_quant, dev_bf16, gemm_reference, host,
+                    rel_fro, say, tensor_amax)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load_library()
+
+
+def dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 80, 512), (37, 200, 384), (1, 16, 128), (130, 129, 256)])
+def test_unit_scales_bit_exact(M, N, K):
+    # all scales 2^0: every partial sum is a multiple of 1/4 below 2^24 -> exact in any order
+    rng = np.random.default_rng(M * N + K)
+    c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    xs = np.full((M, K // 32), 127, np.uint8)
+    ws = np.full((N, K // 32), 127, np.uint8)
+    ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "mxfp4")
+    say(f"case unit-scale exact M {M} N {N} K {K}")
+    y = B.fp4_linear(dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), "mxfp4")
+    assert np.array_equal(host(y).astype(np.float64), ref)
+    yb = B.fp4_linear(dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), "mxfp4",
+                      out_dtype=torch.bfloat16)
+    yb = host(yb.float()).astype(np.float64)
+    assert np.array_equal(yb, O.bf16_rne_f64(ref))
+
+
+def test_scale_byte_extremes_exact():
+    # per-group scales spread over a wide exponent range, still exact in float32
+    rng = np.random.default_rng(3)
+    M, N, K = 48, 64, 1024
+    c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    xs = rng.integers(120, 135, size=(M, K // 32)).astype(np.uint8)
+    ws = rng.integers(120, 135, size=(N, K // 32)).astype(np.uint8)
+    ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "mxfp4")
+    y = B.fp4_linear(dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), "mxfp4")
+    r = rel_fro(host(y), ref)
+    say(f"scale extremes rel fro {r:.3e}")
+    assert r <= 1e-6
+
+
+def quantize_both(x, w, block, fmt):
+    xq = B.fp4_rotate_quantize(dev_bf16(x), block, fmt)
+    wq = B.fp4_quantize_weights(dev_bf16(w), block, fmt)
+    torch.cuda.synchronize()
+    return xq, wq
+
+
+def linear_of(xq, wq, fmt, out_dtype):
+    y = B.fp4_linear(xq[0], xq[1], wq[0], wq[1], fmt, x_ts=xq[2], w_ts=wq[2], out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return host(y.float() if out_dtype == torch.bfloat16 else y).astype(np.float64)
+
+
+@pytest.mark.parametrize("fmt,block", [("mxfp4", 32), ("mxfp4", 128), ("nvfp4", 16), ("nvfp4", 32)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_tiny_end_to_end(fmt, block, out_dtype):
+    w = WL.WORKLOADS["tiny"]
+    x, wt = WL.draw_x(w), WL.draw_w(w)
+    say(f"case tiny linear {fmt} b{block} {out_dtype}")
+    xq, wq = quantize_both(x, wt, block, fmt)
+    assert_quant_parity(compare_quant(xq, x, block, fmt), "tiny X")
+    assert_quant_parity(compare_quant(wq, wt, block, fmt), "tiny W")
+    y = linear_of(xq, wq, fmt, out_dtype)
+    ref = gemm_reference(x, wt, block, fmt, np.arange(x.shape[0]), np.arange(wt.shape[0]))
+    if out_dtype == torch.bfloat16:
+        ref = O.bf16_rne_f64(ref)
+    r = rel_fro(y, ref)
+    say(f"tiny {fmt} b{block} rel fro {r:.3e}")
+    assert r <= GEMM_REL_FRO_TOL
+
+
+@pytest.mark.parametrize("fmt,block", [("mxfp4", 32), ("nvfp4", 16)])
+@pytest.mark.parametrize("M,N,K", [(37, 200, 384), (129, 77, 640), (1, 300, 128)])
+def test_ragged_shapes(fmt, block, M, N, K):
+    x = WL.draw_normal_bf16((M, K), 1.0, seed=M + 1)
+    wt = WL.draw_normal_bf16((N, K), 0.02, seed=N + 2)
+    say(f"case ragged linear {fmt} M {M} N {N} K {K}")
+    xq, wq = quantize_both(x, wt, block, fmt)
+    y = linear_of(xq, wq, fmt, torch.float32)
+    ref = gemm_reference(x, wt, block, fmt, np.arange(M), np.arange(N))
+    r = rel_fro(y, ref)
+    say(f"ragged rel fro {r:.3e}")
+    assert r <= GEMM_REL_FRO_TOL
+
+
+@pytest.mark.parametrize("name", ["decode1", "decode4", "decode16"])
+def test_decode_full(name):
+    w = WL.WORKLOADS[name]
+    x, wt = WL.draw_x(w), WL.draw_w(w)
+    say(f"case {name} M {w.M} N {w.N} K {w.K}")
+    xq, wq = quantize_both(x, wt, w.block, w.fmt)
+    assert_quant_parity(compare_quant(xq, x, w.block, w.fmt), name + " X")
+    y = linear_of(xq, wq, w.fmt, torch.float32)
+    ref = gemm_reference(x, wt, w.block, w.fmt, np.arange(w.M), np.arange(w.N))
+    r = rel_fro(y, ref)
+    say(f"{name} rel fro {r:.3e}")
+    assert r <= GEMM_REL_FRO_TOL
+
+
+@pytest.mark.parametrize("name", ["prefill_mx", "prefill_nv", "large"])
+def test_full_size_sampled(name):
+    w = WL.WORKLOADS[name]
+    x, wt = WL.draw_x(w), WL.draw_w(w)
+    say(f"case {name} M {w.M} N {w.N} K {w.K} b{w.block} {w.fmt} out {w.out_dtype} (sampled)")
+    out_dtype = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
+    xq, wq = quantize_both(x, wt, w.block, w.fmt)
+    y = linear_of(xq, wq, w.fmt, out_dtype)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, w.M - 1], rng.choice(w.M, 48, replace=False)]))
+    cols = np.unique(np.concatenate([[0, w.N - 1], rng.choice(w.N, 384, replace=False)]))
+    xa = wa = None
+    if w.fmt == "nvfp4":
+        xa, wa = tensor_amax(x, w.block), tensor_amax(wt, w.block)
+    assert_quant_parity(compare_quant(xq, x, w.block, w.fmt, rows=rows, t_amax=xa), name + " X")
+    assert_quant_parity(compare_quant(wq, wt, w.block, w.fmt, rows=cols, t_amax=wa), name + " W")
+    ref = gemm_reference(x, wt, w.block, w.fmt, rows, cols, xa, wa)
+    if out_dtype == torch.bfloat16:
+        ref = O.bf16_rne_f64(ref)
+    r = rel_fro(y[np.ix_(rows, cols)], ref)
+    say(f"{name} sampled rel fro {r:.3e}")
+    assert r <= GEMM_REL_FRO_TOL
