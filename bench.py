@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the online FP4 linear-layer path on one MI355X.
+
+A step is one pass of the whole online path over one batch of synthetic input:
+block-Hadamard rotate + MXFP4 quantize of the bf16 activations
+(fp4_rotate_quantize), then the W4A4 GEMM against weights rotated and
+quantized offline (fp4_linear). The default workload is the prefill linear
+layer K=4096, N=14336 with M=2048 tokens, MXFP4, Hadamard block 32, float32
+output. Weights are quantized once, before timing (offline in the method).
+
+Printed: ONE JSON line with the step throughput (TFLOP/s of the linear layer,
+2*M*N*K per step), the GEMM's roofline (MFMA FP4 peak), the rotate+quantize
+roofline on the full-size bandwidth-stress workload (16384 x 8192 bf16, HBM
+peak), and the CPU oracle timed on the host as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "MXFP4 W4A4 linear TFLOP/s + rotate-quantize GB/s (% roofline), K=4096"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(name: str) -> str:
+    p = os.path.join(ROOT, "microscaling_fp4_quantized_amd", "csrc", name)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str, source: str, launches_per_unit: float = 1.0):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, or None if the
+    kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel_key)
+    if not e or e.get("source_sha") != source_sha(source):
+        return None
+    return e["bytes_per_launch"] * launches_per_unit
+
+
+def bf16_dev(bits, dev):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def time_events(fn, iters, torch):
+    """Average device time (ms) of fn() on the current stream, via HIP events."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    for i in range(iters):
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    return sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / iters
+
+
+def cpu_baseline(wl, x_bits, w_bits):
+    """The oracle (plain NumPy, untuned) on one full step of the workload."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import fp4_oracle as O
+
+    wq, ws, wts = O.rotate_quantize(w_bits, wl.block, wl.fmt)  # offline, untimed (as on the GPU)
+    t0 = time.perf_counter()
+    xq, xs, xts = O.rotate_quantize(x_bits, wl.block, wl.fmt)
+    O.linear_f64(xq, xs, wq, ws, wl.fmt, xts, wts)
+    dt = time.perf_counter() - t0
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    flops = 2.0 * wl.M * wl.N * wl.K
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(max(blas) if blas else 1),
+        "kind": "oracle",
+        "sample": f"one full step of {wl.name} (M={wl.M}, K={wl.K}, N={wl.N}): oracle rotate+quantize of X "
+                  f"(float32 FWHT, single-threaded NumPy) + float64 dequantized product (BLAS dgemm); "
+                  f"{dt:.2f} s on {os.cpu_count()} host threads",
+        "seconds": dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_mx")
+    ap.add_argument("--stress", default="stress_mx32", help="rotate+quantize HBM workload ('' to skip)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from microscaling_fp4_quantized_amd import binding as B
+    from microscaling_fp4_quantized_amd import workloads as WL
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.load_library()
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n}), flush=True)
+        return
+
+    wl = WL.WORKLOADS[args.workload]
+    log(f"[bench] workload {wl.name}: M={wl.M} K={wl.K} N={wl.N} {wl.fmt} block {wl.block}")
+    x_bits, w_bits = WL.draw_x(wl), WL.draw_w(wl)
+    x = bf16_dev(x_bits, dev)
+    w = bf16_dev(w_bits, dev)
+    wq, ws, wts = B.fp4_quantize_weights(w, wl.block, wl.fmt)  # offline
+    del w
+    out_dtype = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
+    g = B.group_size(wl.fmt)
+    xq = torch.empty((wl.M, wl.K // 2), dtype=torch.uint8, device=dev)
+    xs = torch.empty((wl.M, wl.K // g), dtype=torch.uint8, device=dev)
+    xts = torch.empty((1,), dtype=torch.float32, device=dev) if wl.fmt == "nvfp4" else None
+    y = torch.empty((wl.M, wl.N), dtype=out_dtype, device=dev)
+
+    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] for k in ("a", "b", "c")}
+
+    def step(i=None):
+        if i is not None:
+            ev["a"][i].record()
+        B.fp4_rotate_quantize(x, wl.block, wl.fmt, out=(xq, xs, xts))
+        if i is not None:
+            ev["b"][i].record()
+        B.fp4_linear(xq, xs, wq, ws, wl.fmt, x_ts=xts, w_ts=wts, out_dtype=out_dtype, out=y)
+        if i is not None:
+            ev["c"][i].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    rq_ms = sum(a.elapsed_time(b) for a, b in zip(ev["a"], ev["b"])) / args.steps
+    gemm_ms = sum(b.elapsed_time(c) for b, c in zip(ev["b"], ev["c"])) / args.steps
+    flops = 2.0 * wl.M * wl.N * wl.K
+    step_tflops = flops / (ms_step * 1e-3) / 1e12
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    peak = MFMA_FP4_PEAK_TFLOPS if wl.fmt == "mxfp4" else MFMA_BF16_PEAK_TFLOPS
+    gemm_src = "gemm_mxfp4.hip" if wl.fmt == "mxfp4" else "gemm_nvfp4.hip"
+    gemm_kernel = "gemm_mxfp4_kernel" if wl.fmt == "mxfp4" else "gemm_nvfp4_kernel"
+    rq_bytes = wl.M * wl.K * (2 + 0.5 + 1.0 / g) + (8 if wl.fmt == "nvfp4" else 0)
+    if wl.fmt == "nvfp4":
+        rq_bytes += wl.M * wl.K * 2  # the tensor-maximum pass reads X a second time
+    y_bytes = wl.M * wl.N * (2 if out_dtype == torch.bfloat16 else 4)
+    gemm_alg_bytes = (wl.M + wl.N) * wl.K * (0.5 + 1.0 / g) + y_bytes
+    log(f"[bench] step {ms_step * 1e3:.1f} us (events: rotate+quantize {rq_ms * 1e3:.1f} us, "
+        f"GEMM {gemm_ms * 1e3:.1f} us = {gemm_tflops:.0f} TFLOP/s)")
+
+    result = {
+        "metric": METRIC,
+        "value": step_tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.fmt,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: prefill linear layer, X {wl.M}x{wl.K} bf16 (Student-t(5), 1% outlier "
+                        f"channels x30) -> block-{wl.block} Hadamard + {wl.fmt.upper()} -> W4A4 GEMM "
+                        f"vs W {wl.N}x{wl.K} (pre-rotated, quantized offline), Y {wl.out_dtype}",
+            "M": wl.M, "K": wl.K, "N": wl.N, "block": wl.block, "format": wl.fmt,
+            "out_dtype": wl.out_dtype, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": gemm_kernel,
+            "bound": "mfma",
+            "achieved": gemm_tflops,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": gemm_tflops / peak,
+            "traffic": measured_traffic(gemm_kernel, gemm_src),
+            "algorithmic_bytes": gemm_alg_bytes,
+            "avg_launch_us": gemm_ms * 1e3,
+        },
+        "components": {
+            "rotate_quantize_step_input": {
+                "us": rq_ms * 1e3,
+                "GB/s": rq_bytes / (rq_ms * 1e-3) / 1e9,
+                "note": "X of the step (16 MiB) stays resident in the 256 MB Infinity Cache between steps",
+            },
+            "gemm": {"us": gemm_ms * 1e3, "TFLOP/s": gemm_tflops},
+        },
+    }
+
+    if args.stress:
+        sw = WL.WORKLOADS[args.stress]
+        log(f"[bench] rotate+quantize stress {sw.name}: {sw.M}x{sw.K} {sw.fmt} block {sw.block}")
+        sx = WL.draw_x(sw)
+        # two input buffers used alternately so no launch finds its X in the 256 MB Infinity Cache
+        bufs = [bf16_dev(sx, dev), bf16_dev(sx, dev)]
+        del sx
+        sg = B.group_size(sw.fmt)
+        outs = (torch.empty((sw.M, sw.K // 2), dtype=torch.uint8, device=dev),
+                torch.empty((sw.M, sw.K // sg), dtype=torch.uint8, device=dev),
+                torch.empty((1,), dtype=torch.float32, device=dev) if sw.fmt == "nvfp4" else None)
+
+        def rq(i):
+            B.fp4_rotate_quantize(bufs[i & 1], sw.block, sw.fmt, out=outs)
+
+        for i in range(5):
+            rq(i)
+        n_it = 40
+        s_ms = time_events(rq, n_it, torch)
+        s_bytes = sw.M * sw.K * (2 + 0.5 + 1.0 / sg)
+        if sw.fmt == "nvfp4":
+            s_bytes += sw.M * sw.K * 2
+        gbs = s_bytes / (s_ms * 1e-3) / 1e9
+        log(f"[bench] stress rotate+quantize {s_ms * 1e3:.1f} us = {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM)")
+        result["roofline_rotate_quantize"] = {
+            "kernel": "rotate_quant_mx" if sw.fmt == "mxfp4" else "rotate_amax + rotate_quant_nv",
+            "workload": f"{sw.name}: X {sw.M}x{sw.K} bf16 Student-t(3) x log-normal channel scales, "
+                        f"block {sw.block}, {sw.fmt.upper()}",
+            "bound": "hbm",
+            "achieved": gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS,
+            "traffic": measured_traffic("rotate_quant_mx_b%d" % sw.block, "rotate_quant.hip")
+            if sw.fmt == "mxfp4" else None,
+            "algorithmic_bytes": s_bytes,
+            "avg_launch_us": s_ms * 1e3,
+        }
+        del bufs, outs
+
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline ...")
+        result["cpu_baseline"] = cpu_baseline(wl, x_bits, w_bits)
+        log(f"[bench] CPU oracle: {result['cpu_baseline']['seconds']:.2f} s per step")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
