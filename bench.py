@@ -180,8 +180,12 @@ def main():
     step_tflops = flops / (ms_step * 1e-3) / 1e12
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     peak = MFMA_FP4_PEAK_TFLOPS if wl.fmt == "mxfp4" else MFMA_BF16_PEAK_TFLOPS
-    gemm_src = "gemm_mxfp4.hip" if wl.fmt == "mxfp4" else "gemm_nvfp4.hip"
-    gemm_kernel = "gemm_mxfp4_kernel" if wl.fmt == "mxfp4" else "gemm_nvfp4_kernel"
+    if wl.fmt == "mxfp4" and wl.K % 512 == 0 and wl.M >= 256 and wl.N >= 256:
+        gemm_src, gemm_kernel = "gemm_mxfp4_ring.hip", "gemm_mxfp4_ring"
+    elif wl.fmt == "mxfp4":
+        gemm_src, gemm_kernel = "gemm_mxfp4.hip", "gemm_mxfp4_kernel"
+    else:
+        gemm_src, gemm_kernel = "gemm_nvfp4.hip", "gemm_nvfp4_kernel"
     rq_bytes = wl.M * wl.K * (2 + 0.5 + 1.0 / g) + (8 if wl.fmt == "nvfp4" else 0)
     if wl.fmt == "nvfp4":
         rq_bytes += wl.M * wl.K * 2  # the tensor-maximum pass reads X a second time

@@ -10,6 +10,9 @@
 // of row (l % 16) and the scale of that 32-element group, which is exactly one
 // MXFP4 group. So the E8M0 scales are consumed natively; no dequantization.
 //
+// This is the general kernel (any K % 128 == 0, any M, N); large shapes with K % 512 == 0
+// go to the 256x256-tile kernel in gemm_mxfp4_ring.hip.
+//
 // Tiling: a workgroup computes a BM x BN tile of Y; its waves split it into
 // WM x WN wave tiles of 16x16 MFMA fragments. Each K stage stages BK = 256 K
 // elements (128 bytes per row) of A, B and their scales in LDS, double buffered:
@@ -189,6 +192,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_mxfp4_kernel(
 hipError_t fp4_launch_gemm_mxfp4(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
                                  const uint8_t* Ws, int64_t M, int64_t N, int64_t K, void* Y,
                                  int out_bf16, hipStream_t st) {
+  if (fp4_gemm_mxfp4_ring_fits(M, N, K)) return fp4_launch_gemm_mxfp4_ring(Xq, Xs, Wq, Ws, M, N, K, Y, out_bf16, st);
   constexpr int BM = 128, BN = 128, WM = 64, WN = 64;
   using C = fp4::Cfg<BM, BN, WM, WN>;
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);

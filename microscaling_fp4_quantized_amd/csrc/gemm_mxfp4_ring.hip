@@ -1,0 +1,280 @@
+// Large-tile W4A4 MXFP4 GEMM for gfx950: Y = dq(Xq) dq(Wq)^T with 256x256 workgroup tiles.
+//
+// "Bridging the Gap Between Promise and Performance for Microscaling FP4
+// Quantization" (gist.science, German edition), Technische Zusammenfassung §2
+// "GPU-Kernel-Unterstützung (QuTLASS)": the 4-bit matmul of the online path.
+//
+// Design for CDNA4 (measured on MI355X):
+//  * v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands runs at twice the rate of the
+//    16x16x128 form, so every product is a 32x32x64 scaled MFMA; lane l carries 32 K
+//    elements (one MXFP4 group) of row l % 32 and that group's E8M0 byte.
+//  * 8 waves (2 per SIMD) in a 2 x 4 layout, 128 x 64 outputs per wave (128 accumulators),
+//    so one wave's LDS reads overlap the other wave's MFMAs.
+//  * K advances in stages of 256 elements (128 bytes per row). A 2-deep LDS ring is filled
+//    with global_load_lds_dwordx4 (LDS DMA, no register staging); 16-byte chunks of a row
+//    are XOR-swizzled so the 32 rows of a fragment read hit distinct banks.
+//  * The workgroup barrier of the ring waits for LDS reads only (each wave has already
+//    waited for its own DMA of the stage), so in-flight prefetches are not drained.
+//  * E8M0 scales are DMA'd 16 bytes per row (two stages) into their own double buffer,
+//    read once per two stages, and shifted per lane half so the MFMA op_sel picks the byte.
+//  * Output tiles go through LDS so Y is written as whole 256-byte row segments.
+//  * Tile order: workgroup i runs on XCD i % 8; each XCD takes a contiguous range of tiles,
+//    walked M-fastest within groups of 8 tile rows, so tiles running together share
+//    A and B slices in that XCD's L2.
+// Requires K % 512 == 0 (whole scale groups); other shapes use the general kernel.
+#include <atomic>
+
+#include "common.hpp"
+
+namespace fp4 {
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 256, BN = 256;        // workgroup tile
+constexpr int WGM = 2, WGN = 4;          // wave layout
+constexpr int WAVES = WGM * WGN, NT = WAVES * 64;
+constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+constexpr int BKB = 128;                 // bytes of K per row per stage (256 elements)
+constexpr int KSTEPS = 4;                // 32x32x64 steps per stage
+constexpr int NS = 2;                    // ring depth
+constexpr int STAGE = (BM + BN) * BKB;   // 64 KB
+constexpr int A_WL = BM / 8 / WAVES, B_WL = BN / 8 / WAVES;  // 1 KB DMA wave-loads per wave
+constexpr int SC_BYTES = (BM + BN) * 16;                     // scales of 2 stages
+constexpr int SC_WL = (BM + BN) / 64 / WAVES;
+constexpr int LOADS = A_WL + B_WL;
+constexpr int LDS_BYTES = NS * STAGE + 2 * SC_BYTES;         // 144 KB
+static_assert(A_WL * 8 * WAVES == BM && B_WL * 8 * WAVES == BN, "row split");
+static_assert(SC_WL * 64 * WAVES == BM + BN, "scale split");
+static_assert(WN == 64, "epilogue assumes 64-column wave tiles");
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+}
+
+// Barrier of the LDS ring: wait for this wave's LDS reads (lgkmcnt(0)) but not for its
+// in-flight DMA loads, then synchronise the workgroup.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int SEL>
+__device__ __forceinline__ v16f mfma32(v8i a, v8i b, v16f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, SEL, sa, SEL, sb);
+}
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(NT) void gemm_mxfp4_ring(const uint8_t* __restrict__ Xq, const uint8_t* __restrict__ Xs,
+                                                      const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Ws,
+                                                      void* __restrict__ Yv, int M, int N, int K, int tiles_m,
+                                                      int tiles_n, int xcd_remap) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  uint8_t* scl = smem + NS * STAGE;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = tiles_m * tiles_n;
+  int L = blockIdx.x;
+  if (xcd_remap) L = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+  constexpr int GM = 8;
+  const int first_m = (L / (GM * tiles_n)) * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int tm = first_m + (L % gsize);
+  const int tn = (L % (GM * tiles_n)) / gsize;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
+  const int KB = K / 2, KS = K / 32;
+  const int nst = K / 256;  // even
+
+  // per-lane DMA sources: 8 rows x 128 bytes per wave-load; rows past M / N repeat the last row
+  const uint8_t* srcA[A_WL];
+  const uint8_t* srcB[B_WL];
+  const uint8_t* srcS[SC_WL];
+#pragma unroll
+  for (int i = 0; i < A_WL; ++i) {
+    const int r = (wave * A_WL + i) * 8 + (lane >> 3), q = lane & 7;
+    srcA[i] = Xq + (size_t)min(m0 + r, M - 1) * KB + ((q ^ swz(r)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < B_WL; ++i) {
+    const int r = (wave * B_WL + i) * 8 + (lane >> 3), q = lane & 7;
+    srcB[i] = Wq + (size_t)min(n0 + r, N - 1) * KB + ((q ^ swz(r)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < SC_WL; ++i) {
+    const int rb = (wave * SC_WL + i) * 64;  // wave-uniform
+    const int r = rb + lane;
+    srcS[i] = rb < BM ? Xs + (size_t)min(m0 + r, M - 1) * KS : Ws + (size_t)min(n0 + r - BM, N - 1) * KS;
+  }
+
+  // stage s: its codes; even stages also bring the scales of stages s, s+1 (16 bytes per row)
+  auto issue_stage = [&](int s) {
+    if ((s & 1) == 0) {
+      uint8_t* dst = scl + ((s >> 1) & 1) * SC_BYTES;
+#pragma unroll
+      for (int i = 0; i < SC_WL; ++i)
+        __builtin_amdgcn_global_load_lds((gbl_void*)(srcS[i] + (s >> 1) * 16),
+                                         (lds_void*)(dst + (wave * SC_WL + i) * 1024), 16, 0, 0);
+    }
+    uint8_t* buf = smem + (s & 1) * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_WL; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_void*)(srcA[i] + s * BKB), (lds_void*)(buf + (wave * A_WL + i) * 1024), 16,
+                                       0, 0);
+#pragma unroll
+    for (int i = 0; i < B_WL; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_void*)(srcB[i] + s * BKB),
+                                       (lds_void*)(buf + BM * BKB + (wave * B_WL + i) * 1024), 16, 0, 0);
+  };
+
+  v16f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int fr = lane & 31, fh = lane >> 5;
+  const unsigned sh = 8u * (unsigned)fh;  // lane half h uses scale byte 2*ks + h
+  v4u sg_a[FM], sg_b[FN];                 // scale dwords of the current two stages, lane-shifted
+
+  issue_stage(0);
+  for (int s = 0; s < nst; ++s) {
+    // stage s resident: with a 2-deep ring nothing is issued after it yet
+    wait_vmcnt<0>();
+    ring_barrier();
+    if (s + 1 < nst) issue_stage(s + 1);  // refills the buffer of stage s-1 (all reads done)
+    const uint8_t* buf = smem + (s & 1) * STAGE;
+    const int sl = s & 1;
+    if (sl == 0) {
+      const uint8_t* sbuf = scl + ((s >> 1) & 1) * SC_BYTES;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sg_a[i] = *reinterpret_cast<const v4u*>(sbuf + (wm0 + i * 32 + fr) * 16) >> sh;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sg_b[j] = *reinterpret_cast<const v4u*>(sbuf + (BM + wn0 + j * 32 + fr) * 16) >> sh;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int c = 2 * ks + fh;  // 16-byte chunk of the row = 32-element group
+      // scale byte 2ks + h of the stage's 8 -> dword 2*sl + ks/2, byte 2*(ks&1) after the shift
+      unsigned xa[FM], xb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) xa[i] = sl == 0 ? sg_a[i][ks >> 1] : sg_a[i][2 + (ks >> 1)];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) xb[j] = sl == 0 ? sg_b[j][ks >> 1] : sg_b[j][2 + (ks >> 1)];
+      v4u a[FM], b[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm0 + i * 32 + fr;
+        a[i] = *reinterpret_cast<const v4u*>(buf + r * BKB + ((c ^ swz(r)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn0 + j * 32 + fr;
+        b[j] = *reinterpret_cast<const v4u*>(buf + BM * BKB + r * BKB + ((c ^ swz(r)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const v8i av = v8i{(int)a[i][0], (int)a[i][1], (int)a[i][2], (int)a[i][3], 0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const v8i bv = v8i{(int)b[j][0], (int)b[j][1], (int)b[j][2], (int)b[j][3], 0, 0, 0, 0};
+          if ((ks & 1) == 0) acc[i][j] = mfma32<0>(av, bv, acc[i][j], (int)xa[i], (int)xb[j]);
+          else acc[i][j] = mfma32<2>(av, bv, acc[i][j], (int)xa[i], (int)xb[j]);
+        }
+      }
+    }
+  }
+
+  // Epilogue: each wave stages one 32 x 64 slab at a time in its own LDS region, then
+  // writes 4 whole rows (256 B fp32 / 128 B bf16 each) per wave instruction.
+  constexpr int EP = WN * 4 + 16;  // padded row pitch (bytes)
+  __syncthreads();                 // every wave is done with the ring
+  float* ep = reinterpret_cast<float*>(smem + wave * 32 * EP);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rr = 8 * (v >> 2) + 4 * fh + (v & 3);  // 32x32 accumulator layout
+        ep[rr * (EP / 4) + j * 32 + fr] = acc[i][j][v];
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's slab is in LDS (wave-private region)
+    const int col = n0 + wn0 + (lane & 15) * 4;
+    const bool vec = (N & 3) == 0;  // rows start 16-byte aligned (Y itself is)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int rr = (lane >> 4) + 4 * k;
+      const v4f val = *reinterpret_cast<const v4f*>(&ep[rr * (EP / 4) + (lane & 15) * 4]);
+      const int row = m0 + wm0 + i * 32 + rr;
+      if (row >= M) continue;
+      if constexpr (OUT_BF16) {
+        __bf16* dst = reinterpret_cast<__bf16*>(Yv) + (size_t)row * N + col;
+        const __bf16 b0 = (__bf16)val[0], b1 = (__bf16)val[1], b2 = (__bf16)val[2], b3 = (__bf16)val[3];
+        if (vec && col + 3 < N) {
+          const uint2 pk = {(unsigned)__builtin_bit_cast(uint16_t, b0) | ((unsigned)__builtin_bit_cast(uint16_t, b1) << 16),
+                            (unsigned)__builtin_bit_cast(uint16_t, b2) | ((unsigned)__builtin_bit_cast(uint16_t, b3) << 16)};
+          __builtin_nontemporal_store(pk.x, reinterpret_cast<unsigned*>(dst));
+          __builtin_nontemporal_store(pk.y, reinterpret_cast<unsigned*>(dst) + 1);
+        } else {
+          const __bf16 bv[4] = {b0, b1, b2, b3};
+          for (int q = 0; q < 4; ++q)
+            if (col + q < N) dst[q] = bv[q];
+        }
+      } else {
+        float* dst = reinterpret_cast<float*>(Yv) + (size_t)row * N + col;
+        if (vec && col + 3 < N) {
+          __builtin_nontemporal_store(val, reinterpret_cast<v4f*>(dst));
+        } else {
+          for (int q = 0; q < 4; ++q)
+            if (col + q < N) dst[q] = val[q];
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // slab read back before the next one overwrites it
+  }
+}
+
+std::atomic<int> g_attr_done[64];
+
+template <bool B>
+hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws, int M, int N, int K,
+                  void* Y, hipStream_t st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  auto kern = gemm_mxfp4_ring<B>;
+  if (dev >= 0 && dev < 64 && !g_attr_done[dev].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    g_attr_done[dev].store(1, std::memory_order_release);
+  }
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int T = tiles_m * tiles_n;
+  hipLaunchKernelGGL(kern, dim3(T), dim3(NT), LDS_BYTES, st, Xq, Xs, Wq, Ws, Y, M, N, K, tiles_m, tiles_n,
+                     (T % 8 == 0) ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace fp4
+
+bool fp4_gemm_mxfp4_ring_fits(int64_t M, int64_t N, int64_t K) {
+  return K % 512 == 0 && M >= 256 && N >= 256;
+}
+
+hipError_t fp4_launch_gemm_mxfp4_ring(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                                      int64_t M, int64_t N, int64_t K, void* Y, int out_bf16, hipStream_t st) {
+  return out_bf16 ? fp4::launch<true>(Xq, Xs, Wq, Ws, (int)M, (int)N, (int)K, Y, st)
+                  : fp4::launch<false>(Xq, Xs, Wq, Ws, (int)M, (int)N, (int)K, Y, st);
+}

@@ -20,6 +20,7 @@ name       X (bf16)                                                     W
 tiny       16x256 N(0,1), 4 outlier channels x50                        256x256 N(0,0.02)
 decode     M in {1,4,16} x 4096, Student-t(5), 1% channels x30           4096x4096 N(0,0.02)
 prefill    2048x4096, Student-t(5), 1% channels x30                      14336x4096 N(0,0.02)
+           (NVFP4 block 16 as stated; also run in MXFP4 block 32, Y bf16)
 large      8192x8192 N(0,1), 0.5% channels x100                          28672x8192 N(0,0.02)
 stress     16384x8192 Student-t(3) x exp(N(0,1)) per channel            (none)
 =========  ==========================================================  =====
@@ -84,9 +85,11 @@ WORKLOADS = {
     "decode16": Workload("decode16", 2, 16, 4096, 4096, 32, "mxfp4", "t5", 0.01, 30.0),
     "prefill_nv": Workload("prefill_nv", 3, 2048, 4096, 14336, 16, "nvfp4", "t5", 0.01, 30.0,
                            out_dtype="bf16"),
-    # The prefill shape (K=4096, N=14336) run in MXFP4 with Hadamard block 32 and
-    # the same activation model: the headline linear-layer workload.
-    "prefill_mx": Workload("prefill_mx", 6, 2048, 4096, 14336, 32, "mxfp4", "t5", 0.01, 30.0),
+    # The prefill shape (K=4096, N=14336) run in MXFP4 with Hadamard block 32, the same
+    # activation model and the same output convention (float32 accumulation, bf16 Y):
+    # the headline linear-layer workload.
+    "prefill_mx": Workload("prefill_mx", 6, 2048, 4096, 14336, 32, "mxfp4", "t5", 0.01, 30.0,
+                           out_dtype="bf16"),
     "prefill_mx_m4096": Workload("prefill_mx_m4096", 7, 4096, 4096, 14336, 32, "mxfp4", "t5",
                                  0.01, 30.0),
     "large": Workload("large", 4, 8192, 8192, 28672, 128, "mxfp4", "normal", 0.005, 100.0),

@@ -46,6 +46,37 @@ def test_unit_scales_bit_exact(M, N, K):
     assert np.array_equal(yb, O.bf16_rne_f64(ref))
 
 
+@pytest.mark.parametrize("M,N,K", [(512, 512, 1024), (300, 520, 512), (256, 261, 512), (777, 1000, 1536)])
+def test_large_tile_kernel_unit_scales_exact(M, N, K):
+    # shapes routed to the 256x256-tile kernel (K % 512 == 0, M, N >= 256), ragged edges included
+    rng = np.random.default_rng(M + N + K)
+    c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    xs = np.full((M, K // 32), 127, np.uint8)
+    ws = np.full((N, K // 32), 127, np.uint8)
+    ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "mxfp4")
+    say(f"case large-tile unit-scale exact M {M} N {N} K {K}")
+    args = (dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), "mxfp4")
+    y = B.fp4_linear(*args)
+    assert np.array_equal(host(y).astype(np.float64), ref)
+    yb = B.fp4_linear(*args, out_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.float()).astype(np.float64), O.bf16_rne_f64(ref))
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 768, 2048), (259, 300, 512)])
+def test_large_tile_kernel_random_scales(M, N, K):
+    rng = np.random.default_rng(7 * M + N)
+    c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    xs = rng.integers(110, 140, size=(M, K // 32)).astype(np.uint8)
+    ws = rng.integers(110, 140, size=(N, K // 32)).astype(np.uint8)
+    ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "mxfp4")
+    y = B.fp4_linear(dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), "mxfp4")
+    r = rel_fro(host(y), ref)
+    say(f"large-tile random scales M {M} N {N} K {K}: rel fro {r:.3e}")
+    assert r <= 1e-6
+
+
 def test_scale_byte_extremes_exact():
     # per-group scales spread over a wide exponent range, still exact in float32
     rng = np.random.default_rng(3)
