@@ -44,7 +44,6 @@ constexpr int STAGE = (BM + BN) * BKB;   // 64 KB
 constexpr int A_WL = BM / 8 / WAVES, B_WL = BN / 8 / WAVES;  // 1 KB DMA wave-loads per wave
 constexpr int SC_BYTES = (BM + BN) * 16;                     // scales of 2 stages
 constexpr int SC_WL = (BM + BN) / 64 / WAVES;
-constexpr int LOADS = A_WL + B_WL;
 constexpr int LDS_BYTES = NS * STAGE + 2 * SC_BYTES;         // 144 KB
 static_assert(A_WL * 8 * WAVES == BM && B_WL * 8 * WAVES == BN, "row split");
 static_assert(SC_WL * 64 * WAVES == BM + BN, "scale split");

@@ -10,7 +10,9 @@
 // the block maximum into (3, 6].
 //
 // Work decomposition: one lane owns one 32-element chunk of a row (64 bytes of
-// bf16 in, 16 bytes of packed codes out). A Hadamard block of b <= 32 lives in
+// bf16 in, 16 bytes of packed codes out). A wave reads its 4 KB of X with fully
+// coalesced 16-byte loads and redistributes them through LDS, so each lane owns a
+// contiguous chunk (per-lane 64-byte strided loads reached only ~55% of HBM peak). A Hadamard block of b <= 32 lives in
 // one lane's registers; b = 64 / 128 spans 2 / 4 adjacent lanes of a quad and
 // its last stages exchange values with DPP quad permutes. The transform follows
 // one fixed order (strides 1, 2, 4, ... then one multiply by fl32(1/sqrt(b)))
@@ -37,21 +39,54 @@ __device__ __forceinline__ uint32_t row_of(uint32_t gc, const RowMap& rm) {
   return (t + ((gc - t) >> 1)) >> (rm.shift - 1);
 }
 
-// Load the lane's 32 bf16 values and widen them to float32 (exact).
-__device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ X, int64_t ldx, uint32_t gc,
-                                           const RowMap& rm, bool contiguous, float v[32]) {
-  const uint16_t* p;
-  if (contiguous) {
-    p = X + (size_t)gc * 32;
-  } else {
-    uint32_t row = row_of(gc, rm);
-    uint32_t kc = gc - row * rm.cpr;
-    p = X + (size_t)row * (size_t)ldx + (size_t)kc * 32;
-  }
-  const v4u* q = reinterpret_cast<const v4u*>(p);
+// Per-wave LDS staging area: 64 lanes x 64 bytes, padded so that both the coalesced
+// writes and the per-lane reads below are free of bank conflicts.
+constexpr int kStage = 4 * 68;  // 16-byte slots per wave
+
+template <bool CONTIG>
+__device__ __forceinline__ const uint16_t* chunk_ptr(const uint16_t* __restrict__ X, int64_t ldx, uint32_t gc,
+                                                     const RowMap& rm) {
+  if constexpr (CONTIG) return X + (size_t)gc * 32;
+  const uint32_t row = row_of(gc, rm);
+  return X + (size_t)row * (size_t)ldx + (size_t)(gc - row * rm.cpr) * 32;
+}
+
+// The wave's four coalesced 16-byte loads: instruction j covers 1 KB, part (lane % 4) of chunk
+// wbase + 16 j + lane / 4. Past the end the chunk index is clamped to the last chunk, so every
+// address stays inside X and all four loads are in flight before the first LDS write.
+template <bool CONTIG>
+__device__ __forceinline__ void load_wave(const uint16_t* __restrict__ X, int64_t ldx, uint32_t wbase, uint32_t total,
+                                          const RowMap& rm, v4u r[4]) {
+  const uint32_t lane = threadIdx.x & 63;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    v4u w = __builtin_nontemporal_load(q + j);
+    const uint32_t owner = min(wbase + 16 * j + (lane >> 2), total - 1);
+    r[j] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(chunk_ptr<CONTIG>(X, ldx, owner, rm)) + (lane & 3));
+  }
+}
+
+// Load the lane's 32 bf16 values and widen them to float32 (exact). The wave reads its 64
+// chunks with fully coalesced loads and transposes them through LDS, so that each lane ends up
+// with its own 64 contiguous bytes. Every lane of the wave must call this (lanes whose chunk
+// is past the end still load for the others); stage is the wave's LDS area.
+__device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ X, int64_t ldx, uint32_t gc, uint32_t total,
+                                           const RowMap& rm, bool contiguous, v4u* stage, float v[32]) {
+  const uint32_t lane = threadIdx.x & 63, wbase = gc - lane;
+  v4u r[4];
+  if (contiguous)
+    load_wave<true>(X, ldx, wbase, total, rm, r);
+  else
+    load_wave<false>(X, ldx, wbase, total, rm, r);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) stage[(16 * j + (lane >> 2)) + (lane & 3) * 68] = r[j];
+  // The area is private to the wave: waiting for its own LDS writes (lgkmcnt(0)) is enough,
+  // and the empty asm keeps the compiler from moving the reads above the writes.
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const v4u w = stage[lane + j * 68];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       v[8 * j + 2 * t] = bf16_lo(w[t]);
@@ -117,10 +152,11 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_mx(const uint16_t* __re
                                                             RowMap rm, uint32_t total, int contiguous,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
+  __shared__ __attribute__((aligned(16))) v4u stage[kThreads / 64][kStage];
   const uint32_t gc = blockIdx.x * kThreads + threadIdx.x;
-  if (gc >= total) return;  // whole quads leave together (total % (B/32) == 0)
   float v[32];
-  load_chunk(X, ldx, gc, rm, contiguous != 0, v);
+  load_chunk(X, ldx, gc, total, rm, contiguous != 0, stage[threadIdx.x >> 6], v);
+  if (gc >= total) return;  // whole quads leave together (total % (B/32) == 0)
   fwht<B>(v);
   const float c = __uint_as_float(hadamard_constant_bits(B));
   float amax = 0.f;
@@ -154,11 +190,12 @@ template <int B>
 __global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restrict__ X, int64_t ldx,
                                                         RowMap rm, uint32_t total, int contiguous,
                                                         unsigned* __restrict__ amax_bits) {
+  __shared__ __attribute__((aligned(16))) v4u stage[kThreads / 64][kStage];
   const uint32_t gc = blockIdx.x * kThreads + threadIdx.x;
   float m = 0.f;
+  float v[32];
+  load_chunk(X, ldx, gc, total, rm, contiguous != 0, stage[threadIdx.x >> 6], v);
   if (gc < total) {
-    float v[32];
-    load_chunk(X, ldx, gc, rm, contiguous != 0, v);
     fwht<B>(v);
 #pragma unroll
     for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
@@ -177,10 +214,11 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_nv(const uint16_t* __re
                                                             const unsigned* __restrict__ amax_bits,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
+  __shared__ __attribute__((aligned(16))) v4u stage[kThreads / 64][kStage];
   const uint32_t gc = blockIdx.x * kThreads + threadIdx.x;
-  if (gc >= total) return;
   float v[32];
-  load_chunk(X, ldx, gc, rm, contiguous != 0, v);
+  load_chunk(X, ldx, gc, total, rm, contiguous != 0, stage[threadIdx.x >> 6], v);
+  if (gc >= total) return;
   fwht<B>(v);
   const float c = __uint_as_float(hadamard_constant_bits(B));
 #pragma unroll
