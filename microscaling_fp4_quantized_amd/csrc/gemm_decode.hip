@@ -1,0 +1,113 @@
+// Decode-shaped W4A4 MXFP4 GEMM for gfx950 (M <= 16 rows of activations).
+//
+// "Bridging the Gap Between Promise and Performance for Microscaling FP4
+// Quantization" (gist.science, German edition), Technische Zusammenfassung §2
+// "GPU-Kernel-Unterstützung (QuTLASS)": the 4-bit matmul of the online path,
+// here in its token-generation shape, where W (N x K codes + scales) is the only
+// large operand and the product is bound by HBM bandwidth on W.
+//
+// Design for CDNA4:
+//  * One workgroup owns 16 output features (16 rows of W) and all of K; its 4 waves
+//    split the 128-wide K steps round-robin and are reduced through LDS at the end.
+//  * Each step is one v_mfma_scale_f32_16x16x128_f8f6f4 with W as the row operand and
+//    X as the column operand: lane l carries row l % 16 and the 32-element group l / 16
+//    of the step (16 bytes of codes, one E8M0 byte), so the output fragment gives each
+//    lane 4 consecutive features of one token.
+//  * Every load of a wave's steps is issued before its first MFMA (up to 8 steps, 8 KB of
+//    W per wave in flight), so the whole of W is requested at once for K <= 4096 and the
+//    kernel runs at the HBM rate instead of the MFMA rate. X rows past M repeat row M-1
+//    (their outputs are discarded); W rows past N repeat row N-1 likewise.
+#include "common.hpp"
+
+namespace fp4 {
+namespace {
+
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = kDecWaves * 64;
+constexpr int kDecBatch = 8;  // K steps per wave kept in flight
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kDecThreads) void gemm_mxfp4_decode(const uint8_t* __restrict__ Xq,
+                                                                 const uint8_t* __restrict__ Xs,
+                                                                 const uint8_t* __restrict__ Wq,
+                                                                 const uint8_t* __restrict__ Ws,
+                                                                 void* __restrict__ Yv, int M, int N, int K) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int r = lane & 15, g = lane >> 4;
+  const size_t KB = (size_t)K / 2, KS = (size_t)K / 32;
+  const int steps = K / 128;
+  const uint8_t* wp = Wq + (size_t)min(n0 + r, N - 1) * KB + 16 * g;  // step t at + 64 t
+  const uint8_t* xp = Xq + (size_t)min(r, M - 1) * KB + 16 * g;
+  const uint8_t* wsp = Ws + (size_t)min(n0 + r, N - 1) * KS + g;      // step t at + 4 t
+  const uint8_t* xsp = Xs + (size_t)min(r, M - 1) * KS + g;
+
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int t0 = wave; t0 < steps; t0 += kDecWaves * kDecBatch) {
+    v4u wa[kDecBatch], xb[kDecBatch];
+    unsigned ws[kDecBatch], xs[kDecBatch];
+#pragma unroll
+    for (int u = 0; u < kDecBatch; ++u) {
+      const int t = min(t0 + u * kDecWaves, steps - 1);  // in bounds; unused steps are skipped below
+      wa[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wp + 64 * (size_t)t));
+      xb[u] = *reinterpret_cast<const v4u*>(xp + 64 * (size_t)t);
+      ws[u] = wsp[4 * (size_t)t];
+      xs[u] = xsp[4 * (size_t)t];
+    }
+#pragma unroll
+    for (int u = 0; u < kDecBatch; ++u) {
+      if (t0 + u * kDecWaves < steps) {  // wave-uniform
+        const v8i a = v8i{(int)wa[u][0], (int)wa[u][1], (int)wa[u][2], (int)wa[u][3], 0, 0, 0, 0};
+        const v8i b = v8i{(int)xb[u][0], (int)xb[u][1], (int)xb[u][2], (int)xb[u][3], 0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 4, 0, (int)ws[u], 0, (int)xs[u]);
+      }
+    }
+  }
+
+  // fixed-order reduction over the waves' K slices
+  __shared__ v4f red[kDecWaves][64];
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) acc += red[w][lane];
+  // lane holds D[n0 + 4g + i][m = r], i = 0..3: four consecutive features of token r
+  const int m = r, n = n0 + 4 * g;
+  if (m >= M) return;
+  const bool vec = (N & 3) == 0 && n + 3 < N;
+  if constexpr (OUT_BF16) {
+    __bf16* dst = reinterpret_cast<__bf16*>(Yv) + (size_t)m * N + n;
+    const __bf16 b[4] = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
+    if (vec) {
+      const uint2 pk = {(unsigned)__builtin_bit_cast(uint16_t, b[0]) | ((unsigned)__builtin_bit_cast(uint16_t, b[1]) << 16),
+                        (unsigned)__builtin_bit_cast(uint16_t, b[2]) | ((unsigned)__builtin_bit_cast(uint16_t, b[3]) << 16)};
+      *reinterpret_cast<uint2*>(dst) = pk;
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (n + i < N) dst[i] = b[i];
+    }
+  } else {
+    float* dst = reinterpret_cast<float*>(Yv) + (size_t)m * N + n;
+    if (vec) {
+      *reinterpret_cast<v4f*>(dst) = acc;
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (n + i < N) dst[i] = acc[i];
+    }
+  }
+}
+
+}  // namespace
+}  // namespace fp4
+
+bool fp4_gemm_mxfp4_decode_fits(int64_t M, int64_t N, int64_t K) { return M <= 16 && K % 128 == 0 && N >= 1; }
+
+hipError_t fp4_launch_gemm_mxfp4_decode(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                                        int64_t M, int64_t N, int64_t K, void* Y, int out_bf16, hipStream_t st) {
+  const dim3 grid((unsigned)((N + 15) / 16)), block(fp4::kDecThreads);
+  if (out_bf16)
+    hipLaunchKernelGGL(fp4::gemm_mxfp4_decode<true>, grid, block, 0, st, Xq, Xs, Wq, Ws, Y, (int)M, (int)N, (int)K);
+  else
+    hipLaunchKernelGGL(fp4::gemm_mxfp4_decode<false>, grid, block, 0, st, Xq, Xs, Wq, Ws, Y, (int)M, (int)N, (int)K);
+  return hipGetLastError();
+}

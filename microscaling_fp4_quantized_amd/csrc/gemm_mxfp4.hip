@@ -192,6 +192,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_mxfp4_kernel(
 hipError_t fp4_launch_gemm_mxfp4(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
                                  const uint8_t* Ws, int64_t M, int64_t N, int64_t K, void* Y,
                                  int out_bf16, hipStream_t st) {
+  if (fp4_gemm_mxfp4_decode_fits(M, N, K)) return fp4_launch_gemm_mxfp4_decode(Xq, Xs, Wq, Ws, M, N, K, Y, out_bf16, st);
   if (fp4_gemm_mxfp4_ring_fits(M, N, K)) return fp4_launch_gemm_mxfp4_ring(Xq, Xs, Wq, Ws, M, N, K, Y, out_bf16, st);
   constexpr int BM = 128, BN = 128, WM = 64, WN = 64;
   using C = fp4::Cfg<BM, BN, WM, WN>;

@@ -201,10 +201,22 @@ __global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restri
     for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
     m *= __uint_as_float(hadamard_constant_bits(B));
   }
-  // wave reduction, then one atomic per wave
+  // Wave reduction, then workgroup reduction through LDS, then at most one atomic per
+  // workgroup. Same-address atomics serialise in L2, so a workgroup whose maximum does not
+  // exceed the value already there skips its atomic (the word only ever grows, so a stale
+  // read can only cause an unneeded atomic, never a missed one).
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0) atomicMax(amax_bits, __float_as_uint(m));
+  __shared__ float wmax[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) b = fmaxf(b, wmax[w]);
+    const unsigned bits = __float_as_uint(b);
+    if (bits > __atomic_load_n(amax_bits, __ATOMIC_RELAXED)) atomicMax(amax_bits, bits);
+  }
 }
 
 // NVFP4 pass 2: group scales and codes given T.

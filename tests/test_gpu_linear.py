@@ -46,6 +46,38 @@ def test_unit_scales_bit_exact(M, N, K):
     assert np.array_equal(yb, O.bf16_rne_f64(ref))
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 77, 128), (5, 300, 640), (16, 4096, 4096), (3, 130, 8192), (16, 18, 1152)])
+def test_decode_kernel_unit_scales_exact(M, N, K):
+    # M <= 16 runs the weight-streaming decode kernel (K split over waves, LDS reduction);
+    # K = 8192 takes two batches of in-flight loads per wave, N % 16 != 0 leaves ragged rows
+    rng = np.random.default_rng(3 * M + N + K)
+    c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    xs = np.full((M, K // 32), 127, np.uint8)
+    ws = np.full((N, K // 32), 127, np.uint8)
+    ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "mxfp4")
+    say(f"case decode-kernel unit-scale exact M {M} N {N} K {K}")
+    args = (dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), "mxfp4")
+    y = B.fp4_linear(*args)
+    assert np.array_equal(host(y).astype(np.float64), ref)
+    yb = B.fp4_linear(*args, out_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.float()).astype(np.float64), O.bf16_rne_f64(ref))
+
+
+def test_decode_kernel_random_scales():
+    rng = np.random.default_rng(99)
+    M, N, K = 7, 520, 2048
+    c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    xs = rng.integers(110, 140, size=(M, K // 32)).astype(np.uint8)
+    ws = rng.integers(110, 140, size=(N, K // 32)).astype(np.uint8)
+    ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "mxfp4")
+    y = B.fp4_linear(dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), "mxfp4")
+    r = rel_fro(host(y), ref)
+    say(f"decode kernel random scales rel fro {r:.3e}")
+    assert r <= 1e-6
+
+
 @pytest.mark.parametrize("M,N,K", [(512, 512, 1024), (300, 520, 512), (256, 261, 512), (777, 1000, 1536)])
 def test_large_tile_kernel_unit_scales_exact(M, N, K):
     # shapes routed to the 256x256-tile kernel (K % 512 == 0, M, N >= 256), ragged edges included
