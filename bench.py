@@ -80,6 +80,32 @@ def time_batch(fn, iters, torch):
     return start.elapsed_time(end) / iters
 
 
+def time_graph(fn, iters, torch):
+    """Average device time (ms) per call of fn(i) with `iters` calls captured in one HIP graph and
+    replayed between two events, so the host's launch rate does not bound kernels that run for a
+    few microseconds. The library launches on torch's current stream, which is the capture stream
+    inside torch.cuda.graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(iters):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters
+
+
 def cpu_baseline(wl, x_bits, w_bits):
     """The oracle (plain NumPy, untuned) on one full step of the workload."""
     from threadpoolctl import threadpool_info
@@ -105,6 +131,70 @@ def cpu_baseline(wl, x_bits, w_bits):
     }
 
 
+def extra_rows(B, WL, torch, dev):
+    """The other rows of the path, each timed over back-to-back launches on the library's stream:
+    NVFP4 rotate+quantize on the bandwidth-stress shape (two passes over X), the NVFP4 prefill
+    GEMM (bf16 MFMA after exact dequantization), and the decode-shaped MXFP4 GEMM (HBM-bound on W)."""
+    out = {}
+    # NVFP4 rotate+quantize, 16384 x 8192, block 32
+    sw = WL.WORKLOADS["stress_nv32"]
+    sx = WL.draw_x(sw)
+    bufs = [bf16_dev(sx, dev), bf16_dev(sx, dev)]
+    del sx
+    o = (torch.empty((sw.M, sw.K // 2), dtype=torch.uint8, device=dev),
+         torch.empty((sw.M, sw.K // 16), dtype=torch.uint8, device=dev),
+         torch.empty((1,), dtype=torch.float32, device=dev))
+    for i in range(3):
+        B.fp4_rotate_quantize(bufs[i & 1], sw.block, "nvfp4", out=o)
+    ms = time_batch(lambda i: B.fp4_rotate_quantize(bufs[i & 1], sw.block, "nvfp4", out=o), 20, torch)
+    nbytes = sw.M * sw.K * (2 + 2 + 0.5 + 1.0 / 16) + 8
+    out["rotate_quantize_nvfp4"] = {
+        "workload": "stress_nv32: X 16384x8192 bf16, block 32, NVFP4 (max pass + quantize pass)",
+        "us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_bytes": nbytes}
+    log(f"[bench] NVFP4 stress rotate+quantize {ms * 1e3:.1f} us = {out['rotate_quantize_nvfp4']['GB/s']:.0f} GB/s")
+    del bufs, o
+    # NVFP4 prefill GEMM, M=2048 K=4096 N=14336, Y bf16
+    wl = WL.WORKLOADS["prefill_nv"]
+    xq, xs, xts = B.fp4_rotate_quantize(bf16_dev(WL.draw_x(wl), dev), wl.block, "nvfp4")
+    wq, ws, wts = B.fp4_quantize_weights(bf16_dev(WL.draw_w(wl), dev), wl.block, "nvfp4")
+    y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        B.fp4_linear(xq, xs, wq, ws, "nvfp4", x_ts=xts, w_ts=wts, out_dtype=torch.bfloat16, out=y)
+    ms = time_batch(lambda i: B.fp4_linear(xq, xs, wq, ws, "nvfp4", x_ts=xts, w_ts=wts,
+                                           out_dtype=torch.bfloat16, out=y), 20, torch)
+    tf = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
+    out["gemm_nvfp4"] = {"workload": "prefill_nv: M=2048 K=4096 N=14336, block 16, Y bf16",
+                         "us": ms * 1e3, "TFLOP/s": tf, "frac_bf16_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+                         "frac_fp4_mfma_peak": tf / MFMA_FP4_PEAK_TFLOPS}
+    log(f"[bench] NVFP4 GEMM {ms * 1e3:.1f} us = {tf:.0f} TFLOP/s")
+    del xq, xs, wq, ws, y
+    # decode-shaped MXFP4 GEMM: W 4096x4096 streamed once per call
+    for name in ("decode1", "decode16"):
+        wl = WL.WORKLOADS[name]
+        xq, xs, _ = B.fp4_rotate_quantize(bf16_dev(WL.draw_x(wl), dev), wl.block, "mxfp4")
+        wq, ws, _ = B.fp4_quantize_weights(bf16_dev(WL.draw_w(wl), dev), wl.block, "mxfp4")
+        y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y)
+        ref = y.clone()
+        ms_calls = time_batch(lambda i: B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y), 50, torch)
+        y.zero_()
+        ms = time_graph(lambda i: B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y), 50, torch)
+        graph_ok = bool(torch.equal(y, ref))
+        wbytes = wl.N * wl.K * (0.5 + 1.0 / 32)
+        nbytes = wbytes + wl.M * wl.K * (0.5 + 1.0 / 32) + wl.M * wl.N * 4
+        out[f"gemm_{name}"] = {"workload": f"{name}: M={wl.M} K={wl.K} N={wl.N} MXFP4, Y fp32",
+                               "us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                               "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+                               "us_per_python_call": ms_calls * 1e3, "graph_replay_matches_eager": graph_ok,
+                               "note": "50 calls captured in one HIP graph; W (8.9 MB) stays in the 256 MB "
+                                       "Infinity Cache across calls"}
+        log(f"[bench] {name} GEMM {ms * 1e3:.2f} us in a graph = {out[f'gemm_{name}']['GB/s']:.0f} GB/s "
+            f"({ms_calls * 1e3:.2f} us per Python call; graph result matches eager: {graph_ok})")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +203,8 @@ def main():
     ap.add_argument("--workload", default="prefill_mx")
     ap.add_argument("--stress", default="stress_mx32", help="rotate+quantize HBM workload ('' to skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the NVFP4 and decode-shaped measurements reported beside the headline")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -285,6 +377,9 @@ def main():
             "avg_launch_us": s_ms * 1e3,
         }
         del bufs, outs
+
+    if not args.no_extra:
+        result["other_rows"] = extra_rows(B, WL, torch, dev)
 
     if not args.no_cpu:
         log("[bench] CPU oracle baseline ...")

@@ -19,8 +19,15 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp4.so")
 
-SOURCES = ["rotate_quant.hip", "gemm_mxfp4.hip", "gemm_mxfp4_ring.hip",
-    "gemm_decode.hip", "gemm_nvfp4.hip", "fp4_abi.cpp"]
+SOURCES = [
+    "rotate_quant.hip",
+    "gemm_mxfp4.hip",
+    "gemm_mxfp4_ring.hip",
+    "gemm_decode.hip",
+    "gemm_nvfp4.hip",
+    "gemm_nvfp4_ring.hip",
+    "fp4_abi.cpp",
+]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -76,6 +76,10 @@ hipError_t fp4_launch_gemm_mxfp4_decode(const uint8_t* Xq, const uint8_t* Xs, co
                                         int64_t M, int64_t N, int64_t K, void* Y, int out_bf16, hipStream_t stream);
 hipError_t fp4_launch_gemm_mxfp4_ring(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
                                       int64_t M, int64_t N, int64_t K, void* Y, int out_bf16, hipStream_t stream);
+bool fp4_gemm_nvfp4_ring_fits(int64_t M, int64_t N, int64_t K);
+hipError_t fp4_launch_gemm_nvfp4_ring(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const uint8_t* Wq,
+                                      const uint8_t* Ws, const float* w_ts, int64_t M, int64_t N, int64_t K, void* Y,
+                                      int out_bf16, hipStream_t stream);
 hipError_t fp4_launch_gemm_nvfp4(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts,
                                  const uint8_t* Wq, const uint8_t* Ws, const float* w_ts, int64_t M,
                                  int64_t N, int64_t K, void* Y, int out_bf16, hipStream_t stream);

@@ -7,24 +7,26 @@
 // large operand and the product is bound by HBM bandwidth on W.
 //
 // Design for CDNA4:
-//  * One workgroup owns 16 output features (16 rows of W) and all of K; its 4 waves
-//    split the 128-wide K steps round-robin and are reduced through LDS at the end.
+//  * One workgroup owns 16 output features (16 rows of W) and all of K; its 8 waves
+//    take batches of 4 consecutive 128-wide K steps round-robin and are reduced through
+//    LDS at the end, in a fixed order.
 //  * Each step is one v_mfma_scale_f32_16x16x128_f8f6f4 with W as the row operand and
 //    X as the column operand: lane l carries row l % 16 and the 32-element group l / 16
 //    of the step (16 bytes of codes, one E8M0 byte), so the output fragment gives each
 //    lane 4 consecutive features of one token.
-//  * Every load of a wave's steps is issued before its first MFMA (up to 8 steps, 8 KB of
-//    W per wave in flight), so the whole of W is requested at once for K <= 4096 and the
-//    kernel runs at the HBM rate instead of the MFMA rate. X rows past M repeat row M-1
+//  * Every load of a wave's batch is issued before its first MFMA (4 steps, 4 KB of W per
+//    wave, 32 KB per workgroup in flight), so the whole of W is requested at once for
+//    K <= 4096 and the kernel runs at the HBM rate instead of the MFMA rate. A batch's
+//    scales are 16 consecutive bytes of the row, read with one 16-byte load. X rows past M repeat row M-1
 //    (their outputs are discarded); W rows past N repeat row N-1 likewise.
 #include "common.hpp"
 
 namespace fp4 {
 namespace {
 
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * 64;
-constexpr int kDecBatch = 8;  // K steps per wave kept in flight
+constexpr int kDecBatch = 4;  // consecutive K steps per wave kept in flight
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kDecThreads) void gemm_mxfp4_decode(const uint8_t* __restrict__ Xq,
@@ -36,30 +38,34 @@ __global__ __launch_bounds__(kDecThreads) void gemm_mxfp4_decode(const uint8_t* 
   const int n0 = blockIdx.x * 16;
   const int r = lane & 15, g = lane >> 4;
   const size_t KB = (size_t)K / 2, KS = (size_t)K / 32;
-  const int steps = K / 128;
-  const uint8_t* wp = Wq + (size_t)min(n0 + r, N - 1) * KB + 16 * g;  // step t at + 64 t
+  const int steps = K / 128;  // 128-element steps; step t, lane group g: group 4t + g of the row
+  const uint8_t* wp = Wq + (size_t)min(n0 + r, N - 1) * KB + 16 * g;
   const uint8_t* xp = Xq + (size_t)min(r, M - 1) * KB + 16 * g;
-  const uint8_t* wsp = Ws + (size_t)min(n0 + r, N - 1) * KS + g;      // step t at + 4 t
-  const uint8_t* xsp = Xs + (size_t)min(r, M - 1) * KS + g;
+  const uint8_t* wsp = Ws + (size_t)min(n0 + r, N - 1) * KS;
+  const uint8_t* xsp = Xs + (size_t)min(r, M - 1) * KS;
+  const unsigned sh = 8u * (unsigned)g;
 
+  // the waves take consecutive batches of kDecBatch steps, round-robin over K
   v4f acc = {0.f, 0.f, 0.f, 0.f};
-  for (int t0 = wave; t0 < steps; t0 += kDecWaves * kDecBatch) {
+  for (int t0 = wave * kDecBatch; t0 < steps; t0 += kDecWaves * kDecBatch) {
     v4u wa[kDecBatch], xb[kDecBatch];
-    unsigned ws[kDecBatch], xs[kDecBatch];
 #pragma unroll
     for (int u = 0; u < kDecBatch; ++u) {
-      const int t = min(t0 + u * kDecWaves, steps - 1);  // in bounds; unused steps are skipped below
+      const int t = min(t0 + u, steps - 1);  // in bounds; unused steps are skipped below
       wa[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wp + 64 * (size_t)t));
       xb[u] = *reinterpret_cast<const v4u*>(xp + 64 * (size_t)t);
-      ws[u] = wsp[4 * (size_t)t];
-      xs[u] = xsp[4 * (size_t)t];
     }
+    // the batch's scale bytes 4 t0 .. 4 t0 + 15 of the row (steps % 4 == 0 keeps them in the row)
+    const int tb = min(t0, steps - kDecBatch);
+    const v4u wsv = *reinterpret_cast<const v4u*>(wsp + 4 * (size_t)tb);
+    const v4u xsv = *reinterpret_cast<const v4u*>(xsp + 4 * (size_t)tb);
 #pragma unroll
     for (int u = 0; u < kDecBatch; ++u) {
-      if (t0 + u * kDecWaves < steps) {  // wave-uniform
+      if (t0 + u < steps) {  // wave-uniform
         const v8i a = v8i{(int)wa[u][0], (int)wa[u][1], (int)wa[u][2], (int)wa[u][3], 0, 0, 0, 0};
         const v8i b = v8i{(int)xb[u][0], (int)xb[u][1], (int)xb[u][2], (int)xb[u][3], 0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 4, 0, (int)ws[u], 0, (int)xs[u]);
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 4, 0, (int)(wsv[u] >> sh), 0,
+                                                                (int)(xsv[u] >> sh));
       }
     }
   }
@@ -100,7 +106,7 @@ __global__ __launch_bounds__(kDecThreads) void gemm_mxfp4_decode(const uint8_t* 
 }  // namespace
 }  // namespace fp4
 
-bool fp4_gemm_mxfp4_decode_fits(int64_t M, int64_t N, int64_t K) { return M <= 16 && K % 128 == 0 && N >= 1; }
+bool fp4_gemm_mxfp4_decode_fits(int64_t M, int64_t N, int64_t K) { return M <= 16 && K % 512 == 0 && N >= 1; }
 
 hipError_t fp4_launch_gemm_mxfp4_decode(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
                                         int64_t M, int64_t N, int64_t K, void* Y, int out_bf16, hipStream_t st) {

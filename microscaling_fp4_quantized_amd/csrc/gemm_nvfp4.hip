@@ -181,6 +181,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_nvfp4_kernel(
 hipError_t fp4_launch_gemm_nvfp4(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts,
                                  const uint8_t* Wq, const uint8_t* Ws, const float* w_ts, int64_t M,
                                  int64_t N, int64_t K, void* Y, int out_bf16, hipStream_t st) {
+  if (fp4_gemm_nvfp4_ring_fits(M, N, K))
+    return fp4_launch_gemm_nvfp4_ring(Xq, Xs, x_ts, Wq, Ws, w_ts, M, N, K, Y, out_bf16, st);
   constexpr int BM = 128, BN = 128, WM = 64, WN = 64;
   using C = fp4::NvCfg<BM, BN, WM, WN>;
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);

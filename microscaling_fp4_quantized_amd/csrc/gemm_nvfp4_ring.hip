@@ -1,0 +1,238 @@
+// Large-tile W4A4 NVFP4 GEMM for gfx950: Y = s_tx s_tw sum_k (e2m1 d_x)(e2m1 d_w), 256x256 tiles.
+//
+// "Bridging the Gap Between Promise and Performance for Microscaling FP4
+// Quantization" (gist.science, Spanish edition), Resumen técnico §2.B item 2
+// (NVFP4 carries E4M3 group scales and a tensor scale) and §2.C (4-bit matmul).
+//
+// The gfx950 scaled MFMA accepts power-of-two scales per 32 K elements only, so the
+// NVFP4 group scale (E4M3, 16 elements) is folded into the operand instead: e2m1 * d
+// has at most 6 significant bits and lies in [2^-10, 2688], so it is exact in bf16, and
+// the product runs on v_mfma_f32_32x32x16_bf16 with float32 accumulation. The two
+// tensor scales multiply the result in the epilogue.
+//
+// Design for CDNA4:
+//  * 8 waves (2 x 4), 128 x 64 outputs per wave as 4 x 2 fragments of 32 x 32.
+//  * K advances 64 per stage. The codes (16 bytes = 32 elements + their two scale bytes
+//    per thread and chunk) are loaded into registers two stages ahead; after stage s is
+//    multiplied, stage s+1 is dequantized once per workgroup into a bf16 tile in the
+//    other LDS buffer (pitch 144 bytes: the fragment reads hit distinct banks).
+//  * W is the row operand and X the column operand of every MFMA, so each lane ends with
+//    four consecutive output features of one token and stores them with one 8- or 16-byte
+//    store.
+//  * Workgroup i runs on XCD i % 8; each XCD takes a contiguous range of tiles, walked
+//    M-fastest within groups of 8 tile rows.
+#include <atomic>
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace fp4 {
+namespace {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 256, BN = 256;
+constexpr int WGM = 2, WGN = 4;
+constexpr int WAVES = WGM * WGN, NT = WAVES * 64;
+constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+constexpr int BKE = 64;                   // K elements per stage
+constexpr int KSTEPS = BKE / 16;          // 32x32x16 steps per stage
+constexpr int PITCH = BKE * 2 + 16;       // bytes per bf16 row in LDS (padded)
+constexpr int STAGE = (BM + BN) * PITCH;  // 73728 bytes
+constexpr int LDS_BYTES = 2 * STAGE;      // 144 KB
+constexpr int CHUNKS = (BM + BN) * 2;     // 32-element chunks per stage
+constexpr int CPT = CHUNKS / NT;          // chunks per thread
+static_assert(CPT * NT == CHUNKS, "chunk split");
+
+// 32 E2M1 codes (16 bytes) with their two E4M3 group scales -> 32 exact bf16 (64 bytes).
+__device__ __forceinline__ void dequant32(const v4u codes, unsigned sc2, v4u out[4]) {
+  const float d0 = e4m3_value(sc2 & 0xFFu), d1 = e4m3_value((sc2 >> 8) & 0xFFu);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float d = w < 2 ? d0 : d1;
+    const v2f f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[w], 1.0f, 0);
+    const v2f f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[w], 1.0f, 1);
+    const v2f f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[w], 1.0f, 2);
+    const v2f f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[w], 1.0f, 3);
+    // the products are exact, so their bf16 is the top half of the float32
+    out[w][0] = __builtin_amdgcn_perm(__float_as_uint(f0[1] * d), __float_as_uint(f0[0] * d), 0x07060302u);
+    out[w][1] = __builtin_amdgcn_perm(__float_as_uint(f1[1] * d), __float_as_uint(f1[0] * d), 0x07060302u);
+    out[w][2] = __builtin_amdgcn_perm(__float_as_uint(f2[1] * d), __float_as_uint(f2[0] * d), 0x07060302u);
+    out[w][3] = __builtin_amdgcn_perm(__float_as_uint(f3[1] * d), __float_as_uint(f3[0] * d), 0x07060302u);
+  }
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(NT) void gemm_nvfp4_ring(const uint8_t* __restrict__ Xq, const uint8_t* __restrict__ Xs,
+                                                      const float* __restrict__ x_ts, const uint8_t* __restrict__ Wq,
+                                                      const uint8_t* __restrict__ Ws, const float* __restrict__ w_ts,
+                                                      void* __restrict__ Yv, int M, int N, int K, int tiles_m,
+                                                      int tiles_n, int xcd_remap) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = tiles_m * tiles_n;
+  int L = blockIdx.x;
+  if (xcd_remap) L = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+  constexpr int GM = 8;
+  const int first_m = (L / (GM * tiles_n)) * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int m0 = (first_m + (L % gsize)) * BM;
+  const int n0 = ((L % (GM * tiles_n)) / gsize) * BN;
+  const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
+  const size_t KB = (size_t)K / 2, KS = (size_t)K / 16;
+  const int nst = K / BKE;
+
+  // chunk c of a stage: tile row c / 2 (A rows first, then B rows), half c % 2 of the row's 64 elements
+  const uint8_t* csrc[CPT];
+  const uint8_t* ssrc[CPT];
+  int ldst[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + i * NT, r = c >> 1, h = c & 1;
+    const bool isA = r < BM;
+    const size_t row = isA ? (size_t)min(m0 + r, M - 1) : (size_t)min(n0 + r - BM, N - 1);
+    csrc[i] = (isA ? Xq : Wq) + row * KB + h * 16;
+    ssrc[i] = (isA ? Xs : Ws) + row * KS + h * 2;
+    ldst[i] = r * PITCH + h * 64;
+  }
+  // two stages of codes in registers: stage s+2 is requested while stage s is multiplied
+  v4u cr[2][CPT];
+  unsigned sr[2][CPT];
+  // register set P holds the stages with parity P (the stage count is even, so the loop below
+  // is unrolled by two and every index into the register arrays is a constant)
+  auto gload = [&](auto P, int s) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      cr[P][i] = *reinterpret_cast<const v4u*>(csrc[i] + (size_t)s * (BKE / 2));
+      sr[P][i] = *reinterpret_cast<const uint16_t*>(ssrc[i] + (size_t)s * (BKE / 16));
+    }
+  };
+  auto lstore = [&](auto P) {  // dequantize register set P into LDS buffer P
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      v4u o[4];
+      dequant32(cr[P][i], sr[P][i], o);
+      v4u* dst = reinterpret_cast<v4u*>(smem + P * STAGE + ldst[i]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = o[q];
+    }
+  };
+
+  v16f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int fr = lane & 31, fh = lane >> 5;
+  auto stage = [&](auto P, int s) {  // multiply stage s (LDS buffer P = s & 1)
+    const uint8_t* buf = smem + P * STAGE;
+    // Register set P was stored to LDS before the last barrier. The prefetch and the store below
+    // run unconditionally (the stage index is clamped, and the last stage's extra store lands in
+    // a buffer nobody reads again) so the whole stage is one block in which the compiler can
+    // interleave the dequantization with the MFMAs.
+    gload(P, min(s + 2, nst - 1));
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      // lane l: row l % 32 of the fragment, K elements 16 ks + 8 (l / 32) .. + 7
+      const int off = ks * 32 + fh * 16;
+      v8bf a[FM], b[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        a[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(buf + (wm0 + i * 32 + fr) * PITCH + off));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        b[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(buf + (BM + wn0 + j * 32 + fr) * PITCH + off));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);  // D[n][m]
+    }
+    lstore(std::integral_constant<int, 1 - P>{});
+    __syncthreads();
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  gload(P0{}, 0);
+  gload(P1{}, 1);
+  lstore(P0{});
+  __syncthreads();
+  for (int s = 0; s < nst; s += 2) {
+    stage(P0{}, s);
+    stage(P1{}, s + 1);
+  }
+
+  // acc[i][j][4q + r] = Y[m][n + r] with m = wm0 + 32 i + l % 32, n = wn0 + 32 j + 8 q + 4 (l / 32)
+  const float ts = x_ts[0] * w_ts[0];
+  const bool vec = (N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm0 + i * 32 + fr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn0 + j * 32 + 8 * q + 4 * fh;
+        const float y[4] = {acc[i][j][4 * q] * ts, acc[i][j][4 * q + 1] * ts, acc[i][j][4 * q + 2] * ts,
+                            acc[i][j][4 * q + 3] * ts};
+        if constexpr (OUT_BF16) {
+          __bf16* dst = reinterpret_cast<__bf16*>(Yv) + (size_t)m * N + n;
+          if (vec && n + 3 < N) {
+            const uint2 pk = {(unsigned)__builtin_bit_cast(uint16_t, (__bf16)y[0]) |
+                                  ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)y[1]) << 16),
+                              (unsigned)__builtin_bit_cast(uint16_t, (__bf16)y[2]) |
+                                  ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)y[3]) << 16)};
+            *reinterpret_cast<uint2*>(dst) = pk;
+          } else {
+            for (int r = 0; r < 4; ++r)
+              if (n + r < N) dst[r] = (__bf16)y[r];
+          }
+        } else {
+          float* dst = reinterpret_cast<float*>(Yv) + (size_t)m * N + n;
+          if (vec && n + 3 < N) {
+            *reinterpret_cast<v4f*>(dst) = v4f{y[0], y[1], y[2], y[3]};
+          } else {
+            for (int r = 0; r < 4; ++r)
+              if (n + r < N) dst[r] = y[r];
+          }
+        }
+      }
+  }
+}
+
+std::atomic<int> g_attr_done[64];
+
+template <bool B>
+hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const uint8_t* Wq, const uint8_t* Ws,
+                  const float* w_ts, int M, int N, int K, void* Y, hipStream_t st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  auto kern = gemm_nvfp4_ring<B>;
+  if (dev >= 0 && dev < 64 && !g_attr_done[dev].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    g_attr_done[dev].store(1, std::memory_order_release);
+  }
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int T = tiles_m * tiles_n;
+  hipLaunchKernelGGL(kern, dim3(T), dim3(NT), LDS_BYTES, st, Xq, Xs, x_ts, Wq, Ws, w_ts, Y, M, N, K, tiles_m,
+                     tiles_n, (T % 8 == 0) ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace fp4
+
+bool fp4_gemm_nvfp4_ring_fits(int64_t M, int64_t N, int64_t K) { return K % 64 == 0 && M >= 256 && N >= 256; }
+
+hipError_t fp4_launch_gemm_nvfp4_ring(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const uint8_t* Wq,
+                                      const uint8_t* Ws, const float* w_ts, int64_t M, int64_t N, int64_t K, void* Y,
+                                      int out_bf16, hipStream_t st) {
+  return out_bf16 ? fp4::launch<true>(Xq, Xs, x_ts, Wq, Ws, w_ts, (int)M, (int)N, (int)K, Y, st)
+                  : fp4::launch<false>(Xq, Xs, x_ts, Wq, Ws, w_ts, (int)M, (int)N, (int)K, Y, st);
+}

@@ -77,6 +77,7 @@ __device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ X, int64
     load_wave<true>(X, ldx, wbase, total, rm, r);
   else
     load_wave<false>(X, ldx, wbase, total, rm, r);
+  asm volatile("" ::: "memory");  // earlier reads of the area (a previous chunk) stay before these writes
 #pragma unroll
   for (int j = 0; j < 4; ++j) stage[(16 * j + (lane >> 2)) + (lane & 3) * 68] = r[j];
   // The area is private to the wave: waiting for its own LDS writes (lgkmcnt(0)) is enough,
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_mx(const uint16_t* __re
 // NVFP4 pass 1: T = max |y| over the tensor, accumulated with an integer
 // atomic max on the float bits (non-negative floats order like their bits).
 // max |fl32(z c)| = fl32(max|z| c) since rounding is monotone, so the final
-// multiply is applied once per lane.
+// multiply is applied once per chunk.
 // ---------------------------------------------------------------------------
 __global__ void clear_word(unsigned* p) {
   if (threadIdx.x == 0) *p = 0u;
@@ -191,15 +192,21 @@ __global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restri
                                                         RowMap rm, uint32_t total, int contiguous,
                                                         unsigned* __restrict__ amax_bits) {
   __shared__ __attribute__((aligned(16))) v4u stage[kThreads / 64][kStage];
-  const uint32_t gc = blockIdx.x * kThreads + threadIdx.x;
+  // Grid-stride over the chunks (the grid is capped at a few workgroups per CU), so each
+  // workgroup pays the reduction and the atomic below once for many chunks.
   float m = 0.f;
-  float v[32];
-  load_chunk(X, ldx, gc, total, rm, contiguous != 0, stage[threadIdx.x >> 6], v);
-  if (gc < total) {
-    fwht<B>(v);
+  const float c = __uint_as_float(hadamard_constant_bits(B));
+  for (uint32_t base = blockIdx.x * kThreads; base < total; base += gridDim.x * kThreads) {
+    const uint32_t gc = base + threadIdx.x;
+    float v[32];
+    load_chunk(X, ldx, gc, total, rm, contiguous != 0, stage[threadIdx.x >> 6], v);
+    if (gc < total) {
+      fwht<B>(v);
+      float a = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
-    m *= __uint_as_float(hadamard_constant_bits(B));
+      for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
+      m = fmaxf(m, a * c);
+    }
   }
   // Wave reduction, then workgroup reduction through LDS, then at most one atomic per
   // workgroup. Same-address atomics serialise in L2, so a workgroup whose maximum does not
@@ -215,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restri
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) b = fmaxf(b, wmax[w]);
     const unsigned bits = __float_as_uint(b);
-    if (bits > __atomic_load_n(amax_bits, __ATOMIC_RELAXED)) atomicMax(amax_bits, bits);
+    if (bits > __hip_atomic_load(amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(amax_bits, bits);
   }
 }
 
@@ -306,7 +313,8 @@ hipError_t launch_b(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int fm
   }
   unsigned* amax = reinterpret_cast<unsigned*>(ts);
   hipLaunchKernelGGL(clear_word, dim3(1), dim3(64), 0, st, amax);
-  hipLaunchKernelGGL(rotate_amax<B>, grid, block, 0, st, X, ldx, rm, total, contiguous, amax);
+  const dim3 grid_max(grid.x < 2048u ? grid.x : 2048u);  // 8 workgroups per CU, grid-stride
+  hipLaunchKernelGGL(rotate_amax<B>, grid_max, block, 0, st, X, ldx, rm, total, contiguous, amax);
   hipLaunchKernelGGL(rotate_quant_nv<B>, grid, block, 0, st, X, ldx, rm, total, contiguous, amax, codes,
                      scales);
   hipLaunchKernelGGL(finish_tensor_scale, dim3(1), dim3(64), 0, st, ts);

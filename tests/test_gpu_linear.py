@@ -46,10 +46,11 @@ def test_unit_scales_bit_exact(M, N, K):
     assert np.array_equal(yb, O.bf16_rne_f64(ref))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 77, 128), (5, 300, 640), (16, 4096, 4096), (3, 130, 8192), (16, 18, 1152)])
+@pytest.mark.parametrize("M,N,K", [(1, 77, 512), (5, 300, 1536), (16, 4096, 4096), (3, 130, 8192), (16, 18, 2560)])
 def test_decode_kernel_unit_scales_exact(M, N, K):
-    # M <= 16 runs the weight-streaming decode kernel (K split over waves, LDS reduction);
-    # K = 8192 takes two batches of in-flight loads per wave, N % 16 != 0 leaves ragged rows
+    # M <= 16 with K % 512 == 0 runs the weight-streaming decode kernel (K split over 8 waves in
+    # batches of 4 steps, LDS reduction); K = 8192 gives each wave two batches, K = 1536 and 2560
+    # leave some waves idle, N % 16 != 0 leaves ragged weight rows
     rng = np.random.default_rng(3 * M + N + K)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
@@ -66,7 +67,7 @@ def test_decode_kernel_unit_scales_exact(M, N, K):
 
 def test_decode_kernel_random_scales():
     rng = np.random.default_rng(99)
-    M, N, K = 7, 520, 2048
+    M, N, K = 7, 520, 3072
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
     xs = rng.integers(110, 140, size=(M, K // 32)).astype(np.uint8)
@@ -121,6 +122,44 @@ def test_scale_byte_extremes_exact():
     y = B.fp4_linear(dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), "mxfp4")
     r = rel_fro(host(y), ref)
     say(f"scale extremes rel fro {r:.3e}")
+    assert r <= 1e-6
+
+
+def dev_f32(v):
+    return torch.tensor([v], dtype=torch.float32).cuda()
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (512, 768, 1024), (300, 520, 384), (777, 1000, 1536)])
+def test_nv_large_tile_kernel_unit_scales_exact(M, N, K):
+    # NVFP4 shapes routed to the 256x256-tile kernel (M, N >= 256): group scales 1.0 (E4M3 code
+    # 0x38) and tensor scales 1.0 make every product a multiple of 1/4 and every sum exact
+    rng = np.random.default_rng(5 * M + N + K)
+    c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    xs = np.full((M, K // 16), 0x38, np.uint8)
+    ws = np.full((N, K // 16), 0x38, np.uint8)
+    ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "nvfp4", 1.0, 1.0)
+    say(f"case NV large-tile unit-scale exact M {M} N {N} K {K}")
+    args = (dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), "nvfp4")
+    y = B.fp4_linear(*args, x_ts=dev_f32(1.0), w_ts=dev_f32(1.0))
+    assert np.array_equal(host(y).astype(np.float64), ref)
+    yb = B.fp4_linear(*args, x_ts=dev_f32(1.0), w_ts=dev_f32(1.0), out_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.float()).astype(np.float64), O.bf16_rne_f64(ref))
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 768, 2048), (259, 300, 512)])
+def test_nv_large_tile_kernel_random_scales(M, N, K):
+    rng = np.random.default_rng(11 * M + N)
+    c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    xs = rng.integers(0, 0x7F, size=(M, K // 16)).astype(np.uint8)  # every finite E4M3 code, subnormals included
+    ws = rng.integers(0, 0x7F, size=(N, K // 16)).astype(np.uint8)
+    xt, wt = 0.0123, 3.5e-3
+    ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "nvfp4", np.float32(xt), np.float32(wt))
+    y = B.fp4_linear(dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), "nvfp4",
+                     x_ts=dev_f32(xt), w_ts=dev_f32(wt))
+    r = rel_fro(host(y), ref)
+    say(f"NV large-tile random scales M {M} N {N} K {K}: rel fro {r:.3e}")
     assert r <= 1e-6
 
 
