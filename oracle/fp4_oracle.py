@@ -69,6 +69,31 @@ R8  Packing: byte j of a row holds element 2j in its low nibble and element
     2j+1 in its high nibble; scales are row-major [rows, K/g].
 R9  The GEMM reference is the exact product of the dequantized operands,
     formed in float64: Y64 = dq(Xq) @ dq(Wq)^T, no bias.
+
+Variants (each is a flag of the same step; the standard path above is unchanged):
+
+R12 OCP floor rule (MXFP4): e = floor(log2 alpha_max) - 2, so the group maximum lands in
+    [4, 8) and elements above 6 saturate. The pages call the (3, 6] mapping standard; this
+    is the other common reading of an MX scale and is offered for comparison.
+R13 Overflow-aware scaling (MXFP4, [UNVEIL-nl] Methodologie, 1. OAS): start from the
+    standard exponent; when alpha_max / 2^e lies in (3, 3.5] use e - 1, so the maximum
+    lands in (6, 7] and saturates to 6 while every smaller element gets twice the
+    resolution. "Doubling the scale factor" in the page is read as doubling the scaled
+    values, which is what moves (3, 3.5] to (6, 7].
+R14 Scale fitting ([BRIDGE-de] §2 "Einführung von MR-GPTQ", item 2: MXFP4 scales fitted to
+    the data range, NVFP4 scales optimised for E4M3 precision). The pages give no
+    procedure; the reading taken is a data-free per-group search: among the standard
+    scale and its two neighbours (MXFP4: e - 1, e + 1; NVFP4: the adjacent E4M3 codes,
+    tensor scale unchanged) keep the one with the least squared error of the group.
+    The error is formed in float32, in element order: d_i = fl32(y_i - deq_i),
+    acc = fl32(acc + fl32(d_i * d_i)), with deq_i = e2m1 * 2^e (MX, exact) or
+    fl32(e2m1 * S) with S = fl32(d * s_t) (NV). Candidates are tried in the order
+    standard, smaller, larger and replace the current one only when strictly better.
+    Meant for weights (offline), where the extra work is paid once.
+R15 Randomized block Hadamard (the QuaRot lineage the pages cite, [BRIDGE-de] §2
+    "Theoretische Analyse der Fehler"): each input channel k is multiplied by a sign
+    s_k in {+1, -1} before the rotation, i.e. R = D H with D = diag(s). The product is
+    unchanged when W is rotated with the same signs.
 """
 from __future__ import annotations
 
@@ -88,11 +113,16 @@ __all__ = [
     "e4m3_value",
     "e4m3_rne_sat",
     "mx_shared_exponent",
+    "mx_exponent_ocp_floor",
+    "mx_exponent_oas",
+    "sse_f32",
+    "SCALE_RULES",
     "quantize_mxfp4",
     "quantize_nvfp4",
     "pack_nibbles",
     "unpack_nibbles",
     "rotate_quantize",
+    "apply_signs",
     "dequantize",
     "linear_f64",
     "bf16_rne_f64",
@@ -250,29 +280,107 @@ def mx_shared_exponent(alpha_max: np.ndarray) -> np.ndarray:
     return np.clip(e, -127, 127)
 
 
-def quantize_mxfp4(y32: np.ndarray):
+SCALE_RULES = ("standard", "ocp_floor", "oas", "fit")
+
+
+def mx_exponent_ocp_floor(alpha_max: np.ndarray) -> np.ndarray:
+    """e = floor(log2 alpha_max) - 2, clamped to [-127, 127]; 0 -> -127 (reading R12).
+
+    With alpha_max = f * 2^E, f in [0.5, 1): floor(log2 alpha_max) = E - 1.
+    """
+    a = np.asarray(alpha_max, dtype=np.float64)
+    f, E = np.frexp(a)
+    e = E.astype(np.int64) - 3
+    e = np.where(a == 0, -127, e)
+    return np.clip(e, -127, 127)
+
+
+def mx_exponent_oas(alpha_max: np.ndarray) -> np.ndarray:
+    """Overflow-aware exponent (reading R13): the standard e, lowered by one when
+    alpha_max / 2^e lies in (3, 3.5] ([UNVEIL-nl] Methodologie, 1. OAS)."""
+    a = np.asarray(alpha_max, dtype=np.float64)
+    e = mx_shared_exponent(a)
+    ratio = a * np.ldexp(1.0, -e)  # exact
+    lower = (a > 0) & (ratio <= 3.5) & (e > -127)
+    return np.where(lower, e - 1, e)
+
+
+def sse_f32(y: np.ndarray, deq: np.ndarray) -> np.ndarray:
+    """Squared error of groups [..., G] in float32, accumulated in element order (reading R14)."""
+    y = np.asarray(y, dtype=np.float32)
+    deq = np.asarray(deq, dtype=np.float32)
+    acc = np.zeros(y.shape[:-1], dtype=np.float32)
+    for i in range(y.shape[-1]):
+        d = (y[..., i] - deq[..., i]).astype(np.float32)
+        acc = (acc + (d * d).astype(np.float32)).astype(np.float32)
+    return acc
+
+
+def _mx_codes(grp32: np.ndarray, e: np.ndarray):
+    """E2M1 codes of groups [..., 32] under exponent e, and their exact dequantized values."""
+    u = grp32.astype(np.float64) * np.ldexp(1.0, -e)[..., None]  # exact
+    codes = e2m1_rne(u)
+    deq = (e2m1_value(codes) * np.ldexp(1.0, e)[..., None]).astype(np.float32)  # exact
+    return codes, deq
+
+
+def quantize_mxfp4(y32: np.ndarray, rule: str = "standard"):
     """MXFP4 codes and E8M0 scale codes of rotated float32 rows y32 [rows, K]."""
     rows, K = y32.shape
     grp = np.asarray(y32, dtype=np.float32).reshape(rows, K // MX_GROUP, MX_GROUP)
     alpha_max = np.max(np.abs(grp), axis=2)  # exact
-    e = mx_shared_exponent(alpha_max)
-    # u = y / 2^e is exact (power-of-two scaling in float64)
-    u = grp.astype(np.float64) * np.ldexp(1.0, -e)[..., None]
-    codes = e2m1_rne(u).reshape(rows, K)
+    if rule == "standard" or rule == "fit":
+        e = mx_shared_exponent(alpha_max)
+    elif rule == "ocp_floor":
+        e = mx_exponent_ocp_floor(alpha_max)
+    elif rule == "oas":
+        e = mx_exponent_oas(alpha_max)
+    else:
+        raise ValueError(rule)
+    codes, deq = _mx_codes(grp, e)
+    if rule == "fit":
+        best = sse_f32(grp, deq)
+        for step in (-1, 1):  # tried after the standard exponent: smaller, then larger
+            cand = e + step
+            valid = (cand >= -127) & (cand <= 127)
+            cand = np.clip(cand, -127, 127)
+            c_codes, c_deq = _mx_codes(grp, cand)
+            c_sse = sse_f32(grp, c_deq)
+            better = valid & (c_sse < best)
+            e = np.where(better, cand, e)
+            best = np.where(better, c_sse, best)
+            codes = np.where(better[..., None], c_codes, codes)
     scales = (e + 127).astype(np.uint8)
-    return codes, scales
+    return codes.reshape(rows, K), scales
 
 
 # --------------------------------------------------------------------------
 # step 3-4, NVFP4 ([BRIDGE-de] §1: 16 elements; [UNVEIL-nl] E4M3 scale;
 # [BRIDGE-es] §2.B: group and tensor scales)
 # --------------------------------------------------------------------------
-def quantize_nvfp4(y32: np.ndarray, tensor_amax: np.float32 | None = None):
-    """NVFP4 codes, E4M3 scale codes and the float32 tensor scale (readings R5, R6).
+def _nv_codes(grp32: np.ndarray, scales: np.ndarray, s_t: np.float32):
+    """E2M1 codes of groups [..., 16] under E4M3 group codes `scales` and tensor scale s_t
+    (reading R6), and their dequantized values fl32(e2m1 * S), S = fl32(d * s_t)."""
+    d = e4m3_value(scales).astype(np.float32)
+    S = (d * s_t).astype(np.float32)
+    zero_group = S < np.float32(2.0 ** -126)
+    S_safe = np.where(zero_group, np.float32(1.0), S)
+    R = (1.0 / S_safe.astype(np.float64)).astype(np.float32)  # = fl32(1/S)
+    u = (grp32 * R[..., None]).astype(np.float32)
+    codes = e2m1_rne(u)
+    codes = np.where(zero_group[..., None], np.signbit(grp32).astype(np.uint8) << 3, codes).astype(np.uint8)
+    deq = (e2m1_value(codes).astype(np.float32) * S[..., None]).astype(np.float32)
+    return codes, deq
+
+
+def quantize_nvfp4(y32: np.ndarray, tensor_amax: np.float32 | None = None, rule: str = "standard"):
+    """NVFP4 codes, E4M3 scale codes and the float32 tensor scale (readings R5, R6; R14 for "fit").
 
     tensor_amax: the absolute maximum over the whole rotated tensor; computed
     from y32 when None (pass it in when y32 holds only some rows).
     """
+    if rule not in ("standard", "fit"):
+        raise ValueError(f"NVFP4 takes the standard or the fit rule, not {rule}")
     rows, K = y32.shape
     y32 = np.asarray(y32, dtype=np.float32)
     T = np.float32(np.max(np.abs(y32))) if tensor_amax is None else np.float32(tensor_amax)
@@ -285,14 +393,20 @@ def quantize_nvfp4(y32: np.ndarray, tensor_amax: np.float32 | None = None):
         return codes, scales, s_t
     q = alpha_max.astype(np.float64) / (6.0 * np.float64(s_t))  # decided exactly (see R5)
     scales = e4m3_rne_sat(q)
-    d = e4m3_value(scales).astype(np.float32)
-    S = (d * s_t).astype(np.float32)
-    zero_group = S < np.float32(2.0 ** -126)
-    S_safe = np.where(zero_group, np.float32(1.0), S)
-    R = (1.0 / S_safe.astype(np.float64)).astype(np.float32)  # = fl32(1/S)
-    u = (grp * R[..., None]).astype(np.float32)
-    codes = e2m1_rne(u)
-    codes = np.where(zero_group[..., None], np.signbit(grp).astype(np.uint8) << 3, codes)
+    codes, deq = _nv_codes(grp, scales, s_t)
+    if rule == "fit":
+        best = sse_f32(grp, deq)
+        base = scales.astype(np.int64)
+        for step in (-1, 1):  # tried after the standard code: smaller, then larger
+            cand = base + step
+            valid = (cand >= 0) & (cand <= 0x7E)
+            cand = np.clip(cand, 0, 0x7E).astype(np.uint8)
+            c_codes, c_deq = _nv_codes(grp, cand, s_t)
+            c_sse = sse_f32(grp, c_deq)
+            better = valid & (c_sse < best)
+            scales = np.where(better, cand, scales).astype(np.uint8)
+            best = np.where(better, c_sse, best)
+            codes = np.where(better[..., None], c_codes, codes)
     return codes.reshape(rows, K).astype(np.uint8), scales, s_t
 
 
@@ -315,17 +429,32 @@ def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # the whole online step: rotate + quantize + pack
 # --------------------------------------------------------------------------
-def rotate_quantize(x_bits: np.ndarray, block: int, fmt: str, tensor_amax=None):
-    """bf16 X [rows, K] -> (packed codes [rows, K/2], scale codes [rows, K/g], s_t or None)."""
+def apply_signs(x32: np.ndarray, signs) -> np.ndarray:
+    """x * s_k per input channel k (reading R15); exact in float32."""
+    if signs is None:
+        return x32
+    s = np.asarray(signs)
+    if s.shape != (x32.shape[-1],) or not np.all((s == 1) | (s == -1)):
+        raise ValueError("signs must be K values in {+1, -1}")
+    return (x32 * s.astype(np.float32)).astype(np.float32)
+
+
+def rotate_quantize(x_bits: np.ndarray, block: int, fmt: str, tensor_amax=None, rule: str = "standard",
+                    signs=None):
+    """bf16 X [rows, K] -> (packed codes [rows, K/2], scale codes [rows, K/g], s_t or None).
+
+    rule: "standard" (R4 / R5), "ocp_floor" (R12, MXFP4), "oas" (R13, MXFP4) or "fit" (R14);
+    signs: optional K values in {+1, -1} applied before the rotation (R15).
+    """
     x32 = widen_bf16(x_bits)
     if x32.ndim != 2:
         raise ValueError("X must be 2-D")
-    y32 = rotate_fwht_f32(x32, block)
+    y32 = rotate_fwht_f32(apply_signs(x32, signs), block)
     if fmt == "mxfp4":
-        codes, scales = quantize_mxfp4(y32)
+        codes, scales = quantize_mxfp4(y32, rule)
         return pack_nibbles(codes), scales, None
     if fmt == "nvfp4":
-        codes, scales, s_t = quantize_nvfp4(y32, tensor_amax)
+        codes, scales, s_t = quantize_nvfp4(y32, tensor_amax, rule)
         return pack_nibbles(codes), scales, s_t
     raise ValueError(fmt)
 

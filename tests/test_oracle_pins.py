@@ -410,3 +410,147 @@ def test_rotation_lowers_mxfp4_error_on_laplace_data():
 
     assert rel_mse(True) < rel_mse(False)
     assert np.isfinite(xw).all()
+
+
+# --------------------------------------------------------------------------
+# scale-rule variants and random signs
+# --------------------------------------------------------------------------
+def _alphas(seed, n=4000):
+    r = rng(seed)
+    a = np.ldexp(r.uniform(0.5, 1.0, n), r.integers(-60, 60, n))
+    exact = np.ldexp(np.array([3.0, 3.5, 3.25, 4.0, 6.0, 7.0, 1.0, 1.5, 1.75]), 5)
+    return np.concatenate([a, exact, np.nextafter(exact, 0), np.nextafter(exact, np.inf)])
+
+
+def test_ocp_floor_exponent_brute_force():
+    # largest e with 2^(e+2) <= alpha, found by walking exact powers of two
+    for a in _alphas(21):
+        e = int(O.mx_exponent_ocp_floor(np.array([a]))[0])
+        assert 2.0 ** (e + 2) <= a < 2.0 ** (e + 3)
+        assert 4.0 <= a / 2.0 ** e < 8.0
+    assert int(O.mx_exponent_ocp_floor(np.array([0.0]))[0]) == -127
+
+
+def test_oas_exponent_brute_force_and_page_interval():
+    iv = facts()["oas_interval"]
+    lo, hi = iv["alpha_max_from"]
+    out_lo, out_hi = iv["after_finer_scale"]
+    for a in _alphas(22):
+        e_std = int(O.mx_shared_exponent(np.array([a]))[0])
+        e = int(O.mx_exponent_oas(np.array([a]))[0])
+        r_std = Fraction(a) / Fraction(2) ** e_std
+        if r_std <= Fraction(hi):  # the page's [3, 3.5] (the standard ratio is always > 3)
+            assert e == e_std - 1
+            r = Fraction(a) / Fraction(2) ** e
+            assert Fraction(out_lo) < r <= Fraction(out_hi)
+        else:
+            assert e == e_std
+            assert Fraction(7, 2) < Fraction(a) / Fraction(2) ** e <= 6
+    assert lo == 3.0
+
+
+def _exact_sse(y, deq):
+    return sum((Fraction(float(a)) - Fraction(float(b))) ** 2 for a, b in zip(y, deq))
+
+
+def _mx_candidate_sse(g, e):
+    u = g.astype(np.float64) * 2.0 ** -e
+    deq = O.e2m1_value(O.e2m1_rne(u)) * 2.0 ** e
+    return _exact_sse(g, deq)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_mx_fit_picks_least_error_neighbour(seed):
+    r = rng(seed)
+    # mixed groups: normal, heavy tails, one large element, near the (3, 3.5] band
+    y = np.concatenate([r.standard_normal((40, 32)), r.standard_t(3, (40, 32)),
+                        r.standard_normal((40, 32)) * np.where(r.random((40, 32)) < 0.05, 20, 1)]).astype(np.float32)
+    codes_std, sc_std = O.quantize_mxfp4(y, "standard")
+    codes_fit, sc_fit = O.quantize_mxfp4(y, "fit")
+    for gi in range(y.shape[0]):
+        g = y[gi]
+        e0 = int(sc_std[gi, 0]) - 127
+        cands = {e: _mx_candidate_sse(g, e) for e in (e0 - 1, e0, e0 + 1)}
+        chosen = int(sc_fit[gi, 0]) - 127
+        assert chosen in cands
+        best = min(cands.values())
+        # the float32 error sum decides; it may only disagree with exact arithmetic on near-ties
+        assert cands[chosen] <= best * (1 + 1e-5) + Fraction(1, 10**30)
+        assert cands[chosen] <= cands[e0]
+        # codes are the standard quantizer's codes under the chosen exponent
+        u = g.astype(np.float64) * 2.0 ** -chosen
+        assert np.array_equal(codes_fit[gi], O.e2m1_rne(u))
+
+
+def test_mx_fit_moves_both_ways_on_constructed_groups():
+    # one element at 3.1 * 2^0 and the rest tiny: the finer scale (max -> 6.2, saturates to 6)
+    # halves every small element's step, so e - 1 must win
+    g = np.full(32, 0.26, np.float32)
+    g[0] = 3.1
+    _, sc = O.quantize_mxfp4(g[None, :], "fit")
+    _, sc0 = O.quantize_mxfp4(g[None, :], "standard")
+    assert int(sc[0, 0]) == int(sc0[0, 0]) - 1
+    # all elements at 5.9 with the standard scale 2^0 round to 6 (error 0.1 each); with 2^1 they are
+    # 2.95 -> 3, i.e. 6 again: equal error, so the standard exponent stays (strict improvement rule)
+    g = np.full(32, 5.9, np.float32)
+    _, sc = O.quantize_mxfp4(g[None, :], "fit")
+    assert int(sc[0, 0]) == 127
+
+
+def test_nv_fit_picks_least_error_neighbour():
+    r = rng(9)
+    y = np.concatenate([r.standard_normal((64, 16)), r.standard_t(3, (64, 16)) * 3]).astype(np.float32)
+    y = y.reshape(16, 128)
+    c_std, s_std, t = O.quantize_nvfp4(y, rule="standard")
+    c_fit, s_fit, t2 = O.quantize_nvfp4(y, rule="fit")
+    assert t == t2
+    grp = y.reshape(-1, 16)
+    s_std = s_std.reshape(-1)
+    s_fit = s_fit.reshape(-1)
+
+    def cand_sse(g, code):
+        codes, deq = O._nv_codes(g[None, :], np.array([code], np.uint8), t)
+        return _exact_sse(g, deq[0]), codes[0]
+
+    changed = 0
+    for gi in range(grp.shape[0]):
+        c0 = int(s_std[gi])
+        cands = {c: cand_sse(grp[gi], c) for c in (c0 - 1, c0, c0 + 1) if 0 <= c <= 0x7E}
+        chosen = int(s_fit[gi])
+        best = min(v[0] for v in cands.values())
+        assert cands[chosen][0] <= best * (1 + 1e-5) + Fraction(1, 10**30)
+        assert cands[chosen][0] <= cands[c0][0]
+        assert np.array_equal(c_fit.reshape(-1, 16)[gi], cands[chosen][1])
+        changed += chosen != c0
+    assert changed > 0  # the search does move some scales on this data
+
+
+def test_random_signs_reduce_and_rotate_like_dense_DH():
+    x = WL.draw_normal_bf16((6, 256), 1.0, seed=5)
+    ones = np.ones(256, np.int8)
+    for fmt, b in (("mxfp4", 32), ("nvfp4", 16), ("mxfp4", 128)):
+        a = O.rotate_quantize(x, b, fmt)
+        c = O.rotate_quantize(x, b, fmt, signs=ones)
+        assert all(np.array_equal(p, q) for p, q in zip(a[:2], c[:2]))
+    s = WL.draw_signs(256, 7)
+    assert set(np.unique(s)) == {-1, 1}
+    x32 = O.widen_bf16(x).astype(np.float64)
+    for b in (32, 128):
+        y = O.rotate_fwht_f32(O.apply_signs(O.widen_bf16(x), s), b).astype(np.float64)
+        H = O.sylvester_hadamard(b) / math.sqrt(b)
+        D = np.diag(s.astype(np.float64))
+        R = np.kron(np.eye(256 // b), H)
+        ref = x32 @ D @ R.T
+        assert np.max(np.abs(y - ref)) <= 1e-5 * np.max(np.abs(ref))
+        # the randomized rotation is still orthogonal: folding it into W keeps X W^T
+        w = WL.draw_normal_bf16((5, 256), 0.02, seed=6)
+        w32 = O.widen_bf16(w).astype(np.float64)
+        RD = R @ D
+        assert np.allclose((x32 @ RD.T) @ (w32 @ RD.T).T, x32 @ w32.T, rtol=0, atol=1e-12)
+    # a sign flip of every channel flips every rotated value, so codes mirror exactly
+    neg = O.rotate_quantize(x, 32, "mxfp4", signs=-ones)
+    pos = O.rotate_quantize(x, 32, "mxfp4")
+    cn, cp = O.unpack_nibbles(neg[0]), O.unpack_nibbles(pos[0])
+    assert np.array_equal(neg[1], pos[1])
+    nz = (cp & 7) != 0
+    assert np.array_equal(cn[nz], cp[nz] ^ 8)
