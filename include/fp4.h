@@ -47,6 +47,14 @@ extern "C" {
  * gist.science, Dutch edition, Technische samenvatting, Probleemstelling). */
 enum { FP4_MXFP4 = 0, FP4_NVFP4 = 1 };
 
+/* Scale rules of fp4_rotate_quantize_ex / fp4_quantize_weights_ex. */
+enum {
+  FP4_SCALE_STANDARD = 0,  /* the rules of fp4_rotate_quantize (both formats)                */
+  FP4_SCALE_OCP_FLOOR = 1, /* MXFP4: e = floor(log2 alpha) - 2, maximum in [4, 8), saturated  */
+  FP4_SCALE_OAS = 2,       /* MXFP4: overflow-aware scaling                                   */
+  FP4_SCALE_FIT = 3        /* both: least-squared-error neighbour of the standard scale       */
+};
+
 /* Output dtypes of fp4_linear. */
 enum { FP4_OUT_F32 = 0, FP4_OUT_BF16 = 1 };
 
@@ -107,6 +115,48 @@ FP4_API int fp4_rotate_quantize(const void *X, int64_t M, int64_t K, int64_t ldx
  */
 FP4_API int fp4_quantize_weights(const void *W, int64_t N, int64_t K, int64_t ldw, int block, int fmt,
                          uint8_t *codes, uint8_t *scales, float *tensor_scale, void *stream);
+
+/*
+ * fp4_rotate_quantize_ex / fp4_quantize_weights_ex - the calls above with two
+ * options of the quantizer; with scale_rule = FP4_SCALE_STANDARD and signs = NULL
+ * they are identical to fp4_rotate_quantize / fp4_quantize_weights.
+ *
+ *  scale_rule  FP4_SCALE_STANDARD: as above.
+ *              FP4_SCALE_OCP_FLOOR (MXFP4 only): e = floor(log2 alpha) - 2,
+ *                clamped to [-127, 127]; the group maximum lands in [4, 8) and
+ *                elements above 6 saturate.
+ *              FP4_SCALE_OAS (MXFP4 only): overflow-aware scaling ("Unveiling the
+ *                Potential of Quantization with MXFP4", gist.science, Dutch
+ *                edition, Methodologie, 1. OAS): the standard e, lowered by one
+ *                when alpha / 2^e lies in (3, 3.5], so the maximum lands in (6, 7]
+ *                and saturates to 6 while smaller elements get twice the resolution.
+ *              FP4_SCALE_FIT (both formats): data-free scale fitting ("Bridging the
+ *                Gap Between Promise and Performance for Microscaling FP4
+ *                Quantization", gist.science, German edition, Technische
+ *                Zusammenfassung §2 "Einführung von MR-GPTQ", item 2: MXFP4 scales
+ *                fitted to the data range, NVFP4 scales optimised for E4M3). Per
+ *                group the standard scale and its two neighbours (MXFP4: e - 1,
+ *                e + 1; NVFP4: the adjacent E4M3 codes, s_t unchanged) are tried in
+ *                the order standard, smaller, larger; a candidate replaces the
+ *                current one when its squared error is strictly smaller. The error
+ *                is float32, summed in element order: d = fl32(y - q * s),
+ *                acc = fl32(acc + fl32(d * d)), with q * s exact for MXFP4 and
+ *                fl32(q * S), S = fl32(d_e4m3 * s_t), for NVFP4. Intended for
+ *                weights: it costs about three quantizations.
+ *  signs       NULL, or device int8 [K], 16-byte aligned: the randomized block
+ *              Hadamard R = D H with D = diag(signs). Channel k is negated before
+ *              the rotation when signs[k] < 0 (entries are meant to be +1 or -1).
+ *              X and W must be quantized with the same signs.
+ * Other arguments, alignment rules and launches as for fp4_rotate_quantize.
+ * Errors: FP4_E_FORMAT for an unknown rule or OCP_FLOOR / OAS with NVFP4;
+ * FP4_E_ALIGN for misaligned signs.
+ */
+FP4_API int fp4_rotate_quantize_ex(const void *X, int64_t M, int64_t K, int64_t ldx, int block, int fmt,
+                                   int scale_rule, const int8_t *signs, uint8_t *codes, uint8_t *scales,
+                                   float *tensor_scale, void *stream);
+FP4_API int fp4_quantize_weights_ex(const void *W, int64_t N, int64_t K, int64_t ldw, int block, int fmt,
+                                    int scale_rule, const int8_t *signs, uint8_t *codes, uint8_t *scales,
+                                    float *tensor_scale, void *stream);
 
 /*
  * fp4_linear - Y[m, n] = sum_k dq(Xq)[m, k] * dq(Wq)[n, k], float32 accumulation.

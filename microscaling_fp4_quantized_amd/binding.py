@@ -60,6 +60,11 @@ def load_library() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = q_args
         f.restype = i32
+    qx_args = [vp, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp]
+    for name in ("fp4_rotate_quantize_ex", "fp4_quantize_weights_ex"):
+        f = getattr(lib, name)
+        f.argtypes = qx_args
+        f.restype = i32
     lib.fp4_linear.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32, vp]
     lib.fp4_linear.restype = i32
     lib.fp4_last_error.argtypes = []
@@ -87,7 +92,10 @@ def _check(status: int):
         raise Fp4Error(status, load_library().fp4_last_error().decode())
 
 
-def _quantize(name: str, x: torch.Tensor, block: int, fmt, out=None):
+SCALE_RULES = {"standard": 0, "ocp_floor": 1, "oas": 2, "fit": 3}
+
+
+def _quantize(name: str, x: torch.Tensor, block: int, fmt, out=None, rule=None, signs=None):
     lib = load_library()
     f = _FMT[fmt]
     if x.dim() != 2 or x.dtype != torch.bfloat16 or not x.is_cuda or x.stride(1) != 1:
@@ -100,23 +108,32 @@ def _quantize(name: str, x: torch.Tensor, block: int, fmt, out=None):
         ts = torch.empty((1,), dtype=torch.float32, device=x.device) if f == FP4_NVFP4 else None
     else:
         codes, scales, ts = out
-    _check(getattr(lib, name)(_ptr(x), M, K, x.stride(0), int(block), f, _ptr(codes), _ptr(scales),
-                              _ptr(ts), _stream(x.device)))
+    if rule is None and signs is None:
+        _check(getattr(lib, name)(_ptr(x), M, K, x.stride(0), int(block), f, _ptr(codes), _ptr(scales),
+                                  _ptr(ts), _stream(x.device)))
+    else:
+        if signs is not None and (signs.dtype != torch.int8 or not signs.is_cuda or signs.numel() != K
+                                  or not signs.is_contiguous()):
+            raise ValueError(f"{name}: signs must be a contiguous int8 CUDA tensor of K entries")
+        r = SCALE_RULES[rule or "standard"]
+        _check(getattr(lib, name + "_ex")(_ptr(x), M, K, x.stride(0), int(block), f, r, _ptr(signs), _ptr(codes),
+                                          _ptr(scales), _ptr(ts), _stream(x.device)))
     return codes, scales, ts
 
 
-def fp4_rotate_quantize(x: torch.Tensor, block: int, fmt="mxfp4", out=None):
+def fp4_rotate_quantize(x: torch.Tensor, block: int, fmt="mxfp4", out=None, rule=None, signs=None):
     """Online block-Hadamard rotation + FP4 quantization of bf16 activations.
 
     Returns (codes [M, K/2] uint8, scales [M, K/g] uint8, tensor_scale [1] float32 or None).
-    ``out`` may pass preallocated (codes, scales, tensor_scale).
+    ``out`` may pass preallocated (codes, scales, tensor_scale). ``rule`` ("standard",
+    "ocp_floor", "oas", "fit") and ``signs`` (int8 [K] of +-1) select fp4_rotate_quantize_ex.
     """
-    return _quantize("fp4_rotate_quantize", x, block, fmt, out)
+    return _quantize("fp4_rotate_quantize", x, block, fmt, out, rule, signs)
 
 
-def fp4_quantize_weights(w: torch.Tensor, block: int, fmt="mxfp4", out=None):
+def fp4_quantize_weights(w: torch.Tensor, block: int, fmt="mxfp4", out=None, rule=None, signs=None):
     """Offline rotation + quantization of a weight matrix [N, K] (same contract)."""
-    return _quantize("fp4_quantize_weights", w, block, fmt, out)
+    return _quantize("fp4_quantize_weights", w, block, fmt, out, rule, signs)
 
 
 def fp4_linear(xq, xs, wq, ws, fmt="mxfp4", x_ts=None, w_ts=None, out_dtype=torch.float32, out=None):

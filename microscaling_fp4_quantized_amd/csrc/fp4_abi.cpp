@@ -57,12 +57,17 @@ int launched(const char* who, hipError_t e) {
   return ok();
 }
 
-int quantize(const char* who, const void* X, int64_t M, int64_t K, int64_t ld, int block, int fmt,
-             uint8_t* codes, uint8_t* scales, float* ts, void* stream) {
+int quantize(const char* who, const void* X, int64_t M, int64_t K, int64_t ld, int block, int fmt, int rule,
+             const int8_t* signs, uint8_t* codes, uint8_t* scales, float* ts, void* stream) {
   int st = check_quantize(who, X, M, K, ld, block, fmt, codes, scales, ts);
   if (st != FP4_OK) return st;
-  return launched(who, fp4_launch_rotate_quantize(static_cast<const uint16_t*>(X), M, K, ld, block, fmt,
-                                                  codes, scales, ts, static_cast<hipStream_t>(stream)));
+  if (rule != FP4_SCALE_STANDARD && rule != FP4_SCALE_OCP_FLOOR && rule != FP4_SCALE_OAS && rule != FP4_SCALE_FIT)
+    return fail(FP4_E_FORMAT, "%s: unknown scale rule %d", who, rule);
+  if (fmt == FP4_NVFP4 && (rule == FP4_SCALE_OCP_FLOOR || rule == FP4_SCALE_OAS))
+    return fail(FP4_E_FORMAT, "%s: scale rule %d applies to MXFP4 only", who, rule);
+  if (signs && !aligned(signs, 16)) return fail(FP4_E_ALIGN, "%s: signs must be 16-byte aligned", who);
+  return launched(who, fp4_launch_rotate_quantize(static_cast<const uint16_t*>(X), M, K, ld, block, fmt, rule,
+                                                  signs, codes, scales, ts, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -71,12 +76,26 @@ extern "C" {
 
 int fp4_rotate_quantize(const void* X, int64_t M, int64_t K, int64_t ldx, int block, int fmt, uint8_t* codes,
                         uint8_t* scales, float* tensor_scale, void* stream) {
-  return quantize("fp4_rotate_quantize", X, M, K, ldx, block, fmt, codes, scales, tensor_scale, stream);
+  return quantize("fp4_rotate_quantize", X, M, K, ldx, block, fmt, FP4_SCALE_STANDARD, nullptr, codes, scales,
+                  tensor_scale, stream);
 }
 
 int fp4_quantize_weights(const void* W, int64_t N, int64_t K, int64_t ldw, int block, int fmt, uint8_t* codes,
                          uint8_t* scales, float* tensor_scale, void* stream) {
-  return quantize("fp4_quantize_weights", W, N, K, ldw, block, fmt, codes, scales, tensor_scale, stream);
+  return quantize("fp4_quantize_weights", W, N, K, ldw, block, fmt, FP4_SCALE_STANDARD, nullptr, codes, scales,
+                  tensor_scale, stream);
+}
+
+int fp4_rotate_quantize_ex(const void* X, int64_t M, int64_t K, int64_t ldx, int block, int fmt, int scale_rule,
+                           const int8_t* signs, uint8_t* codes, uint8_t* scales, float* tensor_scale, void* stream) {
+  return quantize("fp4_rotate_quantize_ex", X, M, K, ldx, block, fmt, scale_rule, signs, codes, scales, tensor_scale,
+                  stream);
+}
+
+int fp4_quantize_weights_ex(const void* W, int64_t N, int64_t K, int64_t ldw, int block, int fmt, int scale_rule,
+                            const int8_t* signs, uint8_t* codes, uint8_t* scales, float* tensor_scale, void* stream) {
+  return quantize("fp4_quantize_weights_ex", W, N, K, ldw, block, fmt, scale_rule, signs, codes, scales,
+                  tensor_scale, stream);
 }
 
 int fp4_linear(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const uint8_t* Wq, const uint8_t* Ws,
@@ -110,6 +129,6 @@ int fp4_linear(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const ui
 
 const char* fp4_last_error(void) { return g_err; }
 
-int fp4_abi_version(void) { return 100; }
+int fp4_abi_version(void) { return 110; }
 
 }  // extern "C"

@@ -144,13 +144,89 @@ __device__ __forceinline__ unsigned sign_codes8(const float* v) {
   return w;
 }
 
+// Randomized block Hadamard: flip channel k when signs[k] < 0, before the rotation. The
+// lane's 32 channels start at 32 * (chunk index within its row).
+__device__ __forceinline__ void apply_signs(float v[32], const int8_t* __restrict__ signs, uint32_t gc,
+                                            const RowMap& rm) {
+  const uint32_t cc = gc - row_of(gc, rm) * rm.cpr;
+  const v4u* p = reinterpret_cast<const v4u*>(signs + (size_t)cc * 32);
+  const v4u s0 = p[0], s1 = p[1];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const unsigned w = i < 16 ? s0[i >> 2] : s1[(i - 16) >> 2];
+    const unsigned neg = (w >> (8 * (i & 3) + 7)) & 1u;
+    v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (neg << 31));
+  }
+}
+
+// Scale rules of the quantizer (the standard one and its variants; see include/fp4.h).
+enum { kRuleStandard = 0, kRuleOcpFloor = 1, kRuleOas = 2, kRuleFit = 3 };
+
+// E8M0 code of a group maximum `ab` (float bits, non-negative) under the standard rule:
+// e = ceil(log2(alpha / 6)) clamped to [-127, 127], code e + 127.
+__device__ __forceinline__ int mx_code_standard(unsigned ab) {
+  const int code = (int)(ab >> 23) - 2 + ((ab & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+  return code < 0 ? 0 : code;
+}
+
+template <int RULE>
+__device__ __forceinline__ int mx_code(unsigned ab) {
+  if constexpr (RULE == kRuleOcpFloor) {
+    // e = floor(log2 alpha) - 2: the group maximum lands in [4, 8) and saturates above 6
+    const int code = (int)(ab >> 23) - 2;
+    return code < 0 ? 0 : code;
+  } else if constexpr (RULE == kRuleOas) {
+    // overflow-aware: when alpha / 2^e is in (3, 3.5] (mantissa in (0.5, 0.75] with the exponent
+    // rounded up) use e - 1, so the maximum lands in (6, 7] and saturates to 6
+    const int code = mx_code_standard(ab);
+    const unsigned m = ab & 0x7FFFFFu;
+    return (code > 0 && m > 0x400000u && m <= 0x600000u) ? code - 1 : code;
+  } else {
+    return mx_code_standard(ab);
+  }
+}
+
+// 2^(code - 127) as a float32 (code 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float pow2_of_code(int code) {
+  return code > 0 ? __uint_as_float((unsigned)code << 23) : __uint_as_float(0x00400000u);
+}
+
+// E2M1 values of eight codes in one dword (element 2j in the low nibble of byte j).
+__device__ __forceinline__ void e2m1_values8(unsigned w, float* q) {
+  const v2f f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const v2f f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const v2f f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const v2f f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  q[0] = f0[0]; q[1] = f0[1]; q[2] = f1[0]; q[3] = f1[1];
+  q[4] = f2[0]; q[5] = f2[1]; q[6] = f3[0]; q[7] = f3[1];
+}
+
+// Squared error of n elements in float32, accumulated in element order: d = fl32(y - q * s),
+// acc = fl32(acc + fl32(d * d)), with q * s exact (MX) or rounded once (NV).
+template <int NE>
+__device__ __forceinline__ float group_sse(const float* y, const unsigned* words, float s) {
+  float acc = 0.f;
+#pragma unroll
+  for (int w = 0; w < NE / 8; ++w) {
+    float q[8];
+    e2m1_values8(words[w], q);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float d = y[8 * w + i] - q[i] * s;
+      acc = acc + d * d;
+    }
+  }
+  return acc;
+}
+
 // ---------------------------------------------------------------------------
 // MXFP4: one kernel. E8M0 code = max(0, biased_exp(alpha) - 2 + [mantissa > 0.5]),
 // i.e. e = ceil(log2(alpha / 6)) clamped to [-127, 127] (alpha = 0 -> code 0).
 // ---------------------------------------------------------------------------
-template <int B>
+template <int B, int RULE>
 __global__ __launch_bounds__(kThreads) void rotate_quant_mx(const uint16_t* __restrict__ X, int64_t ldx,
                                                             RowMap rm, uint32_t total, int contiguous,
+                                                            const int8_t* __restrict__ signs,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
   __shared__ __attribute__((aligned(16))) v4u stage[kThreads / 64][kStage];
@@ -158,6 +234,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_mx(const uint16_t* __re
   float v[32];
   load_chunk(X, ldx, gc, total, rm, contiguous != 0, stage[threadIdx.x >> 6], v);
   if (gc >= total) return;  // whole quads leave together (total % (B/32) == 0)
+  if (signs) apply_signs(v, signs, gc, rm);
   fwht<B>(v);
   const float c = __uint_as_float(hadamard_constant_bits(B));
   float amax = 0.f;
@@ -166,13 +243,31 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_mx(const uint16_t* __re
     v[i] *= c;
     amax = fmaxf(amax, fabsf(v[i]));
   }
-  const unsigned ab = __float_as_uint(amax);
-  int code = (int)(ab >> 23) - 2 + ((ab & 0x7FFFFFu) > 0x400000u ? 1 : 0);
-  code = code < 0 ? 0 : code;
-  const float sc = __uint_as_float((unsigned)code << 23);
+  int code = mx_code<RULE>(__float_as_uint(amax));
   v4u out;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) out[j] = cvt8(v + 8 * j, sc);
+  for (int j = 0; j < 4; ++j) out[j] = cvt8(v + 8 * j, __uint_as_float((unsigned)code << 23));
+  if constexpr (RULE == kRuleFit) {
+    // data-free scale fitting: try the neighbouring exponents (smaller first), keep a strictly
+    // smaller float32 squared error
+    unsigned ow[4] = {out[0], out[1], out[2], out[3]};
+    float best = group_sse<32>(v, ow, pow2_of_code(code));
+    const int base = code;
+#pragma unroll
+    for (int step = -1; step <= 1; step += 2) {
+      const int cand = base + step;
+      if (cand < 0 || cand > 254) continue;
+      unsigned o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = cvt8(v + 8 * j, __uint_as_float((unsigned)cand << 23));
+      const float e = group_sse<32>(v, o, pow2_of_code(cand));
+      if (e < best) {
+        best = e;
+        code = cand;
+        out = v4u{o[0], o[1], o[2], o[3]};
+      }
+    }
+  }
   __builtin_nontemporal_store(out, reinterpret_cast<v4u*>(codes) + gc);
   scales[gc] = (uint8_t)code;
 }
@@ -190,6 +285,7 @@ __global__ void clear_word(unsigned* p) {
 template <int B>
 __global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restrict__ X, int64_t ldx,
                                                         RowMap rm, uint32_t total, int contiguous,
+                                                        const int8_t* __restrict__ signs,
                                                         unsigned* __restrict__ amax_bits) {
   __shared__ __attribute__((aligned(16))) v4u stage[kThreads / 64][kStage];
   // Grid-stride over the chunks (the grid is capped at a few workgroups per CU), so each
@@ -201,6 +297,7 @@ __global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restri
     float v[32];
     load_chunk(X, ldx, gc, total, rm, contiguous != 0, stage[threadIdx.x >> 6], v);
     if (gc < total) {
+      if (signs) apply_signs(v, signs, gc, rm);
       fwht<B>(v);
       float a = 0.f;
 #pragma unroll
@@ -227,9 +324,29 @@ __global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restri
 }
 
 // NVFP4 pass 2: group scales and codes given T.
-template <int B>
+// One group of 16 under E4M3 code `code`: S = fl32(d * s_t), u = fl32(y * fl32(1/S)), codes
+// rounded by the hardware convert (scale 1); S < 2^-126 stores signed zeros.
+__device__ __forceinline__ void nv_group(const float* y, unsigned code, float s_t, unsigned* o, float* S_out) {
+  const float S = e4m3_value(code) * s_t;
+  *S_out = S;
+  if (S < 1.17549435e-38f) {  // 2^-126: the group stores signed zeros
+    o[0] = sign_codes8(y);
+    o[1] = sign_codes8(y + 8);
+    *S_out = 0.f;
+    return;
+  }
+  const float R = (float)(1.0 / (double)S);  // = fl32(1 / S)
+  float u[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) u[i] = y[i] * R;
+  o[0] = cvt8(u, 1.0f);
+  o[1] = cvt8(u + 8, 1.0f);
+}
+
+template <int B, int RULE>
 __global__ __launch_bounds__(kThreads) void rotate_quant_nv(const uint16_t* __restrict__ X, int64_t ldx,
                                                             RowMap rm, uint32_t total, int contiguous,
+                                                            const int8_t* __restrict__ signs,
                                                             const unsigned* __restrict__ amax_bits,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
@@ -238,6 +355,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_nv(const uint16_t* __re
   float v[32];
   load_chunk(X, ldx, gc, total, rm, contiguous != 0, stage[threadIdx.x >> 6], v);
   if (gc >= total) return;
+  if (signs) apply_signs(v, signs, gc, rm);
   fwht<B>(v);
   const float c = __uint_as_float(hadamard_constant_bits(B));
 #pragma unroll
@@ -253,23 +371,37 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_nv(const uint16_t* __re
     const double den = 6.0 * (double)s_t;  // exact
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
+      const float* y = v + 16 * g;
       float a = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[16 * g + i]));
-      const unsigned code = e4m3_rne_sat((double)a / den);
-      const float S = e4m3_value(code) * s_t;
-      sc2 |= code << (8 * g);
-      if (S < 1.17549435e-38f) {  // 2^-126: the group stores signed zeros
-        out[2 * g] = sign_codes8(v + 16 * g);
-        out[2 * g + 1] = sign_codes8(v + 16 * g + 8);
-      } else {
-        const float R = (float)(1.0 / (double)S);  // = fl32(1 / S)
-        float u[16];
+      for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(y[i]));
+      unsigned code = e4m3_rne_sat((double)a / den);
+      unsigned o[2];
+      float S;
+      nv_group(y, code, s_t, o, &S);
+      if constexpr (RULE == kRuleFit) {
+        // data-free search over the neighbouring E4M3 codes (smaller first), tensor scale fixed
+        float best = group_sse<16>(y, o, S);
+        const int base = (int)code;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) u[i] = v[16 * g + i] * R;
-        out[2 * g] = cvt8(u, 1.0f);
-        out[2 * g + 1] = cvt8(u + 8, 1.0f);
+        for (int step = -1; step <= 1; step += 2) {
+          const int cand = base + step;
+          if (cand < 0 || cand > 0x7E) continue;
+          unsigned oc[2];
+          float Sc;
+          nv_group(y, (unsigned)cand, s_t, oc, &Sc);
+          const float e = group_sse<16>(y, oc, Sc);
+          if (e < best) {
+            best = e;
+            code = (unsigned)cand;
+            o[0] = oc[0];
+            o[1] = oc[1];
+          }
+        }
       }
+      sc2 |= code << (8 * g);
+      out[2 * g] = o[0];
+      out[2 * g + 1] = o[1];
     }
   }
   __builtin_nontemporal_store(out, reinterpret_cast<v4u*>(codes) + gc);
@@ -298,39 +430,55 @@ RowMap make_rowmap(uint32_t cpr) {
   return rm;
 }
 
-template <int B>
-hipError_t launch_b(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int fmt, uint8_t* codes,
-                    uint8_t* scales, float* ts, hipStream_t st) {
+template <int B, int RULE>
+hipError_t launch_b(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int fmt, const int8_t* signs,
+                    uint8_t* codes, uint8_t* scales, float* ts, hipStream_t st) {
   const uint32_t cpr = (uint32_t)(K / 32);
   const uint32_t total = (uint32_t)(M * (K / 32));
   const RowMap rm = make_rowmap(cpr);
   const int contiguous = ldx == K;
   const dim3 grid((total + kThreads - 1) / kThreads), block(kThreads);
   if (fmt == 0) {
-    hipLaunchKernelGGL(rotate_quant_mx<B>, grid, block, 0, st, X, ldx, rm, total, contiguous, codes,
+    hipLaunchKernelGGL((rotate_quant_mx<B, RULE>), grid, block, 0, st, X, ldx, rm, total, contiguous, signs, codes,
                        scales);
     return hipGetLastError();
   }
+  constexpr int NV_RULE = RULE == kRuleFit ? kRuleFit : kRuleStandard;  // other rules are MXFP4 only
   unsigned* amax = reinterpret_cast<unsigned*>(ts);
   hipLaunchKernelGGL(clear_word, dim3(1), dim3(64), 0, st, amax);
   const dim3 grid_max(grid.x < 2048u ? grid.x : 2048u);  // 8 workgroups per CU, grid-stride
-  hipLaunchKernelGGL(rotate_amax<B>, grid_max, block, 0, st, X, ldx, rm, total, contiguous, amax);
-  hipLaunchKernelGGL(rotate_quant_nv<B>, grid, block, 0, st, X, ldx, rm, total, contiguous, amax, codes,
-                     scales);
+  hipLaunchKernelGGL(rotate_amax<B>, grid_max, block, 0, st, X, ldx, rm, total, contiguous, signs, amax);
+  hipLaunchKernelGGL((rotate_quant_nv<B, NV_RULE>), grid, block, 0, st, X, ldx, rm, total, contiguous, signs, amax,
+                     codes, scales);
   hipLaunchKernelGGL(finish_tensor_scale, dim3(1), dim3(64), 0, st, ts);
   return hipGetLastError();
+}
+
+template <int RULE>
+hipError_t launch_rule(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int block, int fmt,
+                       const int8_t* signs, uint8_t* codes, uint8_t* scales, float* ts, hipStream_t st) {
+  switch (block) {
+    case 16: return launch_b<16, RULE>(X, M, K, ldx, fmt, signs, codes, scales, ts, st);
+    case 32: return launch_b<32, RULE>(X, M, K, ldx, fmt, signs, codes, scales, ts, st);
+    case 64: return launch_b<64, RULE>(X, M, K, ldx, fmt, signs, codes, scales, ts, st);
+    default: return launch_b<128, RULE>(X, M, K, ldx, fmt, signs, codes, scales, ts, st);
+  }
 }
 
 }  // namespace
 }  // namespace fp4
 
 hipError_t fp4_launch_rotate_quantize(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int block,
-                                      int fmt, uint8_t* codes, uint8_t* scales, float* ts,
-                                      hipStream_t st) {
-  switch (block) {
-    case 16: return fp4::launch_b<16>(X, M, K, ldx, fmt, codes, scales, ts, st);
-    case 32: return fp4::launch_b<32>(X, M, K, ldx, fmt, codes, scales, ts, st);
-    case 64: return fp4::launch_b<64>(X, M, K, ldx, fmt, codes, scales, ts, st);
-    default: return fp4::launch_b<128>(X, M, K, ldx, fmt, codes, scales, ts, st);
+                                      int fmt, int rule, const int8_t* signs, uint8_t* codes, uint8_t* scales,
+                                      float* ts, hipStream_t st) {
+  switch (rule) {
+    case fp4::kRuleOcpFloor:
+      return fp4::launch_rule<fp4::kRuleOcpFloor>(X, M, K, ldx, block, fmt, signs, codes, scales, ts, st);
+    case fp4::kRuleOas:
+      return fp4::launch_rule<fp4::kRuleOas>(X, M, K, ldx, block, fmt, signs, codes, scales, ts, st);
+    case fp4::kRuleFit:
+      return fp4::launch_rule<fp4::kRuleFit>(X, M, K, ldx, block, fmt, signs, codes, scales, ts, st);
+    default:
+      return fp4::launch_rule<fp4::kRuleStandard>(X, M, K, ldx, block, fmt, signs, codes, scales, ts, st);
   }
 }

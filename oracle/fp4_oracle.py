@@ -306,13 +306,17 @@ def mx_exponent_oas(alpha_max: np.ndarray) -> np.ndarray:
 
 
 def sse_f32(y: np.ndarray, deq: np.ndarray) -> np.ndarray:
-    """Squared error of groups [..., G] in float32, accumulated in element order (reading R14)."""
+    """Squared error of groups [..., G] in float32, accumulated in element order (reading R14).
+
+    Groups whose errors exceed about 2^64 overflow to +inf for every candidate; no candidate
+    is then strictly better and the standard scale stays, as float32 arithmetic dictates."""
     y = np.asarray(y, dtype=np.float32)
     deq = np.asarray(deq, dtype=np.float32)
     acc = np.zeros(y.shape[:-1], dtype=np.float32)
-    for i in range(y.shape[-1]):
-        d = (y[..., i] - deq[..., i]).astype(np.float32)
-        acc = (acc + (d * d).astype(np.float32)).astype(np.float32)
+    with np.errstate(over="ignore"):
+        for i in range(y.shape[-1]):
+            d = (y[..., i] - deq[..., i]).astype(np.float32)
+            acc = (acc + (d * d).astype(np.float32)).astype(np.float32)
     return acc
 
 

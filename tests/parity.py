@@ -35,27 +35,31 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
-def tensor_amax(x_bits: np.ndarray, block: int, chunk_rows: int = 2048) -> np.float32:
+def tensor_amax(x_bits: np.ndarray, block: int, chunk_rows: int = 2048, signs=None) -> np.float32:
     """max |rotated x| over the whole tensor (oracle rotation), in row chunks."""
     m = np.float32(0)
     for r in range(0, x_bits.shape[0], chunk_rows):
-        y = O.rotate_fwht_f32(O.widen_bf16(x_bits[r:r + chunk_rows]), block)
+        y = O.rotate_fwht_f32(O.apply_signs(O.widen_bf16(x_bits[r:r + chunk_rows]), signs), block)
         m = max(m, np.float32(np.max(np.abs(y))))
     return np.float32(m)
 
 
-def compare_quant(gpu, x_bits: np.ndarray, block: int, fmt: str, rows=None, t_amax=None):
-    """gpu = (codes, scales, ts) torch tensors for all rows; rows = sampled row indices."""
+def compare_quant(gpu, x_bits: np.ndarray, block: int, fmt: str, rows=None, t_amax=None, rule="standard",
+                  signs=None):
+    """gpu = (codes, scales, ts) torch tensors for all rows; rows = sampled row indices.
+
+    rule / signs: the quantizer variant both sides ran (the flags below are those of the
+    standard rule; the variant tests demand zero mismatches of either kind)."""
     g_codes, g_scales, g_ts = gpu
     if rows is None:
         rows = np.arange(x_bits.shape[0])
     xr = x_bits[rows]
     if fmt == "nvfp4" and t_amax is None:
-        t_amax = tensor_amax(x_bits, block)
-    o_packed, o_scales, o_ts = O.rotate_quantize(xr, block, fmt, tensor_amax=t_amax)
+        t_amax = tensor_amax(x_bits, block, signs=signs)
+    o_packed, o_scales, o_ts = O.rotate_quantize(xr, block, fmt, tensor_amax=t_amax, rule=rule, signs=signs)
     gc = host(g_codes)[rows]
     gs = host(g_scales)[rows]
-    y32 = O.rotate_fwht_f32(O.widen_bf16(xr), block)
+    y32 = O.rotate_fwht_f32(O.apply_signs(O.widen_bf16(xr), signs), block)
     flags = O.near_boundary_flags(y32, o_scales, fmt, o_ts)
     oc, gcu = O.unpack_nibbles(o_packed), O.unpack_nibbles(gc)
     diff = oc != gcu
@@ -77,10 +81,12 @@ def compare_quant(gpu, x_bits: np.ndarray, block: int, fmt: str, rows=None, t_am
     return res
 
 
-def assert_quant_parity(res, label=""):
+def assert_quant_parity(res, label="", exact=False):
     say(f"parity {label}: {res}")
     assert res["code_mismatch_unflagged"] == 0, res
     assert res["scale_mismatch_unflagged"] == 0, res
+    if exact:
+        assert res["code_mismatch_flagged"] == 0 and res["scale_mismatch_flagged"] == 0, res
     if "tensor_scale_equal" in res:
         assert res["tensor_scale_equal"], res
 
@@ -91,8 +97,9 @@ def rel_fro(y: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm(y - ref) / (den if den > 0 else 1.0))
 
 
-def gemm_reference(x_bits, w_bits, block, fmt, xrows, wrows, x_amax=None, w_amax=None):
+def gemm_reference(x_bits, w_bits, block, fmt, xrows, wrows, x_amax=None, w_amax=None, x_rule="standard",
+                   w_rule="standard", signs=None):
     """Oracle Y64[xrows][:, wrows] from oracle-quantized operands (never the GPU's)."""
-    xq, xs, xt = O.rotate_quantize(x_bits[xrows], block, fmt, tensor_amax=x_amax)
-    wq, ws, wt = O.rotate_quantize(w_bits[wrows], block, fmt, tensor_amax=w_amax)
+    xq, xs, xt = O.rotate_quantize(x_bits[xrows], block, fmt, tensor_amax=x_amax, rule=x_rule, signs=signs)
+    wq, ws, wt = O.rotate_quantize(w_bits[wrows], block, fmt, tensor_amax=w_amax, rule=w_rule, signs=signs)
     return O.linear_f64(xq, xs, wq, ws, fmt, xt, wt)

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, s)
     # nothing else with C linkage leaks out
     assert {s for s in exported if s.startswith("fp4_")} == set(declared_symbols())
-    assert lib.fp4_abi_version() == 100
+    assert lib.fp4_abi_version() == 110
 
 
 A16 = 0x10000  # a 16-byte aligned fake address: never dereferenced, validation fails first
@@ -72,6 +72,23 @@ def test_rotate_quantize_validation(lib):
     assert b"multiple of 32" in lib.fp4_last_error() or lib.fp4_last_error()
     assert lib.fp4_quantize_weights(None, 4, 64, 64, 32, 0, A16, A16, None, None) == -1
     assert b"fp4_quantize_weights" in lib.fp4_last_error()
+
+
+def qx(lib, rule=0, signs=None, fmt=0, ts=None, X=A16, M=4, K=64, ldx=64, block=32, codes=A16, scales=A16):
+    return lib.fp4_rotate_quantize_ex(X, M, K, ldx, block, fmt, rule, signs, codes, scales, ts, None)
+
+
+def test_rotate_quantize_ex_validation(lib):
+    assert qx(lib, rule=4) == -4
+    assert qx(lib, rule=-1) == -4
+    assert qx(lib, rule=1, fmt=1, ts=A16) == -4    # the OCP floor rule is MXFP4 only
+    assert qx(lib, rule=2, fmt=1, ts=A16) == -4    # so is OAS
+    assert qx(lib, rule=3, signs=A16 + 8) == -5    # signs 16-byte aligned
+    assert qx(lib, rule=0, X=None) == -1           # the checks shared with fp4_rotate_quantize come first
+    assert qx(lib, rule=9, block=8) == -3
+    assert b"fp4_rotate_quantize_ex" in lib.fp4_last_error()
+    assert lib.fp4_quantize_weights_ex(None, 4, 64, 64, 32, 0, 3, None, A16, A16, None, None) == -1
+    assert b"fp4_quantize_weights_ex" in lib.fp4_last_error()
 
 
 def lin(lib, Xq=A16, Xs=A16, xts=None, Wq=A16, Ws=A16, wts=None, M=4, N=4, K=128, fmt=0, Y=A16, ydt=0):
