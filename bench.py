@@ -148,11 +148,35 @@ def extra_rows(B, WL, torch, dev):
         B.fp4_rotate_quantize(bufs[i & 1], sw.block, "nvfp4", out=o)
     ms = time_batch(lambda i: B.fp4_rotate_quantize(bufs[i & 1], sw.block, "nvfp4", out=o), 20, torch)
     nbytes = sw.M * sw.K * (2 + 2 + 0.5 + 1.0 / 16) + 8
+    t_max = measured_traffic("rotate_amax_b32", "rotate_quant.hip")
+    t_nv = measured_traffic("rotate_quant_nv_b32", "rotate_quant.hip")
     out["rotate_quantize_nvfp4"] = {
         "workload": "stress_nv32: X 16384x8192 bf16, block 32, NVFP4 (max pass + quantize pass)",
         "us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "algorithmic_bytes": nbytes}
+        "algorithmic_bytes": nbytes,
+        "traffic": None if t_max is None or t_nv is None else t_max + t_nv}
     log(f"[bench] NVFP4 stress rotate+quantize {ms * 1e3:.1f} us = {out['rotate_quantize_nvfp4']['GB/s']:.0f} GB/s")
+    # quantizer variants on the same 16384 x 8192 input (block 32)
+    signs = torch.from_numpy(WL.draw_signs(sw.K, 1)).to(dev)
+    var = {}
+    for fmt, rule, sg in (("nvfp4", "fit", None), ("mxfp4", "oas", None), ("mxfp4", "ocp_floor", None),
+                          ("mxfp4", "fit", None), ("mxfp4", "standard", signs)):
+        g = 32 if fmt == "mxfp4" else 16
+        oo = (torch.empty((sw.M, sw.K // 2), dtype=torch.uint8, device=dev),
+              torch.empty((sw.M, sw.K // g), dtype=torch.uint8, device=dev),
+              torch.empty((1,), dtype=torch.float32, device=dev) if fmt == "nvfp4" else None)
+
+        def call(i, fmt=fmt, rule=rule, sg=sg, oo=oo):
+            B.fp4_rotate_quantize(bufs[i & 1], sw.block, fmt, out=oo, rule=rule, signs=sg)
+
+        for i in range(2):
+            call(i)
+        ms = time_batch(call, 10, torch)
+        nb = sw.M * sw.K * ((2 if fmt == "nvfp4" else 0) + 2 + 0.5 + 1.0 / g)
+        name = f"{fmt}_{rule}" + ("_signs" if sg is not None else "")
+        var[name] = {"us": ms * 1e3, "GB/s": nb / (ms * 1e-3) / 1e9, "frac_hbm": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log(f"[bench] variant {name}: {ms * 1e3:.1f} us = {var[name]['GB/s']:.0f} GB/s")
+    out["rotate_quantize_variants"] = {"workload": "16384x8192 bf16, block 32 (stress_nv32 input)", **var}
     del bufs, o
     # NVFP4 prefill GEMM, M=2048 K=4096 N=14336, Y bf16
     wl = WL.WORKLOADS["prefill_nv"]
@@ -166,7 +190,8 @@ def extra_rows(B, WL, torch, dev):
     tf = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
     out["gemm_nvfp4"] = {"workload": "prefill_nv: M=2048 K=4096 N=14336, block 16, Y bf16",
                          "us": ms * 1e3, "TFLOP/s": tf, "frac_bf16_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
-                         "frac_fp4_mfma_peak": tf / MFMA_FP4_PEAK_TFLOPS}
+                         "frac_fp4_mfma_peak": tf / MFMA_FP4_PEAK_TFLOPS,
+                         "traffic": measured_traffic("gemm_nvfp4_ring", "gemm_nvfp4_ring.hip")}
     log(f"[bench] NVFP4 GEMM {ms * 1e3:.1f} us = {tf:.0f} TFLOP/s")
     del xq, xs, wq, ws, y
     # decode-shaped MXFP4 GEMM: W 4096x4096 streamed once per call
@@ -188,6 +213,7 @@ def extra_rows(B, WL, torch, dev):
                                "us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
                                "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
                                "us_per_python_call": ms_calls * 1e3, "graph_replay_matches_eager": graph_ok,
+                               "traffic": measured_traffic("gemm_mxfp4_decode", "gemm_decode.hip"),
                                "note": "50 calls captured in one HIP graph; W (8.9 MB) stays in the 256 MB "
                                        "Infinity Cache across calls"}
         log(f"[bench] {name} GEMM {ms * 1e3:.2f} us in a graph = {out[f'gemm_{name}']['GB/s']:.0f} GB/s "
