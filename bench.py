@@ -106,6 +106,26 @@ def time_graph(fn, iters, torch):
     return start.elapsed_time(end) / iters
 
 
+def time_cold(fn, iters, torch, dev):
+    """Per-launch device time (us) of fn(i) with a 1 GiB buffer written before each launch (flushing
+    the 256 MB Infinity Cache and the L2s); returns the median and the 10th / 90th percentiles."""
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    ts = []
+    for i in range(iters):
+        flush.fill_(float(i))
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(i)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    del flush
+    ts.sort()
+    return {"median_us": ts[len(ts) // 2], "p10_us": ts[len(ts) // 10], "p90_us": ts[(9 * len(ts)) // 10],
+            "launches": iters}
+
+
 def cpu_baseline(wl, x_bits, w_bits):
     """The oracle (plain NumPy, untuned) on one full step of the workload."""
     from threadpoolctl import threadpool_info
@@ -113,10 +133,13 @@ def cpu_baseline(wl, x_bits, w_bits):
     from oracle import fp4_oracle as O
 
     wq, ws, wts = O.rotate_quantize(w_bits, wl.block, wl.fmt)  # offline, untimed (as on the GPU)
-    t0 = time.perf_counter()
-    xq, xs, xts = O.rotate_quantize(x_bits, wl.block, wl.fmt)
-    O.linear_f64(xq, xs, wq, ws, wl.fmt, xts, wts)
-    dt = time.perf_counter() - t0
+    # whole steps until about 10 s of CPU work (at most 12), averaged
+    steps, t0 = 0, time.perf_counter()
+    while steps < 12 and (steps == 0 or time.perf_counter() - t0 < 10.0):
+        xq, xs, xts = O.rotate_quantize(x_bits, wl.block, wl.fmt)
+        O.linear_f64(xq, xs, wq, ws, wl.fmt, xts, wts)
+        steps += 1
+    dt = (time.perf_counter() - t0) / steps
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     flops = 2.0 * wl.M * wl.N * wl.K
     return {
@@ -124,9 +147,9 @@ def cpu_baseline(wl, x_bits, w_bits):
         "unit": "TFLOP/s",
         "cores": int(max(blas) if blas else 1),
         "kind": "oracle",
-        "sample": f"one full step of {wl.name} (M={wl.M}, K={wl.K}, N={wl.N}): oracle rotate+quantize of X "
-                  f"(float32 FWHT, single-threaded NumPy) + float64 dequantized product (BLAS dgemm); "
-                  f"{dt:.2f} s on {os.cpu_count()} host threads",
+        "sample": f"{steps} full steps of {wl.name} (M={wl.M}, K={wl.K}, N={wl.N}), averaged: oracle "
+                  f"rotate+quantize of X (float32 FWHT, single-threaded NumPy) + float64 dequantized product "
+                  f"(BLAS dgemm); {dt:.2f} s per step, {os.cpu_count()} host threads visible",
         "seconds": dt,
     }
 
@@ -322,6 +345,9 @@ def main():
     roof_ms = time_batch(gemm_only, max(args.steps, 20), torch)
     roof_tflops = flops / (roof_ms * 1e-3) / 1e12
     log(f"[bench] GEMM back-to-back {roof_ms * 1e3:.1f} us = {roof_tflops:.0f} TFLOP/s ({roof_tflops / peak:.1%} of peak)")
+    cold = time_cold(gemm_only, 30, torch, dev)
+    log(f"[bench] GEMM cold (1 GiB written between launches): median {cold['median_us']:.1f} us "
+        f"(p10 {cold['p10_us']:.1f}, p90 {cold['p90_us']:.1f})")
 
     result = {
         "metric": METRIC,
@@ -354,6 +380,9 @@ def main():
             "algorithmic_flops": flops,
             "algorithmic_bytes": gemm_alg_bytes,
             "avg_launch_us": roof_ms * 1e3,
+            "cold": {**cold, "TFLOP/s_median": flops / (cold["median_us"] * 1e-6) / 1e12,
+                     "note": "each launch timed alone after writing a 1 GiB buffer, so W and X come from HBM "
+                             "instead of the 256 MB Infinity Cache"},
         },
         "components": {
             "rotate_quantize_step_input": {
