@@ -273,10 +273,11 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_mx(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// NVFP4 pass 1: T = max |y| over the tensor, accumulated with an integer
-// atomic max on the float bits (non-negative floats order like their bits).
-// max |fl32(z c)| = fl32(max|z| c) since rounding is monotone, so the final
-// multiply is applied once per chunk.
+// NVFP4 pass 1: the tensor scale s_t = fl32(T / 2688), T = max |y| over the tensor,
+// accumulated with an integer atomic max on the float bits (non-negative floats order
+// like their bits). x -> fl32(x c) and x -> fl32(x / 2688) are monotone, so
+// max fl32(|z| c) = fl32(max|z| c) (the multiply is applied once per chunk) and the
+// maximum over workgroups of fl32(m / 2688) is fl32(T / 2688): the word ends holding s_t.
 // ---------------------------------------------------------------------------
 __global__ void clear_word(unsigned* p) {
   if (threadIdx.x == 0) *p = 0u;
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restri
     float b = wmax[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) b = fmaxf(b, wmax[w]);
-    const unsigned bits = __float_as_uint(b);
+    const unsigned bits = __float_as_uint((float)((double)b / 2688.0));  // fl32(m / 2688)
     if (bits > __hip_atomic_load(amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(amax_bits, bits);
   }
 }
@@ -360,8 +361,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_nv(const uint16_t* __re
   const float c = __uint_as_float(hadamard_constant_bits(B));
 #pragma unroll
   for (int i = 0; i < 32; ++i) v[i] *= c;
-  const float T = __uint_as_float(*amax_bits);
-  const float s_t = (float)((double)T / 2688.0);  // = fl32(T / 2688)
+  const float s_t = __uint_as_float(*amax_bits);  // = fl32(T / 2688), left by pass 1
   v4u out;
   unsigned sc2 = 0;
   if (s_t == 0.f) {
@@ -408,14 +408,6 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_nv(const uint16_t* __re
   reinterpret_cast<uint16_t*>(scales)[gc] = (uint16_t)sc2;
 }
 
-// NVFP4 pass 3: replace T by s_t = fl32(T / 2688) in the caller's tensor-scale word.
-__global__ void finish_tensor_scale(float* ts) {
-  if (threadIdx.x == 0) {
-    const float T = __uint_as_float(*reinterpret_cast<unsigned*>(ts));
-    *ts = (float)((double)T / 2688.0);
-  }
-}
-
 RowMap make_rowmap(uint32_t cpr) {
   RowMap rm{cpr, 0, 0, 0};
   if ((cpr & (cpr - 1)) == 0) {
@@ -450,7 +442,6 @@ hipError_t launch_b(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int fm
   hipLaunchKernelGGL(rotate_amax<B>, grid_max, block, 0, st, X, ldx, rm, total, contiguous, signs, amax);
   hipLaunchKernelGGL((rotate_quant_nv<B, NV_RULE>), grid, block, 0, st, X, ldx, rm, total, contiguous, signs, amax,
                      codes, scales);
-  hipLaunchKernelGGL(finish_tensor_scale, dim3(1), dim3(64), 0, st, ts);
   return hipGetLastError();
 }
 

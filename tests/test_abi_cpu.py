@@ -91,6 +91,14 @@ def test_rotate_quantize_ex_validation(lib):
     assert b"fp4_quantize_weights_ex" in lib.fp4_last_error()
 
 
+def test_size_limits(lib):
+    # rows * K / 32 must fit in 31 bits (chunk indices); rejected before anything is launched
+    assert q(lib, M=1 << 26, K=1024, ldx=1024) == -2
+    assert q(lib, M=(1 << 26) - 1, K=1024, ldx=1 << 41) == -2   # leading dimension out of range
+    assert lib.fp4_linear(A16, A16, None, A16, A16, None, 1 << 31, 4, 128, 0, A16, 0, None) == -2
+    assert lib.fp4_linear(A16, A16, None, A16, A16, None, 4, 1 << 31, 128, 0, A16, 0, None) == -2
+
+
 def lin(lib, Xq=A16, Xs=A16, xts=None, Wq=A16, Ws=A16, wts=None, M=4, N=4, K=128, fmt=0, Y=A16, ydt=0):
     return lib.fp4_linear(Xq, Xs, xts, Wq, Ws, wts, M, N, K, fmt, Y, ydt, None)
 
