@@ -241,6 +241,26 @@ def extra_rows(B, WL, torch, dev):
                                        "Infinity Cache across calls"}
         log(f"[bench] {name} GEMM {ms * 1e3:.2f} us in a graph = {out[f'gemm_{name}']['GB/s']:.0f} GB/s "
             f"({ms_calls * 1e3:.2f} us per Python call; graph result matches eager: {graph_ok})")
+        # the whole decode step from bf16 X: two calls, or the one-launch fused kernel
+        xb = bf16_dev(WL.draw_x(wl), dev)
+        xqo = (torch.empty((wl.M, wl.K // 2), dtype=torch.uint8, device=dev),
+               torch.empty((wl.M, wl.K // 32), dtype=torch.uint8, device=dev), None)
+        y2 = torch.empty_like(y)
+
+        def two_calls(i):
+            B.fp4_rotate_quantize(xb, wl.block, "mxfp4", out=xqo)
+            B.fp4_linear(xqo[0], xqo[1], wq, ws, "mxfp4", out=y2)
+
+        def fused(i):
+            B.fp4_rotate_quantize_linear(xb, wq, ws, wl.block, out=y)
+
+        ms_two = time_graph(two_calls, 50, torch)
+        ms_fused = time_graph(fused, 50, torch)
+        same = bool(torch.equal(y, y2))
+        out[f"gemm_{name}"]["step_from_bf16_x"] = {"two_calls_us": ms_two * 1e3, "fused_us": ms_fused * 1e3,
+                                                   "fused_equals_two_calls": same}
+        log(f"[bench] {name} step from bf16 X in a graph: two calls {ms_two * 1e3:.2f} us, "
+            f"fused {ms_fused * 1e3:.2f} us (same result: {same})")
     return out
 
 

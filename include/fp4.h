@@ -180,6 +180,31 @@ FP4_API int fp4_linear(const uint8_t *Xq, const uint8_t *Xs, const float *x_ts,
                int64_t M, int64_t N, int64_t K, int fmt,
                void *Y, int y_dtype, void *stream);
 
+/*
+ * fp4_rotate_quantize_linear - one launch for the decode step of an MXFP4 linear layer:
+ * Y = fp4_linear(fp4_rotate_quantize(X, block, MXFP4), Wq, Ws), bit for bit the same as
+ * the two calls (the same device code quantizes X, into on-chip memory instead of HBM).
+ * Every workgroup quantizes the whole of X, so it is meant for a few tokens: on
+ * MI355X (K = N = 4096) one token takes 4.1 us against 5.6 us for the two calls,
+ * while at 16 tokens the redundant quantization makes it slower (8.2 against 7.5 us).
+ * "Bridging the Gap Between Promise and Performance for Microscaling FP4 Quantization"
+ * (gist.science, German edition), Technische Zusammenfassung §2
+ * "GPU-Kernel-Unterstützung (QuTLASS)": the online rotation fused with quantization,
+ * feeding the 4-bit matmul.
+ *
+ *  X       device bf16 [M, ldx], 16-byte aligned, ldx >= K, ldx % 8 == 0.
+ *  M       1..16 tokens.   K: a multiple of 512 with M * (K/2 + 16 + K/32) <= 160 KiB.
+ *  block   16, 32, 64 or 128 (the block W was quantized with).
+ *  Wq, Ws  MXFP4 weights from fp4_quantize_weights: uint8 [N, K/2] (16-byte aligned)
+ *          and [N, K/32] (4-byte aligned).
+ *  Y       device [M, N], float32 or bf16 (y_dtype), 16-byte aligned.
+ * Errors: FP4_E_BLOCK, FP4_E_FORMAT (y_dtype), FP4_E_NULLPTR, FP4_E_SHAPE (M, K, ldx or
+ * the on-chip size), FP4_E_ALIGN. One kernel launch on `stream`.
+ */
+FP4_API int fp4_rotate_quantize_linear(const void *X, int64_t M, int64_t K, int64_t ldx, int block,
+                                       const uint8_t *Wq, const uint8_t *Ws, int64_t N, void *Y, int y_dtype,
+                                       void *stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 FP4_API const char *fp4_last_error(void);
 

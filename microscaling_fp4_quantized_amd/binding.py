@@ -65,6 +65,8 @@ def load_library() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = qx_args
         f.restype = i32
+    lib.fp4_rotate_quantize_linear.argtypes = [vp, i64, i64, i64, i32, vp, vp, i64, vp, i32, vp]
+    lib.fp4_rotate_quantize_linear.restype = i32
     lib.fp4_linear.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32, vp]
     lib.fp4_linear.restype = i32
     lib.fp4_last_error.argtypes = []
@@ -150,6 +152,25 @@ def fp4_linear(xq, xs, wq, ws, fmt="mxfp4", x_ts=None, w_ts=None, out_dtype=torc
     y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
     _check(lib.fp4_linear(_ptr(xq), _ptr(xs), _ptr(x_ts), _ptr(wq), _ptr(ws), _ptr(w_ts), M, N, K, f,
                           _ptr(y), ydt, _stream(xq.device)))
+    return y
+
+
+def fp4_rotate_quantize_linear(x: torch.Tensor, wq, ws, block: int, out_dtype=torch.float32, out=None):
+    """One-launch decode step (MXFP4, 1 <= M <= 16): Y = fp4_linear(fp4_rotate_quantize(x), wq, ws)."""
+    lib = load_library()
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("fp4_rotate_quantize_linear: expects a 2-D bf16 CUDA tensor with unit column stride")
+    for t in (wq, ws):
+        if not t.is_cuda or t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("fp4_rotate_quantize_linear: weight codes and scales must be contiguous uint8 CUDA tensors")
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] * 2 != K:
+        raise ValueError("fp4_rotate_quantize_linear: X and W disagree on K")
+    ydt = {torch.float32: 0, torch.bfloat16: 1}[out_dtype]
+    y = torch.empty((M, N), dtype=out_dtype, device=x.device) if out is None else out
+    _check(lib.fp4_rotate_quantize_linear(_ptr(x), M, K, x.stride(0), int(block), _ptr(wq), _ptr(ws), N, _ptr(y), ydt,
+                                          _stream(x.device)))
     return y
 
 

@@ -72,6 +72,9 @@ hipError_t fp4_launch_gemm_mxfp4(const uint8_t* Xq, const uint8_t* Xs, const uin
                                  int out_bf16, hipStream_t stream);
 bool fp4_gemm_mxfp4_ring_fits(int64_t M, int64_t N, int64_t K);
 bool fp4_gemm_mxfp4_decode_fits(int64_t M, int64_t N, int64_t K);
+bool fp4_decode_fused_fits(int64_t M, int64_t N, int64_t K);
+hipError_t fp4_launch_decode_fused(const uint16_t* X, int64_t ldx, int block, const uint8_t* Wq, const uint8_t* Ws,
+                                   int64_t M, int64_t N, int64_t K, void* Y, int out_bf16, hipStream_t stream);
 hipError_t fp4_launch_gemm_mxfp4_decode(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
                                         int64_t M, int64_t N, int64_t K, void* Y, int out_bf16, hipStream_t stream);
 hipError_t fp4_launch_gemm_mxfp4_ring(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,

@@ -127,8 +127,29 @@ int fp4_linear(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const ui
   return launched(who, e);
 }
 
+int fp4_rotate_quantize_linear(const void* X, int64_t M, int64_t K, int64_t ldx, int block, const uint8_t* Wq,
+                               const uint8_t* Ws, int64_t N, void* Y, int y_dtype, void* stream) {
+  const char* who = "fp4_rotate_quantize_linear";
+  if (block != 16 && block != 32 && block != 64 && block != 128)
+    return fail(FP4_E_BLOCK, "%s: Hadamard block %d not in {16, 32, 64, 128}", who, block);
+  if (y_dtype != FP4_OUT_F32 && y_dtype != FP4_OUT_BF16)
+    return fail(FP4_E_FORMAT, "%s: unknown output dtype %d", who, y_dtype);
+  if (!X || !Wq || !Ws || !Y) return fail(FP4_E_NULLPTR, "%s: X, Wq, Ws and Y must be non-NULL", who);
+  if (M < 1 || M > 16 || N < 1 || K < 512 || K % 512 || N > 0x7FFFFFFF || K > 0x7FFFFFFF)
+    return fail(FP4_E_SHAPE, "%s: need 1 <= M <= 16, N >= 1 and K a positive multiple of 512 (M=%lld N=%lld K=%lld)",
+                who, (long long)M, (long long)N, (long long)K);
+  if (!fp4_decode_fused_fits(M, N, K))
+    return fail(FP4_E_SHAPE, "%s: M * K too large for the workgroup's LDS; use fp4_rotate_quantize + fp4_linear", who);
+  if (ldx < K || ldx > (int64_t)1 << 40) return fail(FP4_E_SHAPE, "%s: leading dimension %lld < K", who, (long long)ldx);
+  if (!aligned(X, 16) || ldx % 8) return fail(FP4_E_ALIGN, "%s: X must be 16-byte aligned, ldx %% 8 == 0", who);
+  if (!aligned(Wq, 16) || !aligned(Ws, 4) || !aligned(Y, 16))
+    return fail(FP4_E_ALIGN, "%s: Wq and Y must be 16-byte aligned, Ws 4-byte aligned", who);
+  return launched(who, fp4_launch_decode_fused(static_cast<const uint16_t*>(X), ldx, block, Wq, Ws, M, N, K, Y,
+                                               y_dtype == FP4_OUT_BF16, static_cast<hipStream_t>(stream)));
+}
+
 const char* fp4_last_error(void) { return g_err; }
 
-int fp4_abi_version(void) { return 110; }
+int fp4_abi_version(void) { return 120; }
 
 }  // extern "C"

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, s)
     # nothing else with C linkage leaks out
     assert {s for s in exported if s.startswith("fp4_")} == set(declared_symbols())
-    assert lib.fp4_abi_version() == 110
+    assert lib.fp4_abi_version() == 120
 
 
 A16 = 0x10000  # a 16-byte aligned fake address: never dereferenced, validation fails first
@@ -97,6 +97,24 @@ def test_size_limits(lib):
     assert q(lib, M=(1 << 26) - 1, K=1024, ldx=1 << 41) == -2   # leading dimension out of range
     assert lib.fp4_linear(A16, A16, None, A16, A16, None, 1 << 31, 4, 128, 0, A16, 0, None) == -2
     assert lib.fp4_linear(A16, A16, None, A16, A16, None, 4, 1 << 31, 128, 0, A16, 0, None) == -2
+
+
+def fused(lib, X=A16, M=4, K=512, ldx=512, block=32, Wq=A16, Ws=A16, N=64, Y=A16, ydt=0):
+    return lib.fp4_rotate_quantize_linear(X, M, K, ldx, block, Wq, Ws, N, Y, ydt, None)
+
+
+def test_fused_decode_validation(lib):
+    assert fused(lib, block=8) == -3
+    assert fused(lib, ydt=2) == -4
+    assert fused(lib, Ws=None) == -1
+    assert fused(lib, M=17) == -2                      # a few tokens only
+    assert fused(lib, M=0) == -2
+    assert fused(lib, K=640, ldx=640) == -2            # K % 512
+    assert fused(lib, M=16, K=1 << 15, ldx=1 << 15) == -2   # too large for on-chip memory
+    assert fused(lib, ldx=256) == -2
+    assert fused(lib, X=A16 + 2) == -5
+    assert fused(lib, Y=A16 + 4) == -5
+    assert b"fp4_rotate_quantize_linear" in lib.fp4_last_error()
 
 
 def lin(lib, Xq=A16, Xs=A16, xts=None, Wq=A16, Ws=A16, wts=None, M=4, N=4, K=128, fmt=0, Y=A16, ydt=0):

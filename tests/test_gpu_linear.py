@@ -244,3 +244,42 @@ def test_full_size_sampled(name):
     r = rel_fro(y[np.ix_(rows, cols)], ref)
     say(f"{name} sampled rel fro {r:.3e}")
     assert r <= GEMM_REL_FRO_TOL
+
+
+@pytest.mark.parametrize("M,N,K,block", [(1, 4096, 4096, 32), (4, 300, 512, 128), (16, 4096, 4096, 32),
+                                         (7, 77, 2048, 16), (16, 520, 1536, 64), (3, 64, 8192, 128)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_fused_decode_equals_two_calls(M, N, K, block, out_dtype):
+    # the one-launch decode step gives the same bits as fp4_rotate_quantize + fp4_linear, and
+    # both match the oracle's product of the oracle-quantized operands
+    x = WL.draw_normal_bf16((M, K), 1.0, seed=M + K)
+    x[:, ::97] = WL.bf16_bits_from_f32(np.full((M, len(range(0, K, 97))), 40.0, np.float32))  # outlier channels
+    wt = WL.draw_normal_bf16((N, K), 0.02, seed=N + 1)
+    say(f"case fused decode M {M} N {N} K {K} b{block} {out_dtype}")
+    wq = B.fp4_quantize_weights(dev_bf16(wt), block, "mxfp4")
+    xd = dev_bf16(x)
+    xq = B.fp4_rotate_quantize(xd, block, "mxfp4")
+    y2 = B.fp4_linear(xq[0], xq[1], wq[0], wq[1], "mxfp4", out_dtype=out_dtype)
+    y1 = B.fp4_rotate_quantize_linear(xd, wq[0], wq[1], block, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    ref = gemm_reference(x, wt, block, "mxfp4", np.arange(M), np.arange(N))
+    if out_dtype == torch.bfloat16:
+        ref = O.bf16_rne_f64(ref)
+    r = rel_fro(host(y1.float() if out_dtype == torch.bfloat16 else y1).astype(np.float64), ref)
+    say(f"fused decode rel fro {r:.3e}")
+    assert r <= GEMM_REL_FRO_TOL
+
+
+def test_fused_decode_strided_x():
+    M, N, K = 5, 256, 1024
+    x = WL.draw_normal_bf16((M, K), 1.0, seed=3)
+    wt = WL.draw_normal_bf16((N, K), 0.02, seed=4)
+    wide = torch.zeros((M, K + 64), dtype=torch.bfloat16, device="cuda")
+    wide[:, :K] = dev_bf16(x)
+    wq = B.fp4_quantize_weights(dev_bf16(wt), 32, "mxfp4")
+    y1 = B.fp4_rotate_quantize_linear(wide[:, :K], wq[0], wq[1], 32)
+    xq = B.fp4_rotate_quantize(dev_bf16(x), 32, "mxfp4")
+    y2 = B.fp4_linear(xq[0], xq[1], wq[0], wq[1], "mxfp4")
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
