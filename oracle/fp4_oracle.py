@@ -90,6 +90,11 @@ R14 Scale fitting ([BRIDGE-de] §2 "Einführung von MR-GPTQ", item 2: MXFP4 scal
     fl32(e2m1 * S) with S = fl32(d * s_t) (NV). Candidates are tried in the order
     standard, smaller, larger and replace the current one only when strictly better.
     Meant for weights (offline), where the extra work is paid once.
+R16 Given tensor scale (NVFP4, optional): s_t is supplied by the caller instead of being
+    computed from this tensor (a calibrated static activation scale; [BRIDGE-es] §2.B treats
+    the tensor scale as a quantity to optimise). Every step after the tensor maximum is the
+    same; group maxima above 2688 s_t saturate at E4M3 448 and elements at E2M1 6. s_t = 0
+    gives signed zeros, as in the computed case.
 R15 Randomized block Hadamard (the QuaRot lineage the pages cite, [BRIDGE-de] §2
     "Theoretische Analyse der Fehler"): each input channel k is multiplied by a sign
     s_k in {+1, -1} before the rotation, i.e. R = D H with D = diag(s). The product is
@@ -377,18 +382,25 @@ def _nv_codes(grp32: np.ndarray, scales: np.ndarray, s_t: np.float32):
     return codes, deq
 
 
-def quantize_nvfp4(y32: np.ndarray, tensor_amax: np.float32 | None = None, rule: str = "standard"):
+def quantize_nvfp4(y32: np.ndarray, tensor_amax: np.float32 | None = None, rule: str = "standard",
+                   tensor_scale=None):
     """NVFP4 codes, E4M3 scale codes and the float32 tensor scale (readings R5, R6; R14 for "fit").
 
     tensor_amax: the absolute maximum over the whole rotated tensor; computed
     from y32 when None (pass it in when y32 holds only some rows).
+    tensor_scale: a given s_t (reading R16); tensor_amax is then not used.
     """
     if rule not in ("standard", "fit"):
         raise ValueError(f"NVFP4 takes the standard or the fit rule, not {rule}")
     rows, K = y32.shape
     y32 = np.asarray(y32, dtype=np.float32)
-    T = np.float32(np.max(np.abs(y32))) if tensor_amax is None else np.float32(tensor_amax)
-    s_t = np.float32(T / np.float32(NV_TENSOR_DIVISOR))  # float32 division, rounded once
+    if tensor_scale is not None:
+        s_t = np.float32(tensor_scale)
+        if not (np.isfinite(s_t) and s_t >= 0):
+            raise ValueError("a given tensor scale must be finite and non-negative")
+    else:
+        T = np.float32(np.max(np.abs(y32))) if tensor_amax is None else np.float32(tensor_amax)
+        s_t = np.float32(T / np.float32(NV_TENSOR_DIVISOR))  # float32 division, rounded once
     grp = y32.reshape(rows, K // NV_GROUP, NV_GROUP)
     alpha_max = np.max(np.abs(grp), axis=2)
     if s_t == 0:
@@ -444,11 +456,12 @@ def apply_signs(x32: np.ndarray, signs) -> np.ndarray:
 
 
 def rotate_quantize(x_bits: np.ndarray, block: int, fmt: str, tensor_amax=None, rule: str = "standard",
-                    signs=None):
+                    signs=None, tensor_scale=None):
     """bf16 X [rows, K] -> (packed codes [rows, K/2], scale codes [rows, K/g], s_t or None).
 
     rule: "standard" (R4 / R5), "ocp_floor" (R12, MXFP4), "oas" (R13, MXFP4) or "fit" (R14);
-    signs: optional K values in {+1, -1} applied before the rotation (R15).
+    signs: optional K values in {+1, -1} applied before the rotation (R15);
+    tensor_scale: NVFP4 only, a given s_t (R16).
     """
     x32 = widen_bf16(x_bits)
     if x32.ndim != 2:
@@ -458,7 +471,7 @@ def rotate_quantize(x_bits: np.ndarray, block: int, fmt: str, tensor_amax=None, 
         codes, scales = quantize_mxfp4(y32, rule)
         return pack_nibbles(codes), scales, None
     if fmt == "nvfp4":
-        codes, scales, s_t = quantize_nvfp4(y32, tensor_amax, rule)
+        codes, scales, s_t = quantize_nvfp4(y32, tensor_amax, rule, tensor_scale)
         return pack_nibbles(codes), scales, s_t
     raise ValueError(fmt)
 

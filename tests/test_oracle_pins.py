@@ -554,3 +554,27 @@ def test_random_signs_reduce_and_rotate_like_dense_DH():
     assert np.array_equal(neg[1], pos[1])
     nz = (cp & 7) != 0
     assert np.array_equal(cn[nz], cp[nz] ^ 8)
+
+
+def test_given_tensor_scale():
+    x = WL.draw_x(WL.WORKLOADS["tiny"])
+    for rule in ("standard", "fit"):
+        dyn = O.rotate_quantize(x, 16, "nvfp4", rule=rule)
+        # the computed scale passed back in gives the computed result
+        given = O.rotate_quantize(x, 16, "nvfp4", rule=rule, tensor_scale=dyn[2])
+        assert all(np.array_equal(a, b) for a, b in zip(dyn[:2], given[:2])) and given[2] == dyn[2]
+    # a scale 8x too small: group codes saturate at 448 (0x7E) and every dequantized value stays
+    # within 6 * 448 * s_t, i.e. the clipping bound of the format
+    dyn = O.rotate_quantize(x, 16, "nvfp4")
+    small = np.float32(dyn[2] / 8)
+    q = O.rotate_quantize(x, 16, "nvfp4", tensor_scale=small)
+    assert q[1].max() == 0x7E
+    dq = O.dequantize(q[0], q[1], "nvfp4", small)
+    assert np.max(np.abs(dq)) <= 6 * 448 * float(small)
+    assert np.max(np.abs(dq)) == 6 * 448 * float(small)  # the outlier groups do clip
+    # power-of-two equivariance: X * 2^k with s_t * 2^k gives the same codes
+    x4 = WL.bf16_bits_from_f32(O.widen_bf16(x) * np.float32(4))
+    q4 = O.rotate_quantize(x4, 16, "nvfp4", tensor_scale=np.float32(dyn[2] * 4))
+    assert np.array_equal(q4[0], dyn[0]) and np.array_equal(q4[1], dyn[1])
+    z = O.rotate_quantize(x, 16, "nvfp4", tensor_scale=np.float32(0))
+    assert np.all(z[1] == 0) and np.all((O.unpack_nibbles(z[0]) & 7) == 0)
