@@ -182,20 +182,24 @@ def extra_rows(B, WL, torch, dev):
     # quantizer variants on the same 16384 x 8192 input (block 32)
     signs = torch.from_numpy(WL.draw_signs(sw.K, 1)).to(dev)
     var = {}
-    for fmt, rule, sg in (("nvfp4", "fit", None), ("mxfp4", "oas", None), ("mxfp4", "ocp_floor", None),
-                          ("mxfp4", "fit", None), ("mxfp4", "standard", signs)):
+    given = torch.tensor([float(o[2].item())], dtype=torch.float32, device=dev)  # the computed s_t, reused
+    for fmt, rule, sg in (("nvfp4", "fit", None), ("nvfp4", "given_scale", None), ("mxfp4", "oas", None),
+                          ("mxfp4", "ocp_floor", None), ("mxfp4", "fit", None), ("mxfp4", "standard", signs)):
         g = 32 if fmt == "mxfp4" else 16
         oo = (torch.empty((sw.M, sw.K // 2), dtype=torch.uint8, device=dev),
               torch.empty((sw.M, sw.K // g), dtype=torch.uint8, device=dev),
               torch.empty((1,), dtype=torch.float32, device=dev) if fmt == "nvfp4" else None)
 
         def call(i, fmt=fmt, rule=rule, sg=sg, oo=oo):
-            B.fp4_rotate_quantize(bufs[i & 1], sw.block, fmt, out=oo, rule=rule, signs=sg)
+            if rule == "given_scale":
+                B.fp4_rotate_quantize(bufs[i & 1], sw.block, fmt, out=oo, tensor_scale=given)
+            else:
+                B.fp4_rotate_quantize(bufs[i & 1], sw.block, fmt, out=oo, rule=rule, signs=sg)
 
         for i in range(2):
             call(i)
         ms = time_batch(call, 10, torch)
-        nb = sw.M * sw.K * ((2 if fmt == "nvfp4" else 0) + 2 + 0.5 + 1.0 / g)
+        nb = sw.M * sw.K * ((2 if fmt == "nvfp4" and rule != "given_scale" else 0) + 2 + 0.5 + 1.0 / g)
         name = f"{fmt}_{rule}" + ("_signs" if sg is not None else "")
         var[name] = {"us": ms * 1e3, "GB/s": nb / (ms * 1e-3) / 1e9, "frac_hbm": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         log(f"[bench] variant {name}: {ms * 1e3:.1f} us = {var[name]['GB/s']:.0f} GB/s")

@@ -52,7 +52,8 @@ enum {
   FP4_SCALE_STANDARD = 0,  /* the rules of fp4_rotate_quantize (both formats)                */
   FP4_SCALE_OCP_FLOOR = 1, /* MXFP4: e = floor(log2 alpha) - 2, maximum in [4, 8), saturated  */
   FP4_SCALE_OAS = 2,       /* MXFP4: overflow-aware scaling                                   */
-  FP4_SCALE_FIT = 3        /* both: least-squared-error neighbour of the standard scale       */
+  FP4_SCALE_FIT = 3,       /* both: least-squared-error neighbour of the standard scale       */
+  FP4_TENSOR_SCALE_IN = 0x10 /* flag, NVFP4 only: *tensor_scale is an input (a given s_t)    */
 };
 
 /* Output dtypes of fp4_linear. */
@@ -143,6 +144,13 @@ FP4_API int fp4_quantize_weights(const void *W, int64_t N, int64_t K, int64_t ld
  *                acc = fl32(acc + fl32(d * d)), with q * s exact for MXFP4 and
  *                fl32(q * S), S = fl32(d_e4m3 * s_t), for NVFP4. Intended for
  *                weights: it costs about three quantizations.
+ *              FP4_TENSOR_SCALE_IN may be OR-ed into FP4_SCALE_STANDARD or
+ *                FP4_SCALE_FIT (NVFP4 only): the tensor scale s_t is read from
+ *                *tensor_scale (a finite, non-negative float, e.g. a calibrated
+ *                static activation scale) instead of being computed from this
+ *                tensor; the word is left unchanged, the tensor-maximum pass is
+ *                skipped (one launch, one pass over X), and group maxima above
+ *                2688 s_t saturate at E4M3 448 and the elements at E2M1 6.
  *  signs       NULL, or device int8 [K], 16-byte aligned: the randomized block
  *              Hadamard R = D H with D = diag(signs). Channel k is negated before
  *              the rotation when signs[k] < 0 (entries are meant to be +1 or -1).

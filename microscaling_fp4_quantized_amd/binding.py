@@ -95,9 +95,10 @@ def _check(status: int):
 
 
 SCALE_RULES = {"standard": 0, "ocp_floor": 1, "oas": 2, "fit": 3}
+TENSOR_SCALE_IN = 0x10
 
 
-def _quantize(name: str, x: torch.Tensor, block: int, fmt, out=None, rule=None, signs=None):
+def _quantize(name: str, x: torch.Tensor, block: int, fmt, out=None, rule=None, signs=None, tensor_scale=None):
     lib = load_library()
     f = _FMT[fmt]
     if x.dim() != 2 or x.dtype != torch.bfloat16 or not x.is_cuda or x.stride(1) != 1:
@@ -110,32 +111,40 @@ def _quantize(name: str, x: torch.Tensor, block: int, fmt, out=None, rule=None, 
         ts = torch.empty((1,), dtype=torch.float32, device=x.device) if f == FP4_NVFP4 else None
     else:
         codes, scales, ts = out
-    if rule is None and signs is None:
+    if tensor_scale is not None:
+        # a given s_t: a device float32 [1] that the call reads and leaves unchanged
+        if tensor_scale.dtype != torch.float32 or not tensor_scale.is_cuda or tensor_scale.numel() != 1:
+            raise ValueError(f"{name}: tensor_scale must be a float32 CUDA tensor of one element")
+        ts = tensor_scale
+    if rule is None and signs is None and tensor_scale is None:
         _check(getattr(lib, name)(_ptr(x), M, K, x.stride(0), int(block), f, _ptr(codes), _ptr(scales),
                                   _ptr(ts), _stream(x.device)))
     else:
         if signs is not None and (signs.dtype != torch.int8 or not signs.is_cuda or signs.numel() != K
                                   or not signs.is_contiguous()):
             raise ValueError(f"{name}: signs must be a contiguous int8 CUDA tensor of K entries")
-        r = SCALE_RULES[rule or "standard"]
+        r = SCALE_RULES[rule or "standard"] | (TENSOR_SCALE_IN if tensor_scale is not None else 0)
         _check(getattr(lib, name + "_ex")(_ptr(x), M, K, x.stride(0), int(block), f, r, _ptr(signs), _ptr(codes),
                                           _ptr(scales), _ptr(ts), _stream(x.device)))
     return codes, scales, ts
 
 
-def fp4_rotate_quantize(x: torch.Tensor, block: int, fmt="mxfp4", out=None, rule=None, signs=None):
+def fp4_rotate_quantize(x: torch.Tensor, block: int, fmt="mxfp4", out=None, rule=None, signs=None,
+                        tensor_scale=None):
     """Online block-Hadamard rotation + FP4 quantization of bf16 activations.
 
     Returns (codes [M, K/2] uint8, scales [M, K/g] uint8, tensor_scale [1] float32 or None).
     ``out`` may pass preallocated (codes, scales, tensor_scale). ``rule`` ("standard",
-    "ocp_floor", "oas", "fit") and ``signs`` (int8 [K] of +-1) select fp4_rotate_quantize_ex.
+    "ocp_floor", "oas", "fit"), ``signs`` (int8 [K] of +-1) and ``tensor_scale`` (NVFP4: a
+    given s_t, float32 [1] on the device) select fp4_rotate_quantize_ex.
     """
-    return _quantize("fp4_rotate_quantize", x, block, fmt, out, rule, signs)
+    return _quantize("fp4_rotate_quantize", x, block, fmt, out, rule, signs, tensor_scale)
 
 
-def fp4_quantize_weights(w: torch.Tensor, block: int, fmt="mxfp4", out=None, rule=None, signs=None):
+def fp4_quantize_weights(w: torch.Tensor, block: int, fmt="mxfp4", out=None, rule=None, signs=None,
+                         tensor_scale=None):
     """Offline rotation + quantization of a weight matrix [N, K] (same contract)."""
-    return _quantize("fp4_quantize_weights", w, block, fmt, out, rule, signs)
+    return _quantize("fp4_quantize_weights", w, block, fmt, out, rule, signs, tensor_scale)
 
 
 def fp4_linear(xq, xs, wq, ws, fmt="mxfp4", x_ts=None, w_ts=None, out_dtype=torch.float32, out=None):

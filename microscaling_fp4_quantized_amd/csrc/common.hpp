@@ -65,8 +65,8 @@ __device__ __forceinline__ float e4m3_value(unsigned c) {
 // Launchers (defined next to their kernels). Arguments are already validated.
 // ---------------------------------------------------------------------------
 hipError_t fp4_launch_rotate_quantize(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int block,
-                                      int fmt, int rule, const int8_t* signs, uint8_t* codes, uint8_t* scales,
-                                      float* tensor_scale, hipStream_t stream);
+                                      int fmt, int rule, bool given_tensor_scale, const int8_t* signs,
+                                      uint8_t* codes, uint8_t* scales, float* tensor_scale, hipStream_t stream);
 hipError_t fp4_launch_gemm_mxfp4(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
                                  const uint8_t* Ws, int64_t M, int64_t N, int64_t K, void* Y,
                                  int out_bf16, hipStream_t stream);

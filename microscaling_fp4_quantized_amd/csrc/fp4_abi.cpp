@@ -61,13 +61,17 @@ int quantize(const char* who, const void* X, int64_t M, int64_t K, int64_t ld, i
              const int8_t* signs, uint8_t* codes, uint8_t* scales, float* ts, void* stream) {
   int st = check_quantize(who, X, M, K, ld, block, fmt, codes, scales, ts);
   if (st != FP4_OK) return st;
+  const bool given_ts = (rule & FP4_TENSOR_SCALE_IN) != 0;
+  rule &= ~FP4_TENSOR_SCALE_IN;
+  if (given_ts && fmt != FP4_NVFP4) return fail(FP4_E_FORMAT, "%s: a given tensor scale applies to NVFP4 only", who);
   if (rule != FP4_SCALE_STANDARD && rule != FP4_SCALE_OCP_FLOOR && rule != FP4_SCALE_OAS && rule != FP4_SCALE_FIT)
     return fail(FP4_E_FORMAT, "%s: unknown scale rule %d", who, rule);
   if (fmt == FP4_NVFP4 && (rule == FP4_SCALE_OCP_FLOOR || rule == FP4_SCALE_OAS))
     return fail(FP4_E_FORMAT, "%s: scale rule %d applies to MXFP4 only", who, rule);
   if (signs && !aligned(signs, 16)) return fail(FP4_E_ALIGN, "%s: signs must be 16-byte aligned", who);
   return launched(who, fp4_launch_rotate_quantize(static_cast<const uint16_t*>(X), M, K, ld, block, fmt, rule,
-                                                  signs, codes, scales, ts, static_cast<hipStream_t>(stream)));
+                                                  given_ts, signs, codes, scales, ts,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace

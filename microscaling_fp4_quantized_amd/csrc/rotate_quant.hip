@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_nv(const uint16_t* __re
   const float c = __uint_as_float(hadamard_constant_bits(B));
 #pragma unroll
   for (int i = 0; i < 32; ++i) v[i] *= c;
-  const float s_t = __uint_as_float(*amax_bits);  // = fl32(T / 2688), left by pass 1
+  const float s_t = __uint_as_float(*amax_bits);  // = fl32(T / 2688) left by pass 1, or given by the caller
   v4u out;
   unsigned sc2 = 0;
   if (s_t == 0.f) {
@@ -284,8 +284,8 @@ RowMap make_rowmap(uint32_t cpr) {
 }
 
 template <int B, int RULE>
-hipError_t launch_b(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int fmt, const int8_t* signs,
-                    uint8_t* codes, uint8_t* scales, float* ts, hipStream_t st) {
+hipError_t launch_b(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int fmt, bool given_ts,
+                    const int8_t* signs, uint8_t* codes, uint8_t* scales, float* ts, hipStream_t st) {
   const uint32_t cpr = (uint32_t)(K / 32);
   const uint32_t total = (uint32_t)(M * (K / 32));
   const RowMap rm = make_rowmap(cpr);
@@ -298,22 +298,24 @@ hipError_t launch_b(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int fm
   }
   constexpr int NV_RULE = RULE == kRuleFit ? kRuleFit : kRuleStandard;  // other rules are MXFP4 only
   unsigned* amax = reinterpret_cast<unsigned*>(ts);
-  hipLaunchKernelGGL(clear_word, dim3(1), dim3(64), 0, st, amax);
-  const dim3 grid_max(grid.x < 2048u ? grid.x : 2048u);  // 8 workgroups per CU, grid-stride
-  hipLaunchKernelGGL(rotate_amax<B>, grid_max, block, 0, st, X, ldx, rm, total, contiguous, signs, amax);
+  if (!given_ts) {  // otherwise the caller's s_t is already in the word
+    hipLaunchKernelGGL(clear_word, dim3(1), dim3(64), 0, st, amax);
+    const dim3 grid_max(grid.x < 2048u ? grid.x : 2048u);  // 8 workgroups per CU, grid-stride
+    hipLaunchKernelGGL(rotate_amax<B>, grid_max, block, 0, st, X, ldx, rm, total, contiguous, signs, amax);
+  }
   hipLaunchKernelGGL((rotate_quant_nv<B, NV_RULE>), grid, block, 0, st, X, ldx, rm, total, contiguous, signs, amax,
                      codes, scales);
   return hipGetLastError();
 }
 
 template <int RULE>
-hipError_t launch_rule(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int block, int fmt,
+hipError_t launch_rule(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int block, int fmt, bool given_ts,
                        const int8_t* signs, uint8_t* codes, uint8_t* scales, float* ts, hipStream_t st) {
   switch (block) {
-    case 16: return launch_b<16, RULE>(X, M, K, ldx, fmt, signs, codes, scales, ts, st);
-    case 32: return launch_b<32, RULE>(X, M, K, ldx, fmt, signs, codes, scales, ts, st);
-    case 64: return launch_b<64, RULE>(X, M, K, ldx, fmt, signs, codes, scales, ts, st);
-    default: return launch_b<128, RULE>(X, M, K, ldx, fmt, signs, codes, scales, ts, st);
+    case 16: return launch_b<16, RULE>(X, M, K, ldx, fmt, given_ts, signs, codes, scales, ts, st);
+    case 32: return launch_b<32, RULE>(X, M, K, ldx, fmt, given_ts, signs, codes, scales, ts, st);
+    case 64: return launch_b<64, RULE>(X, M, K, ldx, fmt, given_ts, signs, codes, scales, ts, st);
+    default: return launch_b<128, RULE>(X, M, K, ldx, fmt, given_ts, signs, codes, scales, ts, st);
   }
 }
 
@@ -321,16 +323,16 @@ hipError_t launch_rule(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int
 }  // namespace fp4
 
 hipError_t fp4_launch_rotate_quantize(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int block,
-                                      int fmt, int rule, const int8_t* signs, uint8_t* codes, uint8_t* scales,
-                                      float* ts, hipStream_t st) {
+                                      int fmt, int rule, bool given_ts, const int8_t* signs, uint8_t* codes,
+                                      uint8_t* scales, float* ts, hipStream_t st) {
   switch (rule) {
     case fp4::kRuleOcpFloor:
-      return fp4::launch_rule<fp4::kRuleOcpFloor>(X, M, K, ldx, block, fmt, signs, codes, scales, ts, st);
+      return fp4::launch_rule<fp4::kRuleOcpFloor>(X, M, K, ldx, block, fmt, given_ts, signs, codes, scales, ts, st);
     case fp4::kRuleOas:
-      return fp4::launch_rule<fp4::kRuleOas>(X, M, K, ldx, block, fmt, signs, codes, scales, ts, st);
+      return fp4::launch_rule<fp4::kRuleOas>(X, M, K, ldx, block, fmt, given_ts, signs, codes, scales, ts, st);
     case fp4::kRuleFit:
-      return fp4::launch_rule<fp4::kRuleFit>(X, M, K, ldx, block, fmt, signs, codes, scales, ts, st);
+      return fp4::launch_rule<fp4::kRuleFit>(X, M, K, ldx, block, fmt, given_ts, signs, codes, scales, ts, st);
     default:
-      return fp4::launch_rule<fp4::kRuleStandard>(X, M, K, ldx, block, fmt, signs, codes, scales, ts, st);
+      return fp4::launch_rule<fp4::kRuleStandard>(X, M, K, ldx, block, fmt, given_ts, signs, codes, scales, ts, st);
   }
 }

@@ -45,7 +45,7 @@ def tensor_amax(x_bits: np.ndarray, block: int, chunk_rows: int = 2048, signs=No
 
 
 def compare_quant(gpu, x_bits: np.ndarray, block: int, fmt: str, rows=None, t_amax=None, rule="standard",
-                  signs=None):
+                  signs=None, tensor_scale=None):
     """gpu = (codes, scales, ts) torch tensors for all rows; rows = sampled row indices.
 
     rule / signs: the quantizer variant both sides ran (the flags below are those of the
@@ -54,9 +54,10 @@ def compare_quant(gpu, x_bits: np.ndarray, block: int, fmt: str, rows=None, t_am
     if rows is None:
         rows = np.arange(x_bits.shape[0])
     xr = x_bits[rows]
-    if fmt == "nvfp4" and t_amax is None:
+    if fmt == "nvfp4" and t_amax is None and tensor_scale is None:
         t_amax = tensor_amax(x_bits, block, signs=signs)
-    o_packed, o_scales, o_ts = O.rotate_quantize(xr, block, fmt, tensor_amax=t_amax, rule=rule, signs=signs)
+    o_packed, o_scales, o_ts = O.rotate_quantize(xr, block, fmt, tensor_amax=t_amax, rule=rule, signs=signs,
+                                                 tensor_scale=tensor_scale)
     gc = host(g_codes)[rows]
     gs = host(g_scales)[rows]
     y32 = O.rotate_fwht_f32(O.apply_signs(O.widen_bf16(xr), signs), block)

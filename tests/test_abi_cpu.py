@@ -84,6 +84,9 @@ def test_rotate_quantize_ex_validation(lib):
     assert qx(lib, rule=1, fmt=1, ts=A16) == -4    # the OCP floor rule is MXFP4 only
     assert qx(lib, rule=2, fmt=1, ts=A16) == -4    # so is OAS
     assert qx(lib, rule=3, signs=A16 + 8) == -5    # signs 16-byte aligned
+    assert qx(lib, rule=0x10) == -4                # a given tensor scale is NVFP4 only
+    assert qx(lib, rule=0x11, fmt=1, ts=A16) == -4  # OCP floor stays MXFP4 only with the flag
+    assert qx(lib, rule=0x20) == -4                # unknown flag
     assert qx(lib, rule=0, X=None) == -1           # the checks shared with fp4_rotate_quantize come first
     assert qx(lib, rule=9, block=8) == -3
     assert b"fp4_rotate_quantize_ex" in lib.fp4_last_error()

@@ -157,3 +157,33 @@ def test_ex_errors_raise():
         B.fp4_rotate_quantize(x, 32, "nvfp4", rule="oas")
     with pytest.raises(ValueError):
         B.fp4_rotate_quantize(x, 32, "mxfp4", signs=torch.ones(63, dtype=torch.int8, device="cuda"))
+
+
+@pytest.mark.parametrize("block", [16, 32])
+@pytest.mark.parametrize("rule", ["standard", "fit"])
+def test_nv_given_tensor_scale(block, rule):
+    # s_t supplied by the caller: the computed one, 1/8 of it (heavy clipping) and 3x it
+    w = WL.WORKLOADS["tiny"]
+    for x in (WL.draw_x(w), WL.draw_normal_bf16((45, 640), 0.3, seed=block)):
+        s_dyn = O.rotate_quantize(x, block, "nvfp4")[2]
+        for factor in (1.0, 0.125, 3.0):
+            st = np.float32(s_dyn * np.float32(factor))
+            ts = torch.tensor([float(st)], dtype=torch.float32, device="cuda")
+            say(f"case NV given s_t x{factor} b{block} {rule} X {x.shape}")
+            q = B.fp4_rotate_quantize(dev_bf16(x), block, "nvfp4", rule=rule, tensor_scale=ts)
+            torch.cuda.synchronize()
+            assert q[2].data_ptr() == ts.data_ptr() and float(ts.item()) == float(st)  # read, not written
+            assert_quant_parity(compare_quant(q, x, block, "nvfp4", rule=rule, tensor_scale=st),
+                                f"nv given x{factor}", exact=True)
+
+
+def test_nv_given_tensor_scale_stress_sampled():
+    w = WL.WORKLOADS["stress_nv32"]
+    x = WL.draw_x(w)
+    st = np.float32(tensor_amax(x, w.block) / np.float32(2688.0) / np.float32(4.0))
+    ts = torch.tensor([float(st)], dtype=torch.float32, device="cuda")
+    q = B.fp4_rotate_quantize(dev_bf16(x), w.block, "nvfp4", tensor_scale=ts)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, w.M - 1], np.random.default_rng(9).choice(w.M, 16, replace=False)]))
+    assert_quant_parity(compare_quant(q, x, w.block, "nvfp4", rows=rows, tensor_scale=st), "nv given stress",
+                        exact=True)
