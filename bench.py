@@ -107,12 +107,16 @@ def time_graph(fn, iters, torch):
 
 
 def time_cold(fn, iters, torch, dev):
-    """Per-launch device time (us) of fn(i) with a 1 GiB buffer written before each launch (flushing
-    the 256 MB Infinity Cache and the L2s); returns the median and the 10th / 90th percentiles."""
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    """Per-launch device time (us) of fn(i) with a 1 GiB buffer read before each launch, so that the
+    256 MB Infinity Cache and the L2s hold only clean lines of that buffer (a written flush would
+    leave dirty lines whose write-back the timed kernel would pay for); returns the median and the
+    10th / 90th percentiles."""
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
     ts = []
     for i in range(iters):
-        flush.fill_(float(i))
+        torch.sum(flush, dim=(0,), out=sink)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -162,14 +166,17 @@ def extra_rows(B, WL, torch, dev):
     # NVFP4 rotate+quantize, 16384 x 8192, block 32
     sw = WL.WORKLOADS["stress_nv32"]
     sx = WL.draw_x(sw)
-    bufs = [bf16_dev(sx, dev), bf16_dev(sx, dev)]
+    bufs = [bf16_dev(sx, dev) for _ in range(3)]
     del sx
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    torch.sum(flush, dim=(0,))
+    del flush
     o = (torch.empty((sw.M, sw.K // 2), dtype=torch.uint8, device=dev),
          torch.empty((sw.M, sw.K // 16), dtype=torch.uint8, device=dev),
          torch.empty((1,), dtype=torch.float32, device=dev))
     for i in range(3):
-        B.fp4_rotate_quantize(bufs[i & 1], sw.block, "nvfp4", out=o)
-    ms = time_batch(lambda i: B.fp4_rotate_quantize(bufs[i & 1], sw.block, "nvfp4", out=o), 20, torch)
+        B.fp4_rotate_quantize(bufs[i % 3], sw.block, "nvfp4", out=o)
+    ms = time_batch(lambda i: B.fp4_rotate_quantize(bufs[i % 3], sw.block, "nvfp4", out=o), 21, torch)
     nbytes = sw.M * sw.K * (2 + 2 + 0.5 + 1.0 / 16) + 8
     t_max = measured_traffic("rotate_amax_b32", "rotate_quant.hip")
     t_nv = measured_traffic("rotate_quant_nv_b32", "rotate_quant.hip")
@@ -192,13 +199,13 @@ def extra_rows(B, WL, torch, dev):
 
         def call(i, fmt=fmt, rule=rule, sg=sg, oo=oo):
             if rule == "given_scale":
-                B.fp4_rotate_quantize(bufs[i & 1], sw.block, fmt, out=oo, tensor_scale=given)
+                B.fp4_rotate_quantize(bufs[i % 3], sw.block, fmt, out=oo, tensor_scale=given)
             else:
-                B.fp4_rotate_quantize(bufs[i & 1], sw.block, fmt, out=oo, rule=rule, signs=sg)
+                B.fp4_rotate_quantize(bufs[i % 3], sw.block, fmt, out=oo, rule=rule, signs=sg)
 
         for i in range(2):
             call(i)
-        ms = time_batch(call, 10, torch)
+        ms = time_batch(call, 12, torch)
         nb = sw.M * sw.K * ((2 if fmt == "nvfp4" and rule != "given_scale" else 0) + 2 + 0.5 + 1.0 / g)
         name = f"{fmt}_{rule}" + ("_signs" if sg is not None else "")
         var[name] = {"us": ms * 1e3, "GB/s": nb / (ms * 1e-3) / 1e9, "frac_hbm": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
@@ -370,7 +377,7 @@ def main():
     roof_tflops = flops / (roof_ms * 1e-3) / 1e12
     log(f"[bench] GEMM back-to-back {roof_ms * 1e3:.1f} us = {roof_tflops:.0f} TFLOP/s ({roof_tflops / peak:.1%} of peak)")
     cold = time_cold(gemm_only, 30, torch, dev)
-    log(f"[bench] GEMM cold (1 GiB written between launches): median {cold['median_us']:.1f} us "
+    log(f"[bench] GEMM cold (1 GiB read between launches): median {cold['median_us']:.1f} us "
         f"(p10 {cold['p10_us']:.1f}, p90 {cold['p90_us']:.1f})")
 
     result = {
@@ -405,7 +412,7 @@ def main():
             "algorithmic_bytes": gemm_alg_bytes,
             "avg_launch_us": roof_ms * 1e3,
             "cold": {**cold, "TFLOP/s_median": flops / (cold["median_us"] * 1e-6) / 1e12,
-                     "note": "each launch timed alone after writing a 1 GiB buffer, so W and X come from HBM "
+                     "note": "each launch timed alone after reading a 1 GiB buffer, so W and X come from HBM "
                              "instead of the 256 MB Infinity Cache"},
         },
         "components": {
@@ -422,25 +429,34 @@ def main():
         sw = WL.WORKLOADS[args.stress]
         log(f"[bench] rotate+quantize stress {sw.name}: {sw.M}x{sw.K} {sw.fmt} block {sw.block}")
         sx = WL.draw_x(sw)
-        # two input buffers used alternately so no launch finds its X in the 256 MB Infinity Cache
-        bufs = [bf16_dev(sx, dev), bf16_dev(sx, dev)]
+        # three input buffers in rotation, and a 1 GiB read after uploading them, so that no launch
+        # finds its X in the 256 MB Infinity Cache (streaming loads may leave lines that were
+        # resident before the first launch in place)
+        bufs = [bf16_dev(sx, dev) for _ in range(3)]
         del sx
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        torch.sum(flush, dim=(0,))
+        del flush
         sg = B.group_size(sw.fmt)
         outs = (torch.empty((sw.M, sw.K // 2), dtype=torch.uint8, device=dev),
                 torch.empty((sw.M, sw.K // sg), dtype=torch.uint8, device=dev),
                 torch.empty((1,), dtype=torch.float32, device=dev) if sw.fmt == "nvfp4" else None)
 
         def rq(i):
-            B.fp4_rotate_quantize(bufs[i & 1], sw.block, sw.fmt, out=outs)
+            B.fp4_rotate_quantize(bufs[i % 3], sw.block, sw.fmt, out=outs)
 
         for i in range(5):
             rq(i)
-        s_ms = time_batch(rq, 40, torch)
+        s_ms = time_batch(rq, 42, torch)
+        s_cold = time_cold(rq, 20, torch, dev)
         s_bytes = sw.M * sw.K * (2 + 0.5 + 1.0 / sg)
         if sw.fmt == "nvfp4":
             s_bytes += sw.M * sw.K * 2
         gbs = s_bytes / (s_ms * 1e-3) / 1e9
         log(f"[bench] stress rotate+quantize {s_ms * 1e3:.1f} us = {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM)")
+        cold_gbs = s_bytes / (s_cold["median_us"] * 1e-6) / 1e9
+        log(f"[bench] stress rotate+quantize cold (1 GiB read before each launch): median {s_cold['median_us']:.1f} us "
+            f"= {cold_gbs:.0f} GB/s ({cold_gbs / HBM_PEAK_GBS:.1%} of HBM)")
         result["roofline_rotate_quantize"] = {
             "kernel": "rotate_quant_mx" if sw.fmt == "mxfp4" else "rotate_amax + rotate_quant_nv",
             "workload": f"{sw.name}: X {sw.M}x{sw.K} bf16 Student-t(3) x log-normal channel scales, "
@@ -454,6 +470,8 @@ def main():
             if sw.fmt == "mxfp4" else None,
             "algorithmic_bytes": s_bytes,
             "avg_launch_us": s_ms * 1e3,
+            "cold": {**s_cold, "GB/s_median": cold_gbs, "frac_median": cold_gbs / HBM_PEAK_GBS,
+                     "note": "each launch timed alone after reading a 1 GiB buffer (no Infinity Cache residency)"},
         }
         del bufs, outs
 

@@ -54,29 +54,34 @@ __device__ __forceinline__ const uint16_t* chunk_ptr(const uint16_t* __restrict_
 // The wave's four coalesced 16-byte loads: instruction j covers 1 KB, part (lane % 4) of chunk
 // wbase + 16 j + lane / 4. Past the end the chunk index is clamped to the last chunk, so every
 // address stays inside X and all four loads are in flight before the first LDS write.
-template <bool CONTIG>
+template <bool CONTIG, bool NT>
 __device__ __forceinline__ void load_wave(const uint16_t* __restrict__ X, int64_t ldx, uint32_t wbase, uint32_t total,
                                           const RowMap& rm, v4u r[4]) {
   const uint32_t lane = threadIdx.x & 63;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint32_t owner = min(wbase + 16 * j + (lane >> 2), total - 1);
-    r[j] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(chunk_ptr<CONTIG>(X, ldx, owner, rm)) + (lane & 3));
+    const v4u* p = reinterpret_cast<const v4u*>(chunk_ptr<CONTIG>(X, ldx, owner, rm)) + (lane & 3);
+    r[j] = NT ? __builtin_nontemporal_load(p) : *p;
   }
 }
 
 // Load the lane's 32 bf16 values and widen them to float32 (exact). The wave reads its 64
 // chunks with fully coalesced loads and transposes them through LDS, so that each lane ends up
 // with its own 64 contiguous bytes. Every lane of the wave must call this (lanes whose chunk
-// is past the end still load for the others); stage is the wave's LDS area.
+// is past the end still load for the others); stage is the wave's LDS area. `mode` bit 0: rows
+// are contiguous (ldx == K); bit 1: streaming (nontemporal) loads, used for inputs too large to
+// stay in the caches; smaller inputs (often just written by the previous kernel) load normally.
 __device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ X, int64_t ldx, uint32_t gc, uint32_t total,
-                                           const RowMap& rm, bool contiguous, v4u* stage, float v[32]) {
+                                           const RowMap& rm, int mode, v4u* stage, float v[32]) {
   const uint32_t lane = threadIdx.x & 63, wbase = gc - lane;
   v4u r[4];
-  if (contiguous)
-    load_wave<true>(X, ldx, wbase, total, rm, r);
-  else
-    load_wave<false>(X, ldx, wbase, total, rm, r);
+  switch (mode & 3) {
+    case 0: load_wave<false, false>(X, ldx, wbase, total, rm, r); break;
+    case 1: load_wave<true, false>(X, ldx, wbase, total, rm, r); break;
+    case 2: load_wave<false, true>(X, ldx, wbase, total, rm, r); break;
+    default: load_wave<true, true>(X, ldx, wbase, total, rm, r); break;
+  }
   asm volatile("" ::: "memory");  // earlier reads of the area (a previous chunk) stay before these writes
 #pragma unroll
   for (int j = 0; j < 4; ++j) stage[(16 * j + (lane >> 2)) + (lane & 3) * 68] = r[j];
@@ -117,14 +122,14 @@ __device__ __forceinline__ void apply_signs(float v[32], const int8_t* __restric
 // ---------------------------------------------------------------------------
 template <int B, int RULE>
 __global__ __launch_bounds__(kThreads) void rotate_quant_mx(const uint16_t* __restrict__ X, int64_t ldx,
-                                                            RowMap rm, uint32_t total, int contiguous,
+                                                            RowMap rm, uint32_t total, int load_mode,
                                                             const int8_t* __restrict__ signs,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
   __shared__ __attribute__((aligned(16))) v4u stage[kThreads / 64][kStage];
   const uint32_t gc = blockIdx.x * kThreads + threadIdx.x;
   float v[32];
-  load_chunk(X, ldx, gc, total, rm, contiguous != 0, stage[threadIdx.x >> 6], v);
+  load_chunk(X, ldx, gc, total, rm, load_mode, stage[threadIdx.x >> 6], v);
   if (gc >= total) return;  // whole quads leave together (total % (B/32) == 0)
   if (signs) apply_signs(v, signs, gc, rm);
   v4u out;
@@ -146,7 +151,7 @@ __global__ void clear_word(unsigned* p) {
 
 template <int B>
 __global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restrict__ X, int64_t ldx,
-                                                        RowMap rm, uint32_t total, int contiguous,
+                                                        RowMap rm, uint32_t total, int load_mode,
                                                         const int8_t* __restrict__ signs,
                                                         unsigned* __restrict__ amax_bits) {
   __shared__ __attribute__((aligned(16))) v4u stage[kThreads / 64][kStage];
@@ -157,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restri
   for (uint32_t base = blockIdx.x * kThreads; base < total; base += gridDim.x * kThreads) {
     const uint32_t gc = base + threadIdx.x;
     float v[32];
-    load_chunk(X, ldx, gc, total, rm, contiguous != 0, stage[threadIdx.x >> 6], v);
+    load_chunk(X, ldx, gc, total, rm, load_mode, stage[threadIdx.x >> 6], v);
     if (gc < total) {
       if (signs) apply_signs(v, signs, gc, rm);
       fwht<B>(v);
@@ -207,7 +212,7 @@ __device__ __forceinline__ void nv_group(const float* y, unsigned code, float s_
 
 template <int B, int RULE>
 __global__ __launch_bounds__(kThreads) void rotate_quant_nv(const uint16_t* __restrict__ X, int64_t ldx,
-                                                            RowMap rm, uint32_t total, int contiguous,
+                                                            RowMap rm, uint32_t total, int load_mode,
                                                             const int8_t* __restrict__ signs,
                                                             const unsigned* __restrict__ amax_bits,
                                                             uint8_t* __restrict__ codes,
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_nv(const uint16_t* __re
   __shared__ __attribute__((aligned(16))) v4u stage[kThreads / 64][kStage];
   const uint32_t gc = blockIdx.x * kThreads + threadIdx.x;
   float v[32];
-  load_chunk(X, ldx, gc, total, rm, contiguous != 0, stage[threadIdx.x >> 6], v);
+  load_chunk(X, ldx, gc, total, rm, load_mode, stage[threadIdx.x >> 6], v);
   if (gc >= total) return;
   if (signs) apply_signs(v, signs, gc, rm);
   fwht<B>(v);
@@ -289,10 +294,13 @@ hipError_t launch_b(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int fm
   const uint32_t cpr = (uint32_t)(K / 32);
   const uint32_t total = (uint32_t)(M * (K / 32));
   const RowMap rm = make_rowmap(cpr);
-  const int contiguous = ldx == K;
+  // load mode: bit 0 contiguous rows; bit 1 streaming loads for inputs beyond 64 MiB (they would
+  // not stay in the 256 MB Infinity Cache next to their outputs anyway)
+  const int64_t x_bytes = M * ldx * 2;
+  const int load_mode = (ldx == K ? 1 : 0) | (x_bytes > (64ll << 20) ? 2 : 0);
   const dim3 grid((total + kThreads - 1) / kThreads), block(kThreads);
   if (fmt == 0) {
-    hipLaunchKernelGGL((rotate_quant_mx<B, RULE>), grid, block, 0, st, X, ldx, rm, total, contiguous, signs, codes,
+    hipLaunchKernelGGL((rotate_quant_mx<B, RULE>), grid, block, 0, st, X, ldx, rm, total, load_mode, signs, codes,
                        scales);
     return hipGetLastError();
   }
@@ -301,9 +309,10 @@ hipError_t launch_b(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int fm
   if (!given_ts) {  // otherwise the caller's s_t is already in the word
     hipLaunchKernelGGL(clear_word, dim3(1), dim3(64), 0, st, amax);
     const dim3 grid_max(grid.x < 2048u ? grid.x : 2048u);  // 8 workgroups per CU, grid-stride
-    hipLaunchKernelGGL(rotate_amax<B>, grid_max, block, 0, st, X, ldx, rm, total, contiguous, signs, amax);
+    // the max pass loads normally so that as much of X as fits stays cached for the second pass
+    hipLaunchKernelGGL(rotate_amax<B>, grid_max, block, 0, st, X, ldx, rm, total, load_mode & 1, signs, amax);
   }
-  hipLaunchKernelGGL((rotate_quant_nv<B, NV_RULE>), grid, block, 0, st, X, ldx, rm, total, contiguous, signs, amax,
+  hipLaunchKernelGGL((rotate_quant_nv<B, NV_RULE>), grid, block, 0, st, X, ldx, rm, total, load_mode, signs, amax,
                      codes, scales);
   return hipGetLastError();
 }
