@@ -98,6 +98,15 @@ SCALE_RULES = {"standard": 0, "ocp_floor": 1, "oas": 2, "fit": 3}
 TENSOR_SCALE_IN = 0x10
 
 
+def _expect(t, shape, dtype, name, what):
+    """Refuse anything but a contiguous CUDA tensor of this shape and dtype: the kernels take plain
+    pointers and trust the sizes they imply, so a short buffer would be read or written out of bounds."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != dtype or \
+            tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        got = repr(t) if not isinstance(t, torch.Tensor) else f"{tuple(t.shape)} {t.dtype} on {t.device}"
+        raise ValueError(f"{name}: {what} must be a contiguous {dtype} CUDA tensor of shape {tuple(shape)}, got {got}")
+
+
 def _quantize(name: str, x: torch.Tensor, block: int, fmt, out=None, rule=None, signs=None, tensor_scale=None):
     lib = load_library()
     f = _FMT[fmt]
@@ -111,6 +120,13 @@ def _quantize(name: str, x: torch.Tensor, block: int, fmt, out=None, rule=None, 
         ts = torch.empty((1,), dtype=torch.float32, device=x.device) if f == FP4_NVFP4 else None
     else:
         codes, scales, ts = out
+        _expect(codes, (M, K // 2), torch.uint8, name, "codes")
+        _expect(scales, (M, K // g), torch.uint8, name, "scales")
+        if f == FP4_NVFP4:
+            if tensor_scale is None:
+                _expect(ts, (1,), torch.float32, name, "tensor scale")
+        elif ts is not None:
+            raise ValueError(f"{name}: MXFP4 has no tensor scale")
     if tensor_scale is not None:
         # a given s_t: a device float32 [1] that the call reads and leaves unchanged
         if tensor_scale.dtype != torch.float32 or not tensor_scale.is_cuda or tensor_scale.numel() != 1:
@@ -151,14 +167,30 @@ def fp4_linear(xq, xs, wq, ws, fmt="mxfp4", x_ts=None, w_ts=None, out_dtype=torc
     """Y = dq(Xq) dq(Wq)^T, [M, N] in float32 or bf16."""
     lib = load_library()
     f = _FMT[fmt]
+    for t in (xq, wq):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise ValueError("fp4_linear: Xq and Wq must be 2-D tensors of packed codes")
     M, N, K = xq.shape[0], wq.shape[0], 2 * xq.shape[1]
-    for t in (xq, xs, wq, ws):
-        if not t.is_cuda or t.dtype != torch.uint8 or not t.is_contiguous():
-            raise ValueError("fp4_linear: codes and scales must be contiguous uint8 CUDA tensors")
     if wq.shape[1] * 2 != K:
         raise ValueError("fp4_linear: X and W disagree on K")
+    g = group_size(f)
+    _expect(xq, (M, K // 2), torch.uint8, "fp4_linear", "Xq")
+    _expect(wq, (N, K // 2), torch.uint8, "fp4_linear", "Wq")
+    _expect(xs, (M, K // g), torch.uint8, "fp4_linear", "Xs")
+    _expect(ws, (N, K // g), torch.uint8, "fp4_linear", "Ws")
+    if f == FP4_NVFP4:
+        _expect(x_ts, (1,), torch.float32, "fp4_linear", "x_ts")
+        _expect(w_ts, (1,), torch.float32, "fp4_linear", "w_ts")
+    elif x_ts is not None or w_ts is not None:
+        raise ValueError("fp4_linear: MXFP4 has no tensor scales")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("fp4_linear: out_dtype must be torch.float32 or torch.bfloat16")
     ydt = {torch.float32: 0, torch.bfloat16: 1}[out_dtype]
-    y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    if out is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    else:
+        _expect(out, (M, N), out_dtype, "fp4_linear", "out")
+        y = out
     _check(lib.fp4_linear(_ptr(xq), _ptr(xs), _ptr(x_ts), _ptr(wq), _ptr(ws), _ptr(w_ts), M, N, K, f,
                           _ptr(y), ydt, _stream(xq.device)))
     return y
@@ -173,11 +205,18 @@ def fp4_rotate_quantize_linear(x: torch.Tensor, wq, ws, block: int, out_dtype=to
         if not t.is_cuda or t.dtype != torch.uint8 or not t.is_contiguous():
             raise ValueError("fp4_rotate_quantize_linear: weight codes and scales must be contiguous uint8 CUDA tensors")
     M, K = x.shape
-    N = wq.shape[0]
-    if wq.shape[1] * 2 != K:
+    if wq.dim() != 2 or wq.shape[1] * 2 != K:
         raise ValueError("fp4_rotate_quantize_linear: X and W disagree on K")
+    N = wq.shape[0]
+    _expect(ws, (N, K // 32), torch.uint8, "fp4_rotate_quantize_linear", "Ws")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("fp4_rotate_quantize_linear: out_dtype must be torch.float32 or torch.bfloat16")
     ydt = {torch.float32: 0, torch.bfloat16: 1}[out_dtype]
-    y = torch.empty((M, N), dtype=out_dtype, device=x.device) if out is None else out
+    if out is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    else:
+        _expect(out, (M, N), out_dtype, "fp4_rotate_quantize_linear", "out")
+        y = out
     _check(lib.fp4_rotate_quantize_linear(_ptr(x), M, K, x.stride(0), int(block), _ptr(wq), _ptr(ws), N, _ptr(y), ydt,
                                           _stream(x.device)))
     return y

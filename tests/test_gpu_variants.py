@@ -187,3 +187,45 @@ def test_nv_given_tensor_scale_stress_sampled():
     rows = np.unique(np.concatenate([[0, w.M - 1], np.random.default_rng(9).choice(w.M, 16, replace=False)]))
     assert_quant_parity(compare_quant(q, x, w.block, "nvfp4", rows=rows, tensor_scale=st), "nv given stress",
                         exact=True)
+
+
+def test_binding_refuses_mismatched_buffers():
+    # the kernels trust the sizes that the pointers imply; the binding refuses a mismatch before any launch
+    x = dev_bf16(WL.draw_normal_bf16((8, 256), 1.0, seed=2))
+    w = dev_bf16(WL.draw_normal_bf16((64, 256), 0.02, seed=3))
+    xq, xs, _ = B.fp4_rotate_quantize(x, 32, "mxfp4")
+    wq, ws, _ = B.fp4_quantize_weights(w, 32, "mxfp4")
+    bad_linear = [
+        dict(xs=xs[:, :4].contiguous()),                       # Xs too narrow
+        dict(ws=ws[:32].contiguous()),                         # Ws too short
+        dict(wq=wq[:, :64].contiguous()),                      # K disagrees
+        dict(out=torch.empty((8, 63), device="cuda")),         # Y too small
+        dict(out=torch.empty((8, 64), device="cuda", dtype=torch.bfloat16)),  # Y of the wrong dtype
+        dict(x_ts=torch.ones(1, device="cuda")),               # MXFP4 has no tensor scale
+        dict(xs=xs.cpu()),                                     # host memory
+    ]
+    for bad in bad_linear:
+        args = dict(xq=xq, xs=xs, wq=wq, ws=ws)
+        kw = {k: v for k, v in bad.items() if k not in args}
+        args.update({k: v for k, v in bad.items() if k in args})
+        with pytest.raises(ValueError):
+            B.fp4_linear(args["xq"], args["xs"], args["wq"], args["ws"], "mxfp4", **kw)
+    nq, ns, nts = B.fp4_rotate_quantize(x, 16, "nvfp4")
+    mq, ms, mts = B.fp4_quantize_weights(w, 16, "nvfp4")
+    with pytest.raises(ValueError):
+        B.fp4_linear(nq, ns, mq, ms, "nvfp4", x_ts=nts)                       # w_ts missing
+    with pytest.raises(ValueError):
+        B.fp4_linear(nq, ns, mq, ms[:, :8].contiguous(), "nvfp4", x_ts=nts, w_ts=mts)
+    with pytest.raises(ValueError):
+        B.fp4_rotate_quantize(x, 32, "mxfp4", out=(xq, xs[:, :7].contiguous(), None))
+    with pytest.raises(ValueError):
+        B.fp4_rotate_quantize(x, 32, "mxfp4", out=(xq[:4].contiguous(), xs, None))
+    with pytest.raises(ValueError):
+        B.fp4_rotate_quantize(x, 16, "nvfp4", out=(nq, ns, None))              # NVFP4 needs its scale word
+    with pytest.raises(ValueError):
+        B.fp4_rotate_quantize_linear(x, wq, ws[:, :4].contiguous(), 32)
+    with pytest.raises(ValueError):
+        B.fp4_rotate_quantize_linear(x, wq, ws, 32, out=torch.empty((8, 32), device="cuda"))
+    # the same buffers, well formed, still run and agree with the two-call path
+    y = B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=torch.empty((8, 64), device="cuda"))
+    assert torch.equal(y, B.fp4_linear(xq, xs, wq, ws, "mxfp4"))
