@@ -114,6 +114,8 @@ int fp4_linear(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const ui
     return fail(FP4_E_NULLPTR, "%s: NVFP4 needs both tensor scales", who);
   if (fmt == FP4_MXFP4 && (x_ts || w_ts))
     return fail(FP4_E_NULLPTR, "%s: tensor scales must be NULL for MXFP4", who);
+  if (fmt == FP4_NVFP4 && (!aligned(x_ts, 4) || !aligned(w_ts, 4)))
+    return fail(FP4_E_ALIGN, "%s: tensor scales must be 4-byte aligned", who);
   if (M < 1 || N < 1 || K < 128 || K % 128)
     return fail(FP4_E_SHAPE, "%s: need M, N >= 1 and K a positive multiple of 128 (M=%lld N=%lld K=%lld)", who,
                 (long long)M, (long long)N, (long long)K);

@@ -209,10 +209,11 @@ hipError_t launch_fused(const uint16_t* X, int64_t ldx, const uint8_t* Wq, const
   const int bi = B == 16 ? 0 : B == 32 ? 1 : B == 64 ? 2 : 3;
   const size_t lds = fused_lds_bytes(M, K) > (size_t)kDecWaves * 64 * 16 ? fused_lds_bytes(M, K)
                                                                          : (size_t)kDecWaves * 64 * 16;
-  if (dev >= 0 && dev < 64 && (g_fused_attr[bi][dev].load(std::memory_order_acquire) & (1 + out_bf16)) == 0) {
+  const bool cached = dev >= 0 && dev < 64;
+  if (!cached || (g_fused_attr[bi][dev].load(std::memory_order_acquire) & (1 + out_bf16)) == 0) {
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
-    g_fused_attr[bi][dev].fetch_or(1 + out_bf16, std::memory_order_acq_rel);
+    if (cached) g_fused_attr[bi][dev].fetch_or(1 + out_bf16, std::memory_order_acq_rel);
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)((N + 15) / 16)), dim3(kDecThreads), lds, st, X, ldx, Wq, Ws, Y, M, N, K);
   return hipGetLastError();

@@ -244,6 +244,8 @@ __global__ __launch_bounds__(NT) void gemm_mxfp4_ring(const uint8_t* __restrict_
   }
 }
 
+// per kernel instantiation and device: the dynamic-LDS limit has been raised
+template <bool B>
 std::atomic<int> g_attr_done[64];
 
 template <bool B>
@@ -253,10 +255,11 @@ hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   auto kern = gemm_mxfp4_ring<B>;
-  if (dev >= 0 && dev < 64 && !g_attr_done[dev].load(std::memory_order_acquire)) {
+  const bool cached = dev >= 0 && dev < 64;
+  if (!cached || !g_attr_done<B>[dev].load(std::memory_order_acquire)) {
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
-    g_attr_done[dev].store(1, std::memory_order_release);
+    if (cached) g_attr_done<B>[dev].store(1, std::memory_order_release);
   }
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int T = tiles_m * tiles_n;

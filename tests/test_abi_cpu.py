@@ -138,4 +138,6 @@ def test_linear_validation(lib):
     assert lin(lib, Xq=A16 + 4) == -5
     assert lin(lib, Xs=A16 + 2) == -5
     assert lin(lib, Y=A16 + 8) == -5
+    assert lin(lib, fmt=1, xts=A16 + 2, wts=A16) == -5   # tensor scales are float words
+    assert lin(lib, fmt=1, xts=A16, wts=A16 + 1) == -5
     assert b"fp4_linear" in lib.fp4_last_error()

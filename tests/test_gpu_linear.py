@@ -222,7 +222,7 @@ def test_decode_full(name):
     assert r <= GEMM_REL_FRO_TOL
 
 
-@pytest.mark.parametrize("name", ["prefill_mx", "prefill_nv", "large"])
+@pytest.mark.parametrize("name", ["prefill_mx", "prefill_mx_m4096", "prefill_nv", "large"])
 def test_full_size_sampled(name):
     w = WL.WORKLOADS[name]
     x, wt = WL.draw_x(w), WL.draw_w(w)
