@@ -344,11 +344,15 @@ def main():
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
+    # per-kernel breakdown from a separate pass: events inside the timed loop would add gaps to it
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
     rq_ms = sum(a.elapsed_time(b) for a, b in zip(ev["a"], ev["b"])) / args.steps
     gemm_ms = sum(b.elapsed_time(c) for b, c in zip(ev["b"], ev["c"])) / args.steps
     flops = 2.0 * wl.M * wl.N * wl.K
