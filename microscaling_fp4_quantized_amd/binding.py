@@ -89,6 +89,24 @@ def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+def _launch(dev, fn, *args):
+    """Call an entry point with the operands' device current (the library launches on the current
+    device) and that device's current stream as the last argument."""
+    for t in args:
+        if isinstance(t, torch.Tensor):
+            raise TypeError("pass data pointers, not tensors")
+    if dev.index is not None and torch.cuda.current_device() != dev.index:
+        with torch.cuda.device(dev):
+            return fn(*args, _stream(dev))
+    return fn(*args, _stream(dev))
+
+
+def _same_device(name, dev, *tensors):
+    for t in tensors:
+        if isinstance(t, torch.Tensor) and t.device != dev:
+            raise ValueError(f"{name}: every operand must be on {dev}, got one on {t.device}")
+
+
 def _check(status: int):
     if status != 0:
         raise Fp4Error(status, load_library().fp4_last_error().decode())
@@ -132,16 +150,17 @@ def _quantize(name: str, x: torch.Tensor, block: int, fmt, out=None, rule=None, 
         if tensor_scale.dtype != torch.float32 or not tensor_scale.is_cuda or tensor_scale.numel() != 1:
             raise ValueError(f"{name}: tensor_scale must be a float32 CUDA tensor of one element")
         ts = tensor_scale
+    _same_device(name, x.device, codes, scales, ts, signs, tensor_scale)
     if rule is None and signs is None and tensor_scale is None:
-        _check(getattr(lib, name)(_ptr(x), M, K, x.stride(0), int(block), f, _ptr(codes), _ptr(scales),
-                                  _ptr(ts), _stream(x.device)))
+        _check(_launch(x.device, getattr(lib, name), _ptr(x), M, K, x.stride(0), int(block), f, _ptr(codes),
+                       _ptr(scales), _ptr(ts)))
     else:
         if signs is not None and (signs.dtype != torch.int8 or not signs.is_cuda or signs.numel() != K
                                   or not signs.is_contiguous()):
             raise ValueError(f"{name}: signs must be a contiguous int8 CUDA tensor of K entries")
         r = SCALE_RULES[rule or "standard"] | (TENSOR_SCALE_IN if tensor_scale is not None else 0)
-        _check(getattr(lib, name + "_ex")(_ptr(x), M, K, x.stride(0), int(block), f, r, _ptr(signs), _ptr(codes),
-                                          _ptr(scales), _ptr(ts), _stream(x.device)))
+        _check(_launch(x.device, getattr(lib, name + "_ex"), _ptr(x), M, K, x.stride(0), int(block), f, r,
+                       _ptr(signs), _ptr(codes), _ptr(scales), _ptr(ts)))
     return codes, scales, ts
 
 
@@ -191,8 +210,9 @@ def fp4_linear(xq, xs, wq, ws, fmt="mxfp4", x_ts=None, w_ts=None, out_dtype=torc
     else:
         _expect(out, (M, N), out_dtype, "fp4_linear", "out")
         y = out
-    _check(lib.fp4_linear(_ptr(xq), _ptr(xs), _ptr(x_ts), _ptr(wq), _ptr(ws), _ptr(w_ts), M, N, K, f,
-                          _ptr(y), ydt, _stream(xq.device)))
+    _same_device("fp4_linear", xq.device, xs, wq, ws, x_ts, w_ts, y)
+    _check(_launch(xq.device, lib.fp4_linear, _ptr(xq), _ptr(xs), _ptr(x_ts), _ptr(wq), _ptr(ws), _ptr(w_ts), M, N,
+                   K, f, _ptr(y), ydt))
     return y
 
 
@@ -217,8 +237,9 @@ def fp4_rotate_quantize_linear(x: torch.Tensor, wq, ws, block: int, out_dtype=to
     else:
         _expect(out, (M, N), out_dtype, "fp4_rotate_quantize_linear", "out")
         y = out
-    _check(lib.fp4_rotate_quantize_linear(_ptr(x), M, K, x.stride(0), int(block), _ptr(wq), _ptr(ws), N, _ptr(y), ydt,
-                                          _stream(x.device)))
+    _same_device("fp4_rotate_quantize_linear", x.device, wq, ws, y)
+    _check(_launch(x.device, lib.fp4_rotate_quantize_linear, _ptr(x), M, K, x.stride(0), int(block), _ptr(wq),
+                   _ptr(ws), N, _ptr(y), ydt))
     return y
 
 
