@@ -40,7 +40,7 @@ What the method computes, step by step (the online path):
 6. multiply the dequantized operands: Y = dq(Xq) dq(Wq)^T ([BRIDGE-de] §2
    "GPU-Kernel-Unterstützung (QuTLASS)", 4-bit matmul).
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 R1  Blocks and groups are contiguous and aligned from k = 0; the Hadamard
     block b and the scale group g are independent (b in {16,32,64,128}).
