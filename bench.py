@@ -211,6 +211,34 @@ def extra_rows(B, WL, torch, dev):
         var[name] = {"us": ms * 1e3, "GB/s": nb / (ms * 1e-3) / 1e9, "frac_hbm": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         log(f"[bench] variant {name}: {ms * 1e3:.1f} us = {var[name]['GB/s']:.0f} GB/s")
     out["rotate_quantize_variants"] = {"workload": "16384x8192 bf16, block 32 (stress_nv32 input)", **var}
+    # the same input with the 128-element Hadamard block, both formats
+    b128 = {}
+    for fmt, key in (("mxfp4", "rotate_quant_mx_b128"), ("nvfp4", None)):
+        g = 32 if fmt == "mxfp4" else 16
+        oo = (torch.empty((sw.M, sw.K // 2), dtype=torch.uint8, device=dev),
+              torch.empty((sw.M, sw.K // g), dtype=torch.uint8, device=dev),
+              torch.empty((1,), dtype=torch.float32, device=dev) if fmt == "nvfp4" else None)
+
+        def call128(i, fmt=fmt, oo=oo):
+            B.fp4_rotate_quantize(bufs[i % 3], 128, fmt, out=oo)
+
+        for i in range(3):
+            call128(i)
+        ms = time_batch(call128, 21, torch)
+        nb = sw.M * sw.K * ((2 if fmt == "nvfp4" else 0) + 2 + 0.5 + 1.0 / g) + (8 if fmt == "nvfp4" else 0)
+        if fmt == "mxfp4":
+            tr = measured_traffic("rotate_quant_mx_b128", "rotate_quant.hip")
+        else:
+            t1 = measured_traffic("rotate_amax_b128", "rotate_quant.hip")
+            t2 = measured_traffic("rotate_quant_nv_b128", "rotate_quant.hip")
+            tr = None if t1 is None or t2 is None else t1 + t2
+        b128[fmt] = {"us": ms * 1e3, "GB/s": nb / (ms * 1e-3) / 1e9, "frac_hbm": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "algorithmic_bytes": nb, "traffic": tr}
+        log(f"[bench] block 128 {fmt} stress rotate+quantize {ms * 1e3:.1f} us = {b128[fmt]['GB/s']:.0f} GB/s "
+            f"({b128[fmt]['frac_hbm']:.1%} of HBM)")
+    out["rotate_quantize_block128"] = {
+        "workload": "stress_mx128 / stress_nv128: X 16384x8192 bf16 (the stress_nv32 input), block 128; NVFP4 "
+                    "counts its max pass as a second read of X", **b128}
     del bufs, o
     # NVFP4 prefill GEMM, M=2048 K=4096 N=14336, Y bf16
     wl = WL.WORKLOADS["prefill_nv"]
