@@ -98,11 +98,12 @@ enum {
  *               its low nibble, element 2j+1 in its high nibble. 16-byte aligned.
  *  scales       device, uint8 [M, K/g] row-major (E8M0 or E4M3FN codes).
  *               NVFP4: 2-byte aligned.
- *  tensor_scale NVFP4: device float[1]; receives s_t (the tensor-maximum pass
- *               accumulates it in place). MXFP4: must be NULL.
+ *  tensor_scale NVFP4: device float[1]; receives s_t. MXFP4: must be NULL.
  *  stream       hipStream_t or NULL.
- * MXFP4 is one kernel launch; NVFP4 is three (clear, tensor maximum, quantize),
- * all on `stream`.
+ * MXFP4 is one kernel launch; NVFP4 is three (the tensor-maximum pass, its
+ * reduction to s_t, and the quantize pass), all on `stream`. Between the first
+ * and the last of them the codes buffer holds intermediate per-workgroup maxima;
+ * the quantize pass overwrites them. No atomics are used, so s_t is deterministic.
  */
 FP4_API int fp4_rotate_quantize(const void *X, int64_t M, int64_t K, int64_t ldx, int block, int fmt,
                         uint8_t *codes, uint8_t *scales, float *tensor_scale, void *stream);

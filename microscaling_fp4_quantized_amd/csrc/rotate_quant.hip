@@ -139,21 +139,38 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_mx(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// NVFP4 pass 1: the tensor scale s_t = fl32(T / 2688), T = max |y| over the tensor,
-// accumulated with an integer atomic max on the float bits (non-negative floats order
-// like their bits). x -> fl32(x c) and x -> fl32(x / 2688) are monotone, so
-// max fl32(|z| c) = fl32(max|z| c) (the multiply is applied once per chunk) and the
-// maximum over workgroups of fl32(m / 2688) is fl32(T / 2688): the word ends holding s_t.
+// NVFP4 pass 1: the tensor scale s_t = fl32(T / 2688), T = max |y| over the tensor.
+// Each workgroup of the max pass writes the maximum of its chunks to its own float slot,
+// then one workgroup reduces the slots and writes s_t. No atomics: when every workgroup
+// finishes at once, same-address atomics serialise in L2. x -> fl32(x c) and
+// x -> fl32(x / 2688) are monotone, so max fl32(|z| c) = fl32(max|z| c) (the multiply is
+// applied once per chunk) and fl32(max / 2688) = fl32(T / 2688).
 // ---------------------------------------------------------------------------
-__global__ void clear_word(unsigned* p) {
-  if (threadIdx.x == 0) *p = 0u;
+constexpr unsigned kMaxPassGrid = 1024;  // 4 workgroups per CU on the 256-CU gfx950, grid-stride
+
+__global__ __launch_bounds__(kThreads) void amax_finish(const float* __restrict__ partial, int n,
+                                                        float* __restrict__ ts) {
+  float m = 0.f;
+  for (int i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, partial[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float wmax[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) b = fmaxf(b, wmax[w]);
+    ts[0] = (float)((double)b / 2688.0);  // fl32(T / 2688): 2688 = 2^7 * 21, so the fp64 step never
+                                          // lands on a float32 rounding midpoint
+  }
 }
 
 template <int B>
 __global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restrict__ X, int64_t ldx,
                                                         RowMap rm, uint32_t total, int load_mode,
                                                         const int8_t* __restrict__ signs,
-                                                        unsigned* __restrict__ amax_bits) {
+                                                        float* __restrict__ partial) {
   __shared__ __attribute__((aligned(16))) v4u stage[kThreads / 64][kStage];
   // Grid-stride over the chunks (the grid is capped at a few workgroups per CU), so each
   // workgroup pays the reduction and the atomic below once for many chunks.
@@ -172,10 +189,7 @@ __global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restri
       m = fmaxf(m, a * c);
     }
   }
-  // Wave reduction, then workgroup reduction through LDS, then at most one atomic per
-  // workgroup. Same-address atomics serialise in L2, so a workgroup whose maximum does not
-  // exceed the value already there skips its atomic (the word only ever grows, so a stale
-  // read can only cause an unneeded atomic, never a missed one).
+  // wave reduction, then workgroup reduction through LDS; one float per workgroup
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   __shared__ float wmax[kThreads / 64];
@@ -185,8 +199,7 @@ __global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restri
     float b = wmax[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) b = fmaxf(b, wmax[w]);
-    const unsigned bits = __float_as_uint((float)((double)b / 2688.0));  // fl32(m / 2688)
-    if (bits > __hip_atomic_load(amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(amax_bits, bits);
+    partial[blockIdx.x] = b;
   }
 }
 
@@ -307,10 +320,12 @@ hipError_t launch_b(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int fm
   constexpr int NV_RULE = RULE == kRuleFit ? kRuleFit : kRuleStandard;  // other rules are MXFP4 only
   unsigned* amax = reinterpret_cast<unsigned*>(ts);
   if (!given_ts) {  // otherwise the caller's s_t is already in the word
-    hipLaunchKernelGGL(clear_word, dim3(1), dim3(64), 0, st, amax);
-    const dim3 grid_max(grid.x < 2048u ? grid.x : 2048u);  // 8 workgroups per CU, grid-stride
-    // the max pass loads normally so that as much of X as fits stays cached for the second pass
-    hipLaunchKernelGGL(rotate_amax<B>, grid_max, block, 0, st, X, ldx, rm, total, load_mode & 1, signs, amax);
+    const dim3 grid_max(grid.x < kMaxPassGrid ? grid.x : kMaxPassGrid);
+    // The per-workgroup maxima live in the codes buffer until the quantize pass overwrites it:
+    // 4 bytes per workgroup against 16 bytes of codes per chunk, and grid_max <= chunks.
+    float* partial = reinterpret_cast<float*>(codes);
+    hipLaunchKernelGGL(rotate_amax<B>, grid_max, block, 0, st, X, ldx, rm, total, load_mode, signs, partial);
+    hipLaunchKernelGGL(amax_finish, dim3(1), block, 0, st, partial, (int)grid_max.x, ts);
   }
   hipLaunchKernelGGL((rotate_quant_nv<B, NV_RULE>), grid, block, 0, st, X, ldx, rm, total, load_mode, signs, amax,
                      codes, scales);
