@@ -1,7 +1,7 @@
 """The library's calls captured in a HIP graph (torch.cuda.graph) replay correctly.
 
-Every kernel the calls launch is an ordinary kernel (the NVFP4 tensor-maximum word is cleared
-by a one-thread kernel, not a memset), so a captured step can be replayed. Each graph is
+Every kernel the calls launch is an ordinary kernel and none of them uses a memset (the NVFP4
+tensor scale is written whole by its reduction kernel), so a captured step can be replayed. Each graph is
 replayed several times with eager work on the same buffers in between, and every replay is
 compared bit for bit with the eager result.
 """
