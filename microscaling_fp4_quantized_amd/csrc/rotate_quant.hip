@@ -150,8 +150,14 @@ constexpr unsigned kMaxPassGrid = 1024;  // 4 workgroups per CU on the 256-CU gf
 
 __global__ __launch_bounds__(kThreads) void amax_finish(const float* __restrict__ partial, int n,
                                                         float* __restrict__ ts) {
+  static_assert(kMaxPassGrid % kThreads == 0, "whole loads per thread");
+  // n <= kMaxPassGrid: every thread issues its (at most four) loads before using any of them
   float m = 0.f;
-  for (int i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, partial[i]);
+#pragma unroll
+  for (int j = 0; j < (int)(kMaxPassGrid / kThreads); ++j) {
+    const int i = (int)threadIdx.x + j * kThreads;
+    m = fmaxf(m, partial[i < n ? i : n - 1]);  // n >= 1; a repeated slot leaves the maximum unchanged
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   __shared__ float wmax[kThreads / 64];
