@@ -12,12 +12,13 @@
 // Work decomposition: one lane owns one 32-element chunk of a row (64 bytes of
 // bf16 in, 16 bytes of packed codes out). A wave reads its 4 KB of X with fully
 // coalesced 16-byte loads and redistributes them through LDS, so each lane owns a
-// contiguous chunk (per-lane 64-byte strided loads reached only ~55% of HBM peak). A Hadamard block of b <= 32 lives in
-// one lane's registers; b = 64 / 128 spans 2 / 4 adjacent lanes of a quad and
-// its last stages exchange values with DPP quad permutes. The transform follows
-// one fixed order (strides 1, 2, 4, ... then one multiply by fl32(1/sqrt(b)))
-// so its float32 result is unique. The whole path is HBM-bound: every byte of X
-// is read once, every code and scale byte written once.
+// contiguous chunk (per-lane 64-byte strided loads reached only ~55% of HBM peak).
+// A Hadamard block of b <= 32 lives in one lane's registers; b = 64 / 128 spans
+// 2 / 4 adjacent lanes of a quad and its last stages exchange values with DPP quad
+// permutes. The transform follows one fixed order (strides 1, 2, 4, ... then one
+// multiply by fl32(1/sqrt(b))) so its float32 result is unique. The path is
+// HBM-bound: MXFP4 reads X once, NVFP4 twice (the tensor maximum first), and every
+// code and scale byte is written once.
 #include "quant_device.hpp"
 
 namespace fp4 {
