@@ -1,0 +1,93 @@
+"""The largest inputs the quantizer accepts, checked on sampled rows against the oracle.
+
+fp4_rotate_quantize takes up to 2^31 - 1 chunks of 32 elements (rows * K / 32 must fit in
+31 bits). The first test runs an input just under that limit (X of 128 GiB, byte offsets far
+beyond 2^32) for MXFP4, and for NVFP4 with a given tensor scale. The second runs the NVFP4
+tensor-maximum pass over an 8 GiB input whose maximum is planted in a known row, so the
+sampled rows determine T exactly. Inputs come from torch's seeded generator on the device;
+only the sampled rows are copied to the host for the oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from microscaling_fp4_quantized_amd import binding as B
+from parity import assert_quant_parity, compare_quant, say
+
+pytestmark = pytest.mark.gpu
+
+GIB = 1 << 30
+
+
+def _free_bytes() -> int:
+    torch.cuda.empty_cache()
+    return torch.cuda.mem_get_info()[0]
+
+
+def _rows_bits(x: torch.Tensor, rows: np.ndarray) -> np.ndarray:
+    sel = x[torch.from_numpy(rows).to(x.device)]
+    return sel.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _rows_out(out, rows: np.ndarray):
+    idx = torch.from_numpy(rows).to(out[0].device)
+    return out[0][idx], out[1][idx], out[2]
+
+
+def test_max_chunk_count():
+    K = 8192
+    M = (2**31 - 1) // (K // 32)  # 8 388 607 rows: 2^31 - 256 chunks
+    need = M * K * 2 + M * K // 2 + M * K // 16 + 2 * GIB
+    if _free_bytes() < need:
+        pytest.skip(f"needs {need / GIB:.0f} GiB of free device memory")
+    say(f"case max chunk count: X {M}x{K} bf16 ({M * K * 2 / GIB:.0f} GiB), MXFP4 b32, then NVFP4 b32 given s_t")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20250531)
+    x = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    x.normal_(generator=gen)
+    rows = np.array([0, 1, 4097, M // 2, M - 2, M - 1])
+    xb = _rows_bits(x, rows)
+
+    out = B.fp4_rotate_quantize(x, 32, "mxfp4")
+    torch.cuda.synchronize()
+    got = _rows_out(out, rows)
+    del out
+    assert_quant_parity(compare_quant(got, xb, 32, "mxfp4"), "max chunk count mxfp4")
+
+    s_t = np.float32(14.0 / 2688.0)  # clips only |y| > 14, far beyond this N(0, 1) input
+    ts = torch.tensor([s_t], dtype=torch.float32, device="cuda")
+    out = B.fp4_rotate_quantize(x, 32, "nvfp4", tensor_scale=ts)
+    torch.cuda.synchronize()
+    got = _rows_out(out, rows)
+    del out, x
+    assert_quant_parity(compare_quant(got, xb, 32, "nvfp4", tensor_scale=s_t), "max chunk count nvfp4 given s_t")
+    torch.cuda.empty_cache()
+
+
+def test_nv_tensor_maximum_beyond_4gib():
+    K = 8192
+    M = 524288  # X of 8 GiB
+    need = M * K * 2 + M * K // 2 + M * K // 16 + GIB
+    if _free_bytes() < need:
+        pytest.skip(f"needs {need / GIB:.0f} GiB of free device memory")
+    say(f"case NVFP4 tensor maximum: X {M}x{K} bf16 ({M * K * 2 / GIB:.0f} GiB), b32, planted maximum")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    x = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    x.normal_(generator=gen)
+    r0, c0 = M - 3, 5000
+    # rotated, this value dominates its block (|y| ~ 1000 / sqrt(32) ~ 177 against ~7 elsewhere),
+    # so T over the sampled rows, which include r0, is T over the tensor
+    x[r0, c0] = 1000.0
+    rows = np.array([0, M // 3, r0, M - 1])
+    xb = _rows_bits(x, rows)
+    out = B.fp4_rotate_quantize(x, 32, "nvfp4")
+    torch.cuda.synchronize()
+    got = _rows_out(out, rows)
+    del out, x
+    res = compare_quant(got, xb, 32, "nvfp4")
+    assert_quant_parity(res, "nvfp4 tensor maximum beyond 4 GiB")
+    assert res["tensor_scale"] > 170.0 / 2688.0
+    torch.cuda.empty_cache()
