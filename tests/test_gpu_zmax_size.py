@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from microscaling_fp4_quantized_amd import binding as B
-from parity import assert_quant_parity, compare_quant, say
+from parity import GEMM_REL_FRO_TOL, assert_quant_parity, compare_quant, gemm_reference, rel_fro, say
 
 pytestmark = pytest.mark.gpu
 
@@ -90,4 +90,35 @@ def test_nv_tensor_maximum_beyond_4gib():
     res = compare_quant(got, xb, 32, "nvfp4")
     assert_quant_parity(res, "nvfp4 tensor maximum beyond 4 GiB")
     assert res["tensor_scale"] > 170.0 / 2688.0
+    torch.cuda.empty_cache()
+
+
+def test_gemm_operand_beyond_4gib():
+    # Xq of 131072 x 32768 bytes: the large-tile kernel's row offsets into it pass 2^32 bytes
+    M, K, N = 131072, 65536, 512
+    need = M * K * 2 + M * K // 2 + M * K // 32 + M * N * 4 + GIB
+    if _free_bytes() < need:
+        pytest.skip(f"needs {need / GIB:.0f} GiB of free device memory")
+    say(f"case GEMM operand beyond 4 GiB: M {M} K {K} N {N}, MXFP4 b32, Xq {M * K // 2 / GIB:.0f} GiB")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    x = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    x.normal_(generator=gen)
+    w = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    w.normal_(mean=0.0, std=0.02, generator=gen)
+    rows = np.array([0, 255, 256, M // 2 + 17, M - 1])
+    cols = np.array([0, 1, 255, 256, N - 1])
+    xb, wb = _rows_bits(x, rows), _rows_bits(w, cols)
+    xq, xs, _ = B.fp4_rotate_quantize(x, 32, "mxfp4")
+    del x
+    wq, ws, _ = B.fp4_quantize_weights(w, 32, "mxfp4")
+    y = B.fp4_linear(xq, xs, wq, ws, "mxfp4")
+    torch.cuda.synchronize()
+    got = y[torch.from_numpy(rows).to(y.device)][:, torch.from_numpy(cols).to(y.device)].cpu().numpy()
+    del xq, xs, wq, ws, y, w
+    ref = gemm_reference(xb, wb, 32, "mxfp4", np.arange(len(rows)), np.arange(len(cols)))
+    assert np.linalg.norm(ref) > 0 and np.count_nonzero(ref) == ref.size
+    r = rel_fro(got, ref)
+    say(f"GEMM beyond 4 GiB sampled rel fro {r:.3e} (|ref| {np.linalg.norm(ref):.3e})")
+    assert r <= GEMM_REL_FRO_TOL
     torch.cuda.empty_cache()
