@@ -1,4 +1,4 @@
-// Large-tile W4A4 MXFP4 GEMM for gfx950: Y = dq(Xq) dq(Wq)^T with 256x256 workgroup tiles.
+// Large-tile W4A4 MXFP4 GEMM for gfx950: Y = dq(Xq) dq(Wq)^T with 256-row workgroup tiles.
 //
 // "Bridging the Gap Between Promise and Performance for Microscaling FP4
 // Quantization" (gist.science, German edition), Technische Zusammenfassung §2
@@ -8,8 +8,8 @@
 //  * v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands runs at twice the rate of the
 //    16x16x128 form, so every product is a 32x32x64 scaled MFMA; lane l carries 32 K
 //    elements (one MXFP4 group) of row l % 32 and that group's E8M0 byte.
-//  * 8 waves (2 per SIMD) in a 2 x 4 layout, 128 x 64 outputs per wave (128 accumulators),
-//    so one wave's LDS reads overlap the other wave's MFMAs.
+//  * 8 waves (2 per SIMD). The 256x256 tile uses a 2 x 4 wave layout, 128 x 64 outputs per
+//    wave (128 accumulators), so one wave's LDS reads overlap the other wave's MFMAs.
 //  * K advances in stages of 256 elements (128 bytes per row). A 2-deep LDS ring is filled
 //    with global_load_lds_dwordx4 (LDS DMA, no register staging); 16-byte chunks of a row
 //    are XOR-swizzled so the 32 rows of a fragment read hit distinct banks.
@@ -17,10 +17,14 @@
 //    waited for its own DMA of the stage), so in-flight prefetches are not drained.
 //  * E8M0 scales are DMA'd 16 bytes per row (two stages) into their own double buffer,
 //    read once per two stages, and shifted per lane half so the MFMA op_sel picks the byte.
-//  * Output tiles go through LDS so Y is written as whole 256-byte row segments.
+//  * Output tiles go through LDS so Y is written as whole row segments.
 //  * Tile order: workgroup i runs on XCD i % 8; each XCD takes a contiguous range of tiles,
 //    walked M-fastest within groups of 8 tile rows, so tiles running together share
 //    A and B slices in that XCD's L2.
+//  * Two tile widths in one launch. When the 256x256 tiles would leave the last round of
+//    workgroups part-filled, the columns left after whole rounds of 256-wide tiles are
+//    covered by 256x192 tiles (4 x 2 waves of 64 x 96), each about 0.78 of a wide tile's
+//    time, so the last round is full of cheaper tiles.
 // Requires K % 512 == 0 (whole scale groups); other shapes use the general kernel.
 #include <atomic>
 
@@ -33,21 +37,34 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gbl_void;
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 256;        // workgroup tile
-constexpr int WGM = 2, WGN = 4;          // wave layout
-constexpr int WAVES = WGM * WGN, NT = WAVES * 64;
-constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+constexpr int BM = 256;                  // workgroup tile rows (both widths)
+constexpr int WAVES = 8, NT = WAVES * 64;
 constexpr int BKB = 128;                 // bytes of K per row per stage (256 elements)
 constexpr int KSTEPS = 4;                // 32x32x64 steps per stage
 constexpr int NS = 2;                    // ring depth
-constexpr int STAGE = (BM + BN) * BKB;   // 64 KB
-constexpr int A_WL = BM / 8 / WAVES, B_WL = BN / 8 / WAVES;  // 1 KB DMA wave-loads per wave
-constexpr int SC_BYTES = (BM + BN) * 16;                     // scales of 2 stages
-constexpr int SC_WL = (BM + BN) / 64 / WAVES;
-constexpr int LDS_BYTES = NS * STAGE + 2 * SC_BYTES;         // 144 KB
-static_assert(A_WL * 8 * WAVES == BM && B_WL * 8 * WAVES == BN, "row split");
-static_assert(SC_WL * 64 * WAVES == BM + BN, "scale split");
-static_assert(WN == 64, "epilogue assumes 64-column wave tiles");
+constexpr int LDS_BYTES = NS * (BM + 256) * BKB + 2 * (BM + 256) * 16;  // sized for the wide tile: 144 KB
+
+// One tile shape: BN columns, WGM x WGN waves.
+template <int BN_, int WGM_, int WGN_>
+struct Tile {
+  static constexpr int BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+  static constexpr int STAGE = (BM + BN) * BKB;
+  static constexpr int A_WL = BM / 8 / WAVES, B_WL = BN / 8 / WAVES;  // 1 KB DMA wave-loads per wave
+  static constexpr int SC_BYTES = (BM + BN) * 16;                      // scales of 2 stages
+  static constexpr int SC_LOADS = (BM + BN) / 64;                      // 64-row scale wave-loads
+  static constexpr int SC_WL = (SC_LOADS + WAVES - 1) / WAVES;
+  static constexpr int EP = WN * 4 + 16;                               // epilogue row pitch (bytes)
+  static_assert(WGM * WGN == WAVES, "wave layout");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "whole 32x32 fragments");
+  static_assert(A_WL * 8 * WAVES == BM && B_WL * 8 * WAVES == BN, "row split");
+  static_assert(SC_LOADS * 64 == BM + BN, "scale split");
+  static_assert(NS * STAGE + 2 * SC_BYTES <= LDS_BYTES, "ring fits");
+  static_assert(WAVES * 32 * EP <= LDS_BYTES, "epilogue staging fits");
+};
+using Wide = Tile<256, 2, 4>;
+using Narrow = Tile<192, 4, 2>;
+constexpr float kNarrowCost = 0.78f;  // measured time of a 256x192 tile over a 256x256 one
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -71,24 +88,16 @@ __device__ __forceinline__ v16f mfma32(v8i a, v8i b, v16f c, int sa, int sb) {
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(NT) void gemm_mxfp4_ring(const uint8_t* __restrict__ Xq, const uint8_t* __restrict__ Xs,
-                                                      const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Ws,
-                                                      void* __restrict__ Yv, int M, int N, int K, int tiles_m,
-                                                      int tiles_n, int xcd_remap) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+// One output tile [m0, m0 + 256) x [n0, n0 + C::BN) over all of K.
+template <bool OUT_BF16, class C>
+__device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restrict__ Xq,
+                                          const uint8_t* __restrict__ Xs, const uint8_t* __restrict__ Wq,
+                                          const uint8_t* __restrict__ Ws, void* __restrict__ Yv, int M, int N,
+                                          int K, int m0, int n0) {
+  constexpr int WGN = C::WGN, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
+  constexpr int STAGE = C::STAGE, A_WL = C::A_WL, B_WL = C::B_WL, SC_BYTES = C::SC_BYTES, SC_WL = C::SC_WL;
   uint8_t* scl = smem + NS * STAGE;
-
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int T = tiles_m * tiles_n;
-  int L = blockIdx.x;
-  if (xcd_remap) L = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
-  constexpr int GM = 8;
-  const int first_m = (L / (GM * tiles_n)) * GM;
-  const int gsize = min(tiles_m - first_m, GM);
-  const int tm = first_m + (L % gsize);
-  const int tn = (L % (GM * tiles_n)) / gsize;
-  const int m0 = tm * BM, n0 = tn * BN;
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
   const int KB = K / 2, KS = K / 32;
   const int nst = K / 256;  // even
@@ -109,7 +118,7 @@ __global__ __launch_bounds__(NT) void gemm_mxfp4_ring(const uint8_t* __restrict_
   }
 #pragma unroll
   for (int i = 0; i < SC_WL; ++i) {
-    const int rb = (wave * SC_WL + i) * 64;  // wave-uniform
+    const int rb = min(wave * SC_WL + i, C::SC_LOADS - 1) * 64;  // wave-uniform; waves past the last load skip
     const int r = rb + lane;
     srcS[i] = rb < BM ? Xs + (size_t)min(m0 + r, M - 1) * KS : Ws + (size_t)min(n0 + r - BM, N - 1) * KS;
   }
@@ -120,8 +129,9 @@ __global__ __launch_bounds__(NT) void gemm_mxfp4_ring(const uint8_t* __restrict_
       uint8_t* dst = scl + ((s >> 1) & 1) * SC_BYTES;
 #pragma unroll
       for (int i = 0; i < SC_WL; ++i)
-        __builtin_amdgcn_global_load_lds((gbl_void*)(srcS[i] + (s >> 1) * 16),
-                                         (lds_void*)(dst + (wave * SC_WL + i) * 1024), 16, 0, 0);
+        if (wave * SC_WL + i < C::SC_LOADS)
+          __builtin_amdgcn_global_load_lds((gbl_void*)(srcS[i] + (s >> 1) * 16),
+                                           (lds_void*)(dst + (wave * SC_WL + i) * 1024), 16, 0, 0);
     }
     uint8_t* buf = smem + (s & 1) * STAGE;
 #pragma unroll
@@ -194,10 +204,11 @@ __global__ __launch_bounds__(NT) void gemm_mxfp4_ring(const uint8_t* __restrict_
     }
   }
 
-  // Epilogue: each wave stages one 32 x 64 slab at a time in its own LDS region, then
-  // writes 4 whole rows (256 B fp32 / 128 B bf16 each) per wave instruction.
-  constexpr int EP = WN * 4 + 16;  // padded row pitch (bytes)
-  __syncthreads();                 // every wave is done with the ring
+  // Epilogue: each wave stages one 32 x WN slab at a time in its own LDS region, then writes
+  // whole 16-byte pieces of its rows (WN / 4 of them per row; 64 per wave instruction).
+  constexpr int EP = C::EP;
+  constexpr int CPR = WN / 4;
+  __syncthreads();  // every wave is done with the ring
   float* ep = reinterpret_cast<float*>(smem + wave * 32 * EP);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -209,13 +220,14 @@ __global__ __launch_bounds__(NT) void gemm_mxfp4_ring(const uint8_t* __restrict_
         ep[rr * (EP / 4) + j * 32 + fr] = acc[i][j][v];
       }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's slab is in LDS (wave-private region)
-    const int col = n0 + wn0 + (lane & 15) * 4;
     const bool vec = (N & 3) == 0;  // rows start 16-byte aligned (Y itself is)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int rr = (lane >> 4) + 4 * k;
-      const v4f val = *reinterpret_cast<const v4f*>(&ep[rr * (EP / 4) + (lane & 15) * 4]);
+    for (int k = 0; k < 32 * CPR / 64; ++k) {
+      const int cix = k * 64 + lane;
+      const int rr = cix / CPR, cc = cix % CPR;
+      const v4f val = *reinterpret_cast<const v4f*>(&ep[rr * (EP / 4) + cc * 4]);
       const int row = m0 + wm0 + i * 32 + rr;
+      const int col = n0 + wn0 + cc * 4;
       if (row >= M) continue;
       if constexpr (OUT_BF16) {
         __bf16* dst = reinterpret_cast<__bf16*>(Yv) + (size_t)row * N + col;
@@ -244,9 +256,68 @@ __global__ __launch_bounds__(NT) void gemm_mxfp4_ring(const uint8_t* __restrict_
   }
 }
 
+// Tile index L of a tiles_m x cnt grid -> (tm, tn): groups of 8 tile rows, M fastest.
+__device__ __forceinline__ void map_tile(int L, int tiles_m, int cnt, int& tm, int& tn) {
+  constexpr int GM = 8;
+  const int first_m = (L / (GM * cnt)) * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  tm = first_m + (L % gsize);
+  tn = (L % (GM * cnt)) / gsize;
+}
+
+// Workgroups [0, tiles_m * tn1) take 256-wide tiles of columns [0, 256 tn1); the rest take
+// 192-wide tiles of the columns from 256 tn1 on. Each range is spread over the XCDs when its
+// size is a multiple of 8.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(NT) void gemm_mxfp4_ring(const uint8_t* __restrict__ Xq, const uint8_t* __restrict__ Xs,
+                                                      const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Ws,
+                                                      void* __restrict__ Yv, int M, int N, int K, int tiles_m, int tn1,
+                                                      int tn2) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int T1 = tiles_m * tn1, T2 = tiles_m * tn2;
+  int b = blockIdx.x, tm, tn;
+  if (b < T1) {
+    const int L = (T1 % 8 == 0) ? (b & 7) * (T1 >> 3) + (b >> 3) : b;
+    map_tile(L, tiles_m, tn1, tm, tn);
+    ring_tile<OUT_BF16, Wide>(smem, Xq, Xs, Wq, Ws, Yv, M, N, K, tm * BM, tn * Wide::BN);
+  } else {
+    b -= T1;
+    const int L = (T1 % 8 == 0 && T2 % 8 == 0) ? (b & 7) * (T2 >> 3) + (b >> 3) : b;
+    map_tile(L, tiles_m, tn2, tm, tn);
+    ring_tile<OUT_BF16, Narrow>(smem, Xq, Xs, Wq, Ws, Yv, M, N, K, tm * BM, tn1 * Wide::BN + tn * Narrow::BN);
+  }
+}
+
+// Split of the columns into tn1 wide and tn2 narrow panels. The wide tiles come first in
+// dispatch order, so the split is only considered when they fill whole rounds of `cus`
+// workgroups: the narrow tiles then start together and the makespan, in wide-tile times, is
+// rounds(wide) + kNarrowCost * rounds(narrow). The uniform tiling is kept unless the split is
+// shorter.
+void plan_columns(int tiles_m, int N, int cus, int& tn1, int& tn2) {
+  const int w_all = (N + Wide::BN - 1) / Wide::BN;
+  tn1 = w_all;
+  tn2 = 0;
+  if (cus <= 0) return;
+  const long long T = (long long)tiles_m * w_all;
+  float best = (float)((T + cus - 1) / cus);
+  for (int a = 0; a < w_all; ++a) {
+    if (((long long)tiles_m * a) % cus != 0) continue;
+    const int rest = N - a * Wide::BN;
+    const int b = (rest + Narrow::BN - 1) / Narrow::BN;
+    const long long T2 = (long long)tiles_m * b;
+    const float t = (float)((long long)tiles_m * a / cus) + kNarrowCost * (float)((T2 + cus - 1) / cus);
+    if (t < best - 1e-3f) {
+      best = t;
+      tn1 = a;
+      tn2 = b;
+    }
+  }
+}
+
 // per kernel instantiation and device: the dynamic-LDS limit has been raised
 template <bool B>
 std::atomic<int> g_attr_done[64];
+std::atomic<int> g_cus[64];  // compute units per device, 0 until queried
 
 template <bool B>
 hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws, int M, int N, int K,
@@ -261,10 +332,17 @@ hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const
     if (e != hipSuccess) return e;
     if (cached) g_attr_done<B>[dev].store(1, std::memory_order_release);
   }
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int T = tiles_m * tiles_n;
-  hipLaunchKernelGGL(kern, dim3(T), dim3(NT), LDS_BYTES, st, Xq, Xs, Wq, Ws, Y, M, N, K, tiles_m, tiles_n,
-                     (T % 8 == 0) ? 1 : 0);
+  int cus = cached ? g_cus[dev].load(std::memory_order_acquire) : 0;
+  if (cus == 0) {
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (cached) g_cus[dev].store(cus, std::memory_order_release);
+  }
+  const int tiles_m = (M + BM - 1) / BM;
+  int tn1, tn2;
+  plan_columns(tiles_m, N, cus, tn1, tn2);
+  hipLaunchKernelGGL(kern, dim3(tiles_m * (tn1 + tn2)), dim3(NT), LDS_BYTES, st, Xq, Xs, Wq, Ws, Y, M, N, K, tiles_m,
+                     tn1, tn2);
   return hipGetLastError();
 }
 

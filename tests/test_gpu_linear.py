@@ -79,9 +79,12 @@ def test_decode_kernel_random_scales():
     assert r <= 1e-6
 
 
-@pytest.mark.parametrize("M,N,K", [(512, 512, 1024), (300, 520, 512), (256, 261, 512), (777, 1000, 1536)])
+@pytest.mark.parametrize("M,N,K", [(512, 512, 1024), (300, 520, 512), (256, 261, 512), (777, 1000, 1536),
+                                   (2048, 8192, 512), (2048, 12544, 512)])
 def test_large_tile_kernel_unit_scales_exact(M, N, K):
-    # shapes routed to the 256x256-tile kernel (K % 512 == 0, M, N >= 256), ragged edges included
+    # shapes routed to the large-tile kernel (K % 512 == 0, M, N >= 256), ragged edges included.
+    # On 256 CUs the column plan is: one round of 256x256 tiles for 2048 x 8192; 256x256 tiles
+    # then 256x192 tiles for 2048 x 12544; 256x192 tiles alone for the small shapes.
     rng = np.random.default_rng(M + N + K)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
@@ -96,7 +99,7 @@ def test_large_tile_kernel_unit_scales_exact(M, N, K):
     assert np.array_equal(host(yb.float()).astype(np.float64), O.bf16_rne_f64(ref))
 
 
-@pytest.mark.parametrize("M,N,K", [(512, 768, 2048), (259, 300, 512)])
+@pytest.mark.parametrize("M,N,K", [(512, 768, 2048), (259, 300, 512), (2048, 12544, 1024)])
 def test_large_tile_kernel_random_scales(M, N, K):
     rng = np.random.default_rng(7 * M + N)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
