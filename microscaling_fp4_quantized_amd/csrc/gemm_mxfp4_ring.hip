@@ -27,6 +27,7 @@
 //    time, so the last round is full of cheaper tiles.
 // Requires K % 512 == 0 (whole scale groups); other shapes use the general kernel.
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -123,9 +124,12 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
     srcS[i] = rb < BM ? Xs + (size_t)min(m0 + r, M - 1) * KS : Ws + (size_t)min(n0 + r - BM, N - 1) * KS;
   }
 
-  // stage s: its codes; even stages also bring the scales of stages s, s+1 (16 bytes per row)
-  auto issue_stage = [&](int s) {
-    if ((s & 1) == 0) {
+  // Part p (0..KSTEPS-1) of the DMA of stage s: its codes, wave-load i going with part
+  // i % KSTEPS, and on part 0 of an even stage the scales of stages s, s+1 (16 bytes per row).
+  // The parts are issued one per k-step of the stage before, so no wave stalls on a burst of
+  // nine loads while it could be issuing MFMAs.
+  auto issue_part = [&](int s, int p) {
+    if (p == 0 && (s & 1) == 0) {
       uint8_t* dst = scl + ((s >> 1) & 1) * SC_BYTES;
 #pragma unroll
       for (int i = 0; i < SC_WL; ++i)
@@ -136,12 +140,14 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
     uint8_t* buf = smem + (s & 1) * STAGE;
 #pragma unroll
     for (int i = 0; i < A_WL; ++i)
-      __builtin_amdgcn_global_load_lds((gbl_void*)(srcA[i] + s * BKB), (lds_void*)(buf + (wave * A_WL + i) * 1024), 16,
-                                       0, 0);
+      if (i % KSTEPS == p)
+        __builtin_amdgcn_global_load_lds((gbl_void*)(srcA[i] + s * BKB), (lds_void*)(buf + (wave * A_WL + i) * 1024),
+                                         16, 0, 0);
 #pragma unroll
     for (int i = 0; i < B_WL; ++i)
-      __builtin_amdgcn_global_load_lds((gbl_void*)(srcB[i] + s * BKB),
-                                       (lds_void*)(buf + BM * BKB + (wave * B_WL + i) * 1024), 16, 0, 0);
+      if (i % KSTEPS == p)
+        __builtin_amdgcn_global_load_lds((gbl_void*)(srcB[i] + s * BKB),
+                                         (lds_void*)(buf + BM * BKB + (wave * B_WL + i) * 1024), 16, 0, 0);
   };
 
   v16f acc[FM][FN];
@@ -156,12 +162,14 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
   const unsigned sh = 8u * (unsigned)fh;  // lane half h uses scale byte 2*ks + h
   v4u sg_a[FM], sg_b[FN];                 // scale dwords of the current two stages, lane-shifted
 
-  issue_stage(0);
-  for (int s = 0; s < nst; ++s) {
-    // stage s resident: with a 2-deep ring nothing is issued after it yet
+  // Stage s: wait for its DMA (this wave's, then everyone's at the barrier), then multiply it
+  // while the parts of stage s+1 refill the buffer of stage s-1, which every wave has finished
+  // reading once past the barrier. The last stage is peeled off so that the loop body issues
+  // its DMA unconditionally (a per-k-step condition makes the compiler wait on the DMA before
+  // every LDS read).
+  auto run_stage = [&](int s, auto with_dma) {
     wait_vmcnt<0>();
     ring_barrier();
-    if (s + 1 < nst) issue_stage(s + 1);  // refills the buffer of stage s-1 (all reads done)
     const uint8_t* buf = smem + (s & 1) * STAGE;
     const int sl = s & 1;
     if (sl == 0) {
@@ -173,6 +181,7 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
     }
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
+      if constexpr (decltype(with_dma)::value) issue_part(s + 1, ks);
       const int c = 2 * ks + fh;  // 16-byte chunk of the row = 32-element group
       // scale byte 2ks + h of the stage's 8 -> dword 2*sl + ks/2, byte 2*(ks&1) after the shift
       unsigned xa[FM], xb[FN];
@@ -202,7 +211,11 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
         }
       }
     }
-  }
+  };
+#pragma unroll
+  for (int p = 0; p < KSTEPS; ++p) issue_part(0, p);
+  for (int s = 0; s + 1 < nst; ++s) run_stage(s, std::true_type{});
+  run_stage(nst - 1, std::false_type{});
 
   // Epilogue: each wave stages one 32 x WN slab at a time in its own LDS region, then writes
   // whole 16-byte pieces of its rows (WN / 4 of them per row; 64 per wave instruction).
