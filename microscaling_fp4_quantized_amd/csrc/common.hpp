@@ -86,3 +86,28 @@ hipError_t fp4_launch_gemm_nvfp4_ring(const uint8_t* Xq, const uint8_t* Xs, cons
 hipError_t fp4_launch_gemm_nvfp4(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts,
                                  const uint8_t* Wq, const uint8_t* Ws, const float* w_ts, int64_t M,
                                  int64_t N, int64_t K, void* Y, int out_bf16, hipStream_t stream);
+
+// Column plan of the large-tile GEMMs: tn1 panels of 256 columns, then tn2 panels of 192.
+// The 256-wide tiles come first in dispatch order, so a split is only considered when they
+// fill whole rounds of `cus` workgroups (the narrow tiles then start together); its makespan,
+// in 256-wide tile times, is rounds(wide) + narrow_cost * rounds(narrow). The uniform 256-wide
+// tiling is kept unless a split is shorter.
+inline void fp4_plan_tile_columns(int tiles_m, int64_t N, int cus, float narrow_cost, int& tn1, int& tn2) {
+  const int w_all = (int)((N + 255) / 256);
+  tn1 = w_all;
+  tn2 = 0;
+  if (cus <= 0) return;
+  const long long T = (long long)tiles_m * w_all;
+  float best = (float)((T + cus - 1) / cus);
+  for (int a = 0; a < w_all; ++a) {
+    if (((long long)tiles_m * a) % cus != 0) continue;
+    const int b = (int)((N - 256LL * a + 191) / 192);
+    const long long T2 = (long long)tiles_m * b;
+    const float t = (float)((long long)tiles_m * a / cus) + narrow_cost * (float)((T2 + cus - 1) / cus);
+    if (t < best - 1e-3f) {
+      best = t;
+      tn1 = a;
+      tn2 = b;
+    }
+  }
+}

@@ -65,7 +65,7 @@ struct Tile {
 };
 using Wide = Tile<256, 2, 4>;
 using Narrow = Tile<192, 4, 2>;
-constexpr float kNarrowCost = 0.78f;  // measured time of a 256x192 tile over a 256x256 one
+constexpr float kNarrowCost = 0.78f;  // measured time of a 256x192 tile over a 256x256 one (MXFP4)
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -301,32 +301,6 @@ __global__ __launch_bounds__(NT) void gemm_mxfp4_ring(const uint8_t* __restrict_
   }
 }
 
-// Split of the columns into tn1 wide and tn2 narrow panels. The wide tiles come first in
-// dispatch order, so the split is only considered when they fill whole rounds of `cus`
-// workgroups: the narrow tiles then start together and the makespan, in wide-tile times, is
-// rounds(wide) + kNarrowCost * rounds(narrow). The uniform tiling is kept unless the split is
-// shorter.
-void plan_columns(int tiles_m, int N, int cus, int& tn1, int& tn2) {
-  const int w_all = (N + Wide::BN - 1) / Wide::BN;
-  tn1 = w_all;
-  tn2 = 0;
-  if (cus <= 0) return;
-  const long long T = (long long)tiles_m * w_all;
-  float best = (float)((T + cus - 1) / cus);
-  for (int a = 0; a < w_all; ++a) {
-    if (((long long)tiles_m * a) % cus != 0) continue;
-    const int rest = N - a * Wide::BN;
-    const int b = (rest + Narrow::BN - 1) / Narrow::BN;
-    const long long T2 = (long long)tiles_m * b;
-    const float t = (float)((long long)tiles_m * a / cus) + kNarrowCost * (float)((T2 + cus - 1) / cus);
-    if (t < best - 1e-3f) {
-      best = t;
-      tn1 = a;
-      tn2 = b;
-    }
-  }
-}
-
 // per kernel instantiation and device: the dynamic-LDS limit has been raised
 template <bool B>
 std::atomic<int> g_attr_done[64];
@@ -353,7 +327,7 @@ hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const
   }
   const int tiles_m = (M + BM - 1) / BM;
   int tn1, tn2;
-  plan_columns(tiles_m, N, cus, tn1, tn2);
+  fp4_plan_tile_columns(tiles_m, N, cus, kNarrowCost, tn1, tn2);
   hipLaunchKernelGGL(kern, dim3(tiles_m * (tn1 + tn2)), dim3(NT), LDS_BYTES, st, Xq, Xs, Wq, Ws, Y, M, N, K, tiles_m,
                      tn1, tn2);
   return hipGetLastError();

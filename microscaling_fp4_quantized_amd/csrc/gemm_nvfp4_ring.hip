@@ -1,4 +1,4 @@
-// Large-tile W4A4 NVFP4 GEMM for gfx950: Y = s_tx s_tw sum_k (e2m1 d_x)(e2m1 d_w), 256x256 tiles.
+// Large-tile W4A4 NVFP4 GEMM for gfx950: Y = s_tx s_tw sum_k (e2m1 d_x)(e2m1 d_w), 256-row tiles.
 //
 // "Bridging the Gap Between Promise and Performance for Microscaling FP4
 // Quantization" (gist.science, Spanish edition), Resumen técnico §2.B item 2
@@ -21,6 +21,9 @@
 //    store.
 //  * Workgroup i runs on XCD i % 8; each XCD takes a contiguous range of tiles, walked
 //    M-fastest within groups of 8 tile rows.
+//  * Two tile widths in one launch, as in the MXFP4 kernel: when 256x256 tiles would leave
+//    the last round part-filled, the columns after whole rounds of them are covered by
+//    256x192 tiles (4 x 2 waves of 64 x 96).
 #include <atomic>
 #include <type_traits>
 
@@ -31,18 +34,29 @@ namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 256;
-constexpr int WGM = 2, WGN = 4;
-constexpr int WAVES = WGM * WGN, NT = WAVES * 64;
-constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
-constexpr int BKE = 64;                   // K elements per stage
-constexpr int KSTEPS = BKE / 16;          // 32x32x16 steps per stage
-constexpr int PITCH = BKE * 2 + 16;       // bytes per bf16 row in LDS (padded)
-constexpr int STAGE = (BM + BN) * PITCH;  // 73728 bytes
-constexpr int LDS_BYTES = 2 * STAGE;      // 144 KB
-constexpr int CHUNKS = (BM + BN) * 2;     // 32-element chunks per stage
-constexpr int CPT = CHUNKS / NT;          // chunks per thread
-static_assert(CPT * NT == CHUNKS, "chunk split");
+constexpr int BM = 256;                       // tile rows (both widths)
+constexpr int WAVES = 8, NT = WAVES * 64;
+constexpr int BKE = 64;                       // K elements per stage
+constexpr int KSTEPS = BKE / 16;              // 32x32x16 steps per stage
+constexpr int PITCH = BKE * 2 + 16;           // bytes per bf16 row in LDS (padded)
+constexpr int LDS_BYTES = 2 * (BM + 256) * PITCH;  // sized for the wide tile: 144 KB
+
+// One tile shape: BN columns, WGM x WGN waves.
+template <int BN_, int WGM_, int WGN_>
+struct Tile {
+  static constexpr int BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+  static constexpr int STAGE = (BM + BN) * PITCH;
+  static constexpr int CHUNKS = (BM + BN) * 2;         // 32-element chunks per stage
+  static constexpr int CPT = (CHUNKS + NT - 1) / NT;   // chunks per thread (the last round may be partial)
+  static_assert(WGM * WGN == WAVES, "wave layout");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "whole 32x32 fragments");
+  static_assert(CHUNKS % 64 == 0, "whole waves per chunk round");
+  static_assert(2 * STAGE <= LDS_BYTES, "two stages fit");
+};
+using Wide = Tile<256, 2, 4>;
+using Narrow = Tile<192, 4, 2>;
+constexpr float kNvNarrowCost = 0.84f;  // measured time of a 256x192 tile over a 256x256 one
 
 // 32 E2M1 codes (16 bytes) with their two E4M3 group scales -> 32 exact bf16 (64 bytes).
 __device__ __forceinline__ void dequant32(const v4u codes, unsigned sc2, v4u out[4]) {
@@ -62,33 +76,28 @@ __device__ __forceinline__ void dequant32(const v4u codes, unsigned sc2, v4u out
   }
 }
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(NT) void gemm_nvfp4_ring(const uint8_t* __restrict__ Xq, const uint8_t* __restrict__ Xs,
-                                                      const float* __restrict__ x_ts, const uint8_t* __restrict__ Wq,
-                                                      const uint8_t* __restrict__ Ws, const float* __restrict__ w_ts,
-                                                      void* __restrict__ Yv, int M, int N, int K, int tiles_m,
-                                                      int tiles_n, int xcd_remap) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+// One output tile [m0, m0 + 256) x [n0, n0 + C::BN) over all of K.
+template <bool OUT_BF16, class C>
+__device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict__ Xq, const uint8_t* __restrict__ Xs,
+                                        const float* __restrict__ x_ts, const uint8_t* __restrict__ Wq,
+                                        const uint8_t* __restrict__ Ws, const float* __restrict__ w_ts,
+                                        void* __restrict__ Yv, int M, int N, int K, int m0, int n0) {
+  constexpr int WGN = C::WGN, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
+  constexpr int STAGE = C::STAGE, CHUNKS = C::CHUNKS, CPT = C::CPT;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int T = tiles_m * tiles_n;
-  int L = blockIdx.x;
-  if (xcd_remap) L = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
-  constexpr int GM = 8;
-  const int first_m = (L / (GM * tiles_n)) * GM;
-  const int gsize = min(tiles_m - first_m, GM);
-  const int m0 = (first_m + (L % gsize)) * BM;
-  const int n0 = ((L % (GM * tiles_n)) / gsize) * BN;
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
   const size_t KB = (size_t)K / 2, KS = (size_t)K / 16;
   const int nst = K / BKE;
 
-  // chunk c of a stage: tile row c / 2 (A rows first, then B rows), half c % 2 of the row's 64 elements
+  // chunk c of a stage: tile row c / 2 (A rows first, then B rows), half c % 2 of the row's 64
+  // elements. When CHUNKS is not a multiple of the thread count, the waves past the end of the
+  // last round (a whole number of waves) skip it; their clamped chunk keeps every address valid.
   const uint8_t* csrc[CPT];
   const uint8_t* ssrc[CPT];
   int ldst[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int c = tid + i * NT, r = c >> 1, h = c & 1;
+    const int c = min(tid + i * NT, CHUNKS - 1), r = c >> 1, h = c & 1;
     const bool isA = r < BM;
     const size_t row = isA ? (size_t)min(m0 + r, M - 1) : (size_t)min(n0 + r - BM, N - 1);
     csrc[i] = (isA ? Xq : Wq) + row * KB + h * 16;
@@ -103,6 +112,7 @@ __global__ __launch_bounds__(NT) void gemm_nvfp4_ring(const uint8_t* __restrict_
   auto gload = [&](auto P, int s) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
+      if ((i + 1) * NT > CHUNKS && wave * 64 + i * NT >= CHUNKS) continue;  // wave-uniform
       cr[P][i] = *reinterpret_cast<const v4u*>(csrc[i] + (size_t)s * (BKE / 2));
       sr[P][i] = *reinterpret_cast<const uint16_t*>(ssrc[i] + (size_t)s * (BKE / 16));
     }
@@ -110,6 +120,7 @@ __global__ __launch_bounds__(NT) void gemm_nvfp4_ring(const uint8_t* __restrict_
   auto lstore = [&](auto P) {  // dequantize register set P into LDS buffer P
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
+      if ((i + 1) * NT > CHUNKS && wave * 64 + i * NT >= CHUNKS) continue;  // wave-uniform
       v4u o[4];
       dequant32(cr[P][i], sr[P][i], o);
       v4u* dst = reinterpret_cast<v4u*>(smem + P * STAGE + ldst[i]);
@@ -204,9 +215,43 @@ __global__ __launch_bounds__(NT) void gemm_nvfp4_ring(const uint8_t* __restrict_
   }
 }
 
+// Tile index L of a tiles_m x cnt grid -> (tm, tn): groups of 8 tile rows, M fastest.
+__device__ __forceinline__ void map_tile(int L, int tiles_m, int cnt, int& tm, int& tn) {
+  constexpr int GM = 8;
+  const int first_m = (L / (GM * cnt)) * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  tm = first_m + (L % gsize);
+  tn = (L % (GM * cnt)) / gsize;
+}
+
+// Workgroups [0, tiles_m * tn1) take 256-wide tiles of columns [0, 256 tn1); the rest take
+// 192-wide tiles of the columns from 256 tn1 on. Each range is spread over the XCDs when its
+// size is a multiple of 8.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(NT) void gemm_nvfp4_ring(const uint8_t* __restrict__ Xq, const uint8_t* __restrict__ Xs,
+                                                      const float* __restrict__ x_ts, const uint8_t* __restrict__ Wq,
+                                                      const uint8_t* __restrict__ Ws, const float* __restrict__ w_ts,
+                                                      void* __restrict__ Yv, int M, int N, int K, int tiles_m, int tn1,
+                                                      int tn2) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int T1 = tiles_m * tn1, T2 = tiles_m * tn2;
+  int b = blockIdx.x, tm, tn;
+  if (b < T1) {
+    const int L = (T1 % 8 == 0) ? (b & 7) * (T1 >> 3) + (b >> 3) : b;
+    map_tile(L, tiles_m, tn1, tm, tn);
+    nv_tile<OUT_BF16, Wide>(smem, Xq, Xs, x_ts, Wq, Ws, w_ts, Yv, M, N, K, tm * BM, tn * Wide::BN);
+  } else {
+    b -= T1;
+    const int L = (T1 % 8 == 0 && T2 % 8 == 0) ? (b & 7) * (T2 >> 3) + (b >> 3) : b;
+    map_tile(L, tiles_m, tn2, tm, tn);
+    nv_tile<OUT_BF16, Narrow>(smem, Xq, Xs, x_ts, Wq, Ws, w_ts, Yv, M, N, K, tm * BM, tn1 * Wide::BN + tn * Narrow::BN);
+  }
+}
+
 // per kernel instantiation and device: the dynamic-LDS limit has been raised
 template <bool B>
 std::atomic<int> g_attr_done[64];
+std::atomic<int> g_cus[64];  // compute units per device, 0 until queried
 
 template <bool B>
 hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const uint8_t* Wq, const uint8_t* Ws,
@@ -221,10 +266,17 @@ hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const
     if (e != hipSuccess) return e;
     if (cached) g_attr_done<B>[dev].store(1, std::memory_order_release);
   }
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int T = tiles_m * tiles_n;
-  hipLaunchKernelGGL(kern, dim3(T), dim3(NT), LDS_BYTES, st, Xq, Xs, x_ts, Wq, Ws, w_ts, Y, M, N, K, tiles_m,
-                     tiles_n, (T % 8 == 0) ? 1 : 0);
+  int cus = cached ? g_cus[dev].load(std::memory_order_acquire) : 0;
+  if (cus == 0) {
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (cached) g_cus[dev].store(cus, std::memory_order_release);
+  }
+  const int tiles_m = (M + BM - 1) / BM;
+  int tn1, tn2;
+  fp4_plan_tile_columns(tiles_m, N, cus, kNvNarrowCost, tn1, tn2);
+  hipLaunchKernelGGL(kern, dim3(tiles_m * (tn1 + tn2)), dim3(NT), LDS_BYTES, st, Xq, Xs, x_ts, Wq, Ws, w_ts, Y, M, N,
+                     K, tiles_m, tn1, tn2);
   return hipGetLastError();
 }
 

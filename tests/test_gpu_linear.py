@@ -132,10 +132,13 @@ def dev_f32(v):
     return torch.tensor([v], dtype=torch.float32).cuda()
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (512, 768, 1024), (300, 520, 384), (777, 1000, 1536)])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (512, 768, 1024), (300, 520, 384), (777, 1000, 1536),
+                                   (2048, 8192, 256), (2048, 12544, 256)])
 def test_nv_large_tile_kernel_unit_scales_exact(M, N, K):
-    # NVFP4 shapes routed to the 256x256-tile kernel (M, N >= 256): group scales 1.0 (E4M3 code
-    # 0x38) and tensor scales 1.0 make every product a multiple of 1/4 and every sum exact
+    # NVFP4 shapes routed to the large-tile kernel (M, N >= 256): group scales 1.0 (E4M3 code
+    # 0x38) and tensor scales 1.0 make every product a multiple of 1/4 and every sum exact.
+    # Column plans on 256 CUs: one round of 256x256 tiles for 2048 x 8192, 256x256 then 256x192
+    # tiles for 2048 x 12544, 256x192 tiles alone for the small shapes.
     rng = np.random.default_rng(5 * M + N + K)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
