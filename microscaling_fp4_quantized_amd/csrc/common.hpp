@@ -99,8 +99,15 @@ inline void fp4_plan_tile_columns(int tiles_m, int64_t N, int cus, float narrow_
   if (cus <= 0) return;
   const long long T = (long long)tiles_m * w_all;
   float best = (float)((T + cus - 1) / cus);
-  for (int a = 0; a < w_all; ++a) {
-    if (((long long)tiles_m * a) % cus != 0) continue;
+  // tiles_m * a is a multiple of cus exactly when a is a multiple of cus / gcd(tiles_m, cus)
+  int g = cus, rem = tiles_m % cus;
+  while (rem != 0) {
+    const int r = g % rem;
+    g = rem;
+    rem = r;
+  }
+  const int step = cus / g;
+  for (int a = 0; a < w_all; a += step) {
     const int b = (int)((N - 256LL * a + 191) / 192);
     const long long T2 = (long long)tiles_m * b;
     const float t = (float)((long long)tiles_m * a / cus) + narrow_cost * (float)((T2 + cus - 1) / cus);
