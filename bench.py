@@ -161,7 +161,8 @@ def cpu_baseline(wl, x_bits, w_bits):
 def extra_rows(B, WL, torch, dev):
     """The other rows of the path, each timed over back-to-back launches on the library's stream:
     NVFP4 rotate+quantize on the bandwidth-stress shape (two passes over X), the NVFP4 prefill
-    GEMM (bf16 MFMA after exact dequantization), and the decode-shaped MXFP4 GEMM (HBM-bound on W)."""
+    GEMM (bf16 MFMA after exact dequantization), the large MXFP4 GEMM, and the decode-shaped MXFP4
+    GEMM (HBM-bound on W)."""
     out = {}
     # NVFP4 rotate+quantize, 16384 x 8192, block 32
     sw = WL.WORKLOADS["stress_nv32"]
@@ -255,6 +256,21 @@ def extra_rows(B, WL, torch, dev):
                          "frac_fp4_mfma_peak": tf / MFMA_FP4_PEAK_TFLOPS,
                          "traffic": measured_traffic("gemm_nvfp4_ring", "gemm_nvfp4_ring.hip")}
     log(f"[bench] NVFP4 GEMM {ms * 1e3:.1f} us = {tf:.0f} TFLOP/s")
+    del xq, xs, wq, ws, y
+    # the large MXFP4 configuration: M=8192 K=8192 N=28672, block 128, Y fp32 (whole rounds of tiles)
+    wl = WL.WORKLOADS["large"]
+    xq, xs, _ = B.fp4_rotate_quantize(bf16_dev(WL.draw_x(wl), dev), wl.block, "mxfp4")
+    wq, ws, _ = B.fp4_quantize_weights(bf16_dev(WL.draw_w(wl), dev), wl.block, "mxfp4")
+    y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y)
+    ms = time_batch(lambda i: B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y), 10, torch)
+    tf = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
+    out["gemm_mxfp4_large"] = {"workload": "large: M=8192 K=8192 N=28672, block 128, Y fp32",
+                               "us": ms * 1e3, "TFLOP/s": tf, "frac_fp4_mfma_peak": tf / MFMA_FP4_PEAK_TFLOPS,
+                               "algorithmic_bytes": (wl.M + wl.N) * wl.K * (0.5 + 1.0 / 32) + wl.M * wl.N * 4,
+                               "traffic": measured_traffic("gemm_mxfp4_ring_large", "gemm_mxfp4_ring.hip")}
+    log(f"[bench] large MXFP4 GEMM {ms * 1e3:.1f} us = {tf:.0f} TFLOP/s ({tf / MFMA_FP4_PEAK_TFLOPS:.1%} of peak)")
     del xq, xs, wq, ws, y
     # decode-shaped MXFP4 GEMM: W 4096x4096 streamed once per call
     for name in ("decode1", "decode16"):
