@@ -262,7 +262,7 @@ def extra_rows(B, WL, torch, dev):
     xq, xs, _ = B.fp4_rotate_quantize(bf16_dev(WL.draw_x(wl), dev), wl.block, "mxfp4")
     wq, ws, _ = B.fp4_quantize_weights(bf16_dev(WL.draw_w(wl), dev), wl.block, "mxfp4")
     y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
-    for _ in range(3):
+    for _ in range(20):  # about 20 ms of this kernel first, so that it is timed at its own steady clocks
         B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y)
     ms = time_batch(lambda i: B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y), 10, torch)
     tf = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
