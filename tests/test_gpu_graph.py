@@ -36,8 +36,10 @@ def _capture(fn):
     return g
 
 
+# 2048 x 12544 plans 256x256 then 256x192 tiles in one launch (on 256 CUs), for both formats
 @pytest.mark.parametrize("fmt,block,M,N,K", [("mxfp4", 32, 512, 768, 1024), ("nvfp4", 16, 300, 520, 512),
-                                             ("mxfp4", 128, 4, 4096, 4096)])
+                                             ("mxfp4", 128, 4, 4096, 4096), ("mxfp4", 32, 2048, 12544, 512),
+                                             ("nvfp4", 16, 2048, 12544, 512)])
 def test_step_graph_replays_match_eager(fmt, block, M, N, K):
     x = dev_bf16(WL.draw_normal_bf16((M, K), 1.0, seed=M))
     x2 = dev_bf16(WL.draw_normal_bf16((M, K), 2.0, seed=M + 1))
