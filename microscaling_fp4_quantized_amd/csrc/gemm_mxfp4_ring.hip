@@ -11,8 +11,11 @@
 //  * 8 waves (2 per SIMD). The 256x256 tile uses a 2 x 4 wave layout, 128 x 64 outputs per
 //    wave (128 accumulators), so one wave's LDS reads overlap the other wave's MFMAs.
 //  * K advances in stages of 256 elements (128 bytes per row). A 2-deep LDS ring is filled
-//    with global_load_lds_dwordx4 (LDS DMA, no register staging); 16-byte chunks of a row
-//    are XOR-swizzled so the 32 rows of a fragment read hit distinct banks.
+//    with buffer_load_dwordx4 ... lds (LDS DMA, no register staging); 16-byte chunks of a row
+//    are XOR-swizzled so the 32 rows of a fragment read hit distinct banks. The buffer form,
+//    not global_load_lds: the compiler counts a pending FLAT-encoded DMA as a possible LDS
+//    access and so waits for every LDS read (lgkmcnt(0)) before each MFMA group while one is
+//    in flight; with the buffer form it waits only for the fragments the MFMAs use.
 //  * The workgroup barrier of the ring waits for LDS reads only (each wave has already
 //    waited for its own DMA of the stage), so in-flight prefetches are not drained.
 //  * E8M0 scales are DMA'd 16 bytes per row (two stages) into their own double buffer,
@@ -25,7 +28,8 @@
 //    workgroups part-filled, the columns left after whole rounds of 256-wide tiles are
 //    covered by 256x192 tiles (4 x 2 waves of 64 x 96), each about 0.78 of a wide tile's
 //    time, so the last round is full of cheaper tiles.
-// Requires K % 512 == 0 (whole scale groups); other shapes use the general kernel.
+// Requires K % 512 == 0 (whole scale groups) and K < 2^25 (32-bit buffer offsets); other
+// shapes use the general kernel.
 #include <atomic>
 #include <type_traits>
 
@@ -35,7 +39,6 @@ namespace fp4 {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void gbl_void;
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256;                  // workgroup tile rows (both widths)
@@ -87,6 +90,13 @@ __device__ __forceinline__ v16f mfma32(v8i a, v8i b, v16f c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, SEL, sa, SEL, sb);
 }
 
+// Raw buffer resource over [base, base + bytes): stride 0, last word 0x00020000 (32-bit data
+// format in the gfx9-family descriptor layout, which untyped loads need). Offsets at or past
+// `bytes` read as zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const uint8_t* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // One output tile [m0, m0 + 256) x [n0, n0 + C::BN) over all of K.
@@ -103,25 +113,32 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
   const int KB = K / 2, KS = K / 32;
   const int nst = K / 256;  // even
 
-  // per-lane DMA sources: 8 rows x 128 bytes per wave-load; rows past M / N repeat the last row
-  const uint8_t* srcA[A_WL];
-  const uint8_t* srcB[B_WL];
-  const uint8_t* srcS[SC_WL];
+  // DMA sources: 8 rows x 128 bytes per wave-load; rows past M / N repeat the last row. The
+  // loads take the buffer form: a wave-uniform resource at the tile's first row of each operand
+  // (its range the rows the tile may touch) and a 32-bit per-lane offset, which stays below
+  // 256 * K / 2 < 2^32 since the kernel requires K < 2^25.
+  const int rows_a = min(M - m0, BM), rows_b = min(N - n0, C::BN);
+  const __amdgpu_buffer_rsrc_t rsA = buffer_rsrc(Xq + (size_t)m0 * KB, (unsigned)rows_a * KB);
+  const __amdgpu_buffer_rsrc_t rsB = buffer_rsrc(Wq + (size_t)n0 * KB, (unsigned)rows_b * KB);
+  unsigned offA[A_WL], offB[B_WL], offS[SC_WL];
 #pragma unroll
   for (int i = 0; i < A_WL; ++i) {
     const int r = (wave * A_WL + i) * 8 + (lane >> 3), q = lane & 7;
-    srcA[i] = Xq + (size_t)min(m0 + r, M - 1) * KB + ((q ^ swz(r)) << 4);
+    offA[i] = (unsigned)min(r, rows_a - 1) * KB + ((q ^ swz(r)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < B_WL; ++i) {
     const int r = (wave * B_WL + i) * 8 + (lane >> 3), q = lane & 7;
-    srcB[i] = Wq + (size_t)min(n0 + r, N - 1) * KB + ((q ^ swz(r)) << 4);
+    offB[i] = (unsigned)min(r, rows_b - 1) * KB + ((q ^ swz(r)) << 4);
   }
+  // scale rows: loads below BM / 64 are X's rows, the rest W's (wave-uniform per load)
+  const __amdgpu_buffer_rsrc_t rsXs = buffer_rsrc(Xs + (size_t)m0 * KS, (unsigned)rows_a * KS);
+  const __amdgpu_buffer_rsrc_t rsWs = buffer_rsrc(Ws + (size_t)n0 * KS, (unsigned)rows_b * KS);
 #pragma unroll
   for (int i = 0; i < SC_WL; ++i) {
     const int rb = min(wave * SC_WL + i, C::SC_LOADS - 1) * 64;  // wave-uniform; waves past the last load skip
     const int r = rb + lane;
-    srcS[i] = rb < BM ? Xs + (size_t)min(m0 + r, M - 1) * KS : Ws + (size_t)min(n0 + r - BM, N - 1) * KS;
+    offS[i] = rb < BM ? (unsigned)min(r, rows_a - 1) * KS : (unsigned)min(r - BM, rows_b - 1) * KS;
   }
 
   // Part p (0..KSTEPS-1) of the DMA of stage s: its codes, wave-load i going with part
@@ -134,20 +151,21 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
 #pragma unroll
       for (int i = 0; i < SC_WL; ++i)
         if (wave * SC_WL + i < C::SC_LOADS)
-          __builtin_amdgcn_global_load_lds((gbl_void*)(srcS[i] + (s >> 1) * 16),
-                                           (lds_void*)(dst + (wave * SC_WL + i) * 1024), 16, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds((wave * SC_WL + i) * 64 < BM ? rsXs : rsWs,
+                                                   (lds_void*)(dst + (wave * SC_WL + i) * 1024), 16,
+                                                   offS[i] + (unsigned)(s >> 1) * 16, 0, 0, 0);
     }
     uint8_t* buf = smem + (s & 1) * STAGE;
 #pragma unroll
     for (int i = 0; i < A_WL; ++i)
       if (i % KSTEPS == p)
-        __builtin_amdgcn_global_load_lds((gbl_void*)(srcA[i] + s * BKB), (lds_void*)(buf + (wave * A_WL + i) * 1024),
-                                         16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(buf + (wave * A_WL + i) * 1024), 16,
+                                                 offA[i] + (unsigned)s * BKB, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < B_WL; ++i)
       if (i % KSTEPS == p)
-        __builtin_amdgcn_global_load_lds((gbl_void*)(srcB[i] + s * BKB),
-                                         (lds_void*)(buf + BM * BKB + (wave * B_WL + i) * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void*)(buf + BM * BKB + (wave * B_WL + i) * 1024), 16,
+                                                 offB[i] + (unsigned)s * BKB, 0, 0, 0);
   };
 
   v16f acc[FM][FN];
@@ -337,7 +355,7 @@ hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const
 }  // namespace fp4
 
 bool fp4_gemm_mxfp4_ring_fits(int64_t M, int64_t N, int64_t K) {
-  return K % 512 == 0 && M >= 256 && N >= 256;
+  return K % 512 == 0 && K < ((int64_t)1 << 25) && M >= 256 && N >= 256;
 }
 
 hipError_t fp4_launch_gemm_mxfp4_ring(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
