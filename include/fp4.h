@@ -172,8 +172,11 @@ FP4_API int fp4_quantize_weights_ex(const void *W, int64_t N, int64_t K, int64_t
  *  MXFP4: dq = e2m1(code) * 2^(scale - 127); runs on gfx950 scaled MFMA with
  *         the E8M0 scales consumed by the instruction.
  *  NVFP4: dq = e2m1(code) * e4m3(scale) * s_t; the E4M3 group scale is folded
- *         into an exact bf16 operand in the kernel prologue (E4M3 scales have no
- *         native MFMA form on gfx950), x_ts * w_ts is applied in the epilogue.
+ *         into an exact 16-bit operand in the kernel prologue (fp16 in the
+ *         256-row-tile kernel used when M, N >= 256, bf16 in the general one; E4M3
+ *         scales have no native MFMA form on gfx950), x_ts * w_ts is applied in the
+ *         epilogue. Scale codes are the finite non-negative E4M3FN codes
+ *         0x00..0x7E that the quantizers write; other codes are outside the contract.
  *
  *  Xq  device uint8 [M, K/2], Xs device uint8 [M, K/g]  (fp4_rotate_quantize output)
  *  Wq  device uint8 [N, K/2], Ws device uint8 [N, K/g]  (fp4_quantize_weights output)

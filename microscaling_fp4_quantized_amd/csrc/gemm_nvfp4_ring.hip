@@ -6,15 +6,16 @@
 //
 // The gfx950 scaled MFMA accepts power-of-two scales per 32 K elements only, so the
 // NVFP4 group scale (E4M3, 16 elements) is folded into the operand instead: e2m1 * d
-// has at most 6 significant bits and lies in [2^-10, 2688], so it is exact in bf16, and
-// the product runs on v_mfma_f32_32x32x16_bf16 with float32 accumulation. The two
-// tensor scales multiply the result in the epilogue.
+// has at most 6 significant bits and lies in [2^-10, 2688], so it is exact in fp16, and
+// the product runs on v_mfma_f32_32x32x16_f16 with float32 accumulation. The two
+// tensor scales multiply the result in the epilogue. fp16 rather than bf16 (the products
+// are exact in both): one packed convert and one packed multiply make two operands.
 //
 // Design for CDNA4:
 //  * 8 waves (2 x 4), 128 x 64 outputs per wave as 4 x 2 fragments of 32 x 32.
 //  * K advances 64 per stage. The codes (16 bytes = 32 elements + their two scale bytes
 //    per thread and chunk) are loaded into registers two stages ahead; after stage s is
-//    multiplied, stage s+1 is dequantized once per workgroup into a bf16 tile in the
+//    multiplied, stage s+1 is dequantized once per workgroup into an fp16 tile in the
 //    other LDS buffer (pitch 144 bytes: the fragment reads hit distinct banks).
 //  * W is the row operand and X the column operand of every MFMA, so each lane ends with
 //    four consecutive output features of one token and stores them with one 8- or 16-byte
@@ -38,7 +39,7 @@ constexpr int BM = 256;                       // tile rows (both widths)
 constexpr int WAVES = 8, NT = WAVES * 64;
 constexpr int BKE = 64;                       // K elements per stage
 constexpr int KSTEPS = BKE / 16;              // 32x32x16 steps per stage
-constexpr int PITCH = BKE * 2 + 16;           // bytes per bf16 row in LDS (padded)
+constexpr int PITCH = BKE * 2 + 16;           // bytes per fp16 row in LDS (padded)
 constexpr int LDS_BYTES = 2 * (BM + 256) * PITCH;  // sized for the wide tile: 144 KB
 
 // One tile shape: BN columns, WGM x WGN waves.
@@ -58,21 +59,26 @@ using Wide = Tile<256, 2, 4>;
 using Narrow = Tile<192, 4, 2>;
 constexpr float kNvNarrowCost = 0.84f;  // measured time of a 256x192 tile over a 256x256 one
 
-// 32 E2M1 codes (16 bytes) with their two E4M3 group scales -> 32 exact bf16 (64 bytes).
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// 32 E2M1 codes (16 bytes) with their two E4M3 group scales (low byte first) -> 32 exact fp16
+// (64 bytes). The E4M3 code's seven magnitude bits, shifted left by 7, are the fp16 bit
+// pattern of d * 2^-8 (the E4M3 exponent bias is 7, fp16's is 15; E4M3 subnormals land on
+// fp16 subnormals, exactly), and the sign goes to bit 15. The packed convert's power-of-two
+// scale 256 restores the factor: (e2m1 * 256) * (d * 2^-8) = e2m1 * d, exact in fp16.
 __device__ __forceinline__ void dequant32(const v4u codes, unsigned sc2, v4u out[4]) {
-  const float d0 = e4m3_value(sc2 & 0xFFu), d1 = e4m3_value((sc2 >> 8) & 0xFFu);
+  const unsigned lo = ((sc2 & 0x7Fu) << 7) | ((sc2 & 0x80u) << 8);
+  const unsigned hi = ((sc2 & 0x7F00u) >> 1) | (sc2 & 0x8000u);
+  const h2 dd0 = __builtin_bit_cast(h2, lo | (lo << 16)), dd1 = __builtin_bit_cast(h2, hi | (hi << 16));
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const float d = w < 2 ? d0 : d1;
-    const v2f f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[w], 1.0f, 0);
-    const v2f f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[w], 1.0f, 1);
-    const v2f f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[w], 1.0f, 2);
-    const v2f f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[w], 1.0f, 3);
-    // the products are exact, so their bf16 is the top half of the float32
-    out[w][0] = __builtin_amdgcn_perm(__float_as_uint(f0[1] * d), __float_as_uint(f0[0] * d), 0x07060302u);
-    out[w][1] = __builtin_amdgcn_perm(__float_as_uint(f1[1] * d), __float_as_uint(f1[0] * d), 0x07060302u);
-    out[w][2] = __builtin_amdgcn_perm(__float_as_uint(f2[1] * d), __float_as_uint(f2[0] * d), 0x07060302u);
-    out[w][3] = __builtin_amdgcn_perm(__float_as_uint(f3[1] * d), __float_as_uint(f3[0] * d), 0x07060302u);
+    const h2 dd = w < 2 ? dd0 : dd1;  // words 0-1 are the first 16 elements (group 2c), 2-3 the second
+    // byte q of the word holds elements 2q (low nibble) and 2q+1
+    out[w][0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[w], 256.0f, 0) * dd);
+    out[w][1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[w], 256.0f, 1) * dd);
+    out[w][2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[w], 256.0f, 2) * dd);
+    out[w][3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[w], 256.0f, 3) * dd);
   }
 }
 
@@ -95,26 +101,30 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
   const uint8_t* csrc[CPT];
   const uint8_t* ssrc[CPT];
   int ldst[CPT];
+  unsigned shs[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = min(tid + i * NT, CHUNKS - 1), r = c >> 1, h = c & 1;
     const bool isA = r < BM;
     const size_t row = isA ? (size_t)min(m0 + r, M - 1) : (size_t)min(n0 + r - BM, N - 1);
     csrc[i] = (isA ? Xq : Wq) + row * KB + h * 16;
-    ssrc[i] = (isA ? Xs : Ws) + row * KS + h * 2;
+    ssrc[i] = (isA ? Xs : Ws) + row * KS;  // the row's 4 scale bytes of a stage; this chunk's are 2h, 2h+1
     ldst[i] = r * PITCH + h * 64;
+    shs[i] = 16 * h;
   }
   // two stages of codes in registers: stage s+2 is requested while stage s is multiplied
   v4u cr[2][CPT];
   unsigned sr[2][CPT];
   // register set P holds the stages with parity P (the stage count is even, so the loop below
   // is unrolled by two and every index into the register arrays is a constant)
+  // The loads are unconditional (a skipped chunk loads its clamped, valid address) and the
+  // scales come as whole dwords: a load under a branch, or a 16-bit load the compiler re-masks
+  // where the two register sets meet, makes it wait for loads issued just before.
   auto gload = [&](auto P, int s) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      if ((i + 1) * NT > CHUNKS && wave * 64 + i * NT >= CHUNKS) continue;  // wave-uniform
       cr[P][i] = *reinterpret_cast<const v4u*>(csrc[i] + (size_t)s * (BKE / 2));
-      sr[P][i] = *reinterpret_cast<const uint16_t*>(ssrc[i] + (size_t)s * (BKE / 16));
+      sr[P][i] = *reinterpret_cast<const unsigned*>(ssrc[i] + (size_t)s * (BKE / 16));
     }
   };
   auto lstore = [&](auto P) {  // dequantize register set P into LDS buffer P
@@ -122,7 +132,7 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
     for (int i = 0; i < CPT; ++i) {
       if ((i + 1) * NT > CHUNKS && wave * 64 + i * NT >= CHUNKS) continue;  // wave-uniform
       v4u o[4];
-      dequant32(cr[P][i], sr[P][i], o);
+      dequant32(cr[P][i], sr[P][i] >> shs[i], o);
       v4u* dst = reinterpret_cast<v4u*>(smem + P * STAGE + ldst[i]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) dst[q] = o[q];
@@ -149,18 +159,18 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
     for (int ks = 0; ks < KSTEPS; ++ks) {
       // lane l: row l % 32 of the fragment, K elements 16 ks + 8 (l / 32) .. + 7
       const int off = ks * 32 + fh * 16;
-      v8bf a[FM], b[FN];
+      v8h a[FM], b[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        a[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(buf + (wm0 + i * 32 + fr) * PITCH + off));
+        a[i] = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(buf + (wm0 + i * 32 + fr) * PITCH + off));
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        b[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(buf + (BM + wn0 + j * 32 + fr) * PITCH + off));
+        b[j] = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(buf + (BM + wn0 + j * 32 + fr) * PITCH + off));
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);  // D[n][m]
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[j], a[i], acc[i][j], 0, 0, 0);  // D[n][m]
     }
     lstore(std::integral_constant<int, 1 - P>{});
     __syncthreads();
