@@ -1,11 +1,12 @@
-"""The largest inputs the quantizer accepts, checked on sampled rows against the oracle.
+"""The largest inputs the quantizer and the GEMM accept, checked on sampled rows against the oracle.
 
 fp4_rotate_quantize takes up to 2^31 - 1 chunks of 32 elements (rows * K / 32 must fit in
 31 bits). The first test runs an input just under that limit (X of 128 GiB, byte offsets far
 beyond 2^32) for MXFP4, and for NVFP4 with a given tensor scale. The second runs the NVFP4
 tensor-maximum pass over an 8 GiB input whose maximum is planted in a known row, so the
-sampled rows determine T exactly. Inputs come from torch's seeded generator on the device;
-only the sampled rows are copied to the host for the oracle.
+sampled rows determine T exactly. The GEMM tests take an operand beyond 4 GiB, and K at the
+large-tile kernel's 32-bit offset limit and one step past it. Inputs come from torch's seeded
+generator on the device; only the sampled rows are copied to the host for the oracle.
 """
 from __future__ import annotations
 
@@ -122,3 +123,37 @@ def test_gemm_operand_beyond_4gib():
     say(f"GEMM beyond 4 GiB sampled rel fro {r:.3e} (|ref| {np.linalg.norm(ref):.3e})")
     assert r <= GEMM_REL_FRO_TOL
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("K", [2**25 - 512, 2**25])
+def test_gemm_k_at_the_offset_limit(K):
+    # The large-tile MXFP4 kernel addresses a tile's operand rows from the tile's first row with
+    # 32-bit offsets, so it takes K < 2^25 (256 rows x K/2 bytes < 2^32). K = 2^25 - 512 is the
+    # largest K it runs, with offsets just below 4 GiB; K = 2^25 goes to the general kernel.
+    M = N = 256
+    need = 2 * M * K * 2 + 2 * (M * K // 2 + M * K // 32) + M * N * 4 + 2 * GIB
+    if _free_bytes() < need:
+        pytest.skip(f"needs {need / GIB:.0f} GiB of free device memory")
+    say(f"case GEMM K at the 32-bit offset limit: M {M} N {N} K {K}, MXFP4 b32")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(K % 1000 + 5)
+    x = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    x.normal_(generator=gen)
+    w = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    w.normal_(mean=0.0, std=0.02, generator=gen)
+    rows, cols = np.array([0, M - 1]), np.array([3, N - 2])
+    xb, wb = _rows_bits(x, rows), _rows_bits(w, cols)
+    xq, xs, _ = B.fp4_rotate_quantize(x, 32, "mxfp4")
+    del x
+    wq, ws, _ = B.fp4_quantize_weights(w, 32, "mxfp4")
+    del w
+    y = B.fp4_linear(xq, xs, wq, ws, "mxfp4")
+    torch.cuda.synchronize()
+    got = y[torch.from_numpy(rows).to(y.device)][:, torch.from_numpy(cols).to(y.device)].cpu().numpy()
+    del xq, xs, wq, ws, y
+    torch.cuda.empty_cache()
+    ref = gemm_reference(xb, wb, 32, "mxfp4", np.arange(len(rows)), np.arange(len(cols)))
+    assert np.count_nonzero(ref) == ref.size
+    r = rel_fro(got, ref)
+    say(f"GEMM K={K} sampled rel fro {r:.3e}")
+    assert r <= GEMM_REL_FRO_TOL
