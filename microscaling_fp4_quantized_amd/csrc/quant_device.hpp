@@ -41,6 +41,47 @@ __device__ __forceinline__ void fwht(float v[32]) {
   }
 }
 
+// max_i |y_i| over this lane's 32 outputs of fwht<B> (before the 1/sqrt(B) factor), exactly,
+// with the last butterfly stage folded into the maximum: for the two outputs of a pair,
+// max(|fl(a + b)|, |fl(a - b)|) = fl(|a| + |b|), since {|a + b|, |a - b|} = {|a| + |b|,
+// ||a| - |b||} and rounding to nearest is monotonic and symmetric in sign. Only the magnitudes
+// are kept, so the cross-lane last stage (B >= 64) needs no per-lane sign flip. `v` is
+// overwritten.
+template <int B>
+__device__ __forceinline__ float fwht_absmax(float v[32]) {
+  constexpr int IN_LANE = B < 32 ? B : 32;
+  // every in-lane stage but the last when B <= 32 (that one is folded below)
+  constexpr int IN_LANE_FULL = B <= 32 ? IN_LANE / 2 : IN_LANE;
+#pragma unroll
+  for (int h = 1; h < IN_LANE_FULL; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (!(i & h)) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+  float m = 0.f;
+  if constexpr (B <= 32) {
+    constexpr int h = IN_LANE / 2;  // the last stage, in lane
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if (!(i & h)) m = fmaxf(m, fabsf(v[i]) + fabsf(v[i + h]));
+  } else if constexpr (B == 64) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(quad_xor<1>(v[i])) + fabsf(v[i]));
+  } else {
+    const unsigned flip = (threadIdx.x & 1) ? 0x80000000u : 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = quad_xor<1>(v[i]) + __uint_as_float(__float_as_uint(v[i]) ^ flip);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(quad_xor<2>(v[i])) + fabsf(v[i]));
+  }
+  return m;
+}
+
 // Eight float32 values -> one dword of eight E2M1 codes (element 2j in the low
 // nibble of byte j), dividing by 2^(exponent field of `scale` - 127) exactly and
 // rounding to nearest, ties to even, saturating at 6, keeping the sign.

@@ -189,11 +189,7 @@ __global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restri
     load_chunk(X, ldx, gc, total, rm, load_mode, stage[threadIdx.x >> 6], v);
     if (gc < total) {
       if (signs) apply_signs(v, signs, gc, rm);
-      fwht<B>(v);
-      float a = 0.f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
-      m = fmaxf(m, a * c);
+      m = fmaxf(m, fwht_absmax<B>(v) * c);
     }
   }
   // wave reduction, then workgroup reduction through LDS; one float per workgroup
