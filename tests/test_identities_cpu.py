@@ -1,0 +1,61 @@
+"""Arithmetic identities the HIP kernels rely on, checked in IEEE arithmetic on the CPU.
+
+- The max pass of NVFP4 rotate+quantize folds the butterfly's last stage into the
+  maximum: max(|fl(a + b)|, |fl(a - b)|) == fl(|a| + |b|) in float32 (round to nearest
+  is monotonic and symmetric in sign).
+- The large-tile NVFP4 GEMM decodes an E4M3 scale by shifting its seven magnitude bits
+  left by 7, which is the fp16 bit pattern of d * 2^-8 (sign to bit 15), and the packed
+  fp4 -> fp16 convert scales the E2M1 value by 256, so (e2m1 * 256) * (d * 2^-8) ==
+  e2m1 * d exactly in fp16 for every code pair.
+
+E4M3 and E2M1 values are written out here from the formats' definitions (OCP E4M3FN:
+bias 7, 3 mantissa bits, subnormals k * 2^-9; E2M1: {0, 0.5, 1, 1.5, 2, 3, 4, 6}).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def e4m3_value(code: int) -> float:
+    e, m = (code >> 3) & 15, code & 7
+    mag = m * 2.0**-9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+    return -mag if code & 0x80 else mag
+
+
+def test_folded_last_butterfly_stage_float32():
+    rng = np.random.default_rng(12)
+    n = 1 << 21
+    # magnitudes from subnormal to near overflow, mixed signs, plus exact cancellations
+    a = (rng.standard_normal(n) * np.exp2(rng.integers(-140, 120, n))).astype(np.float32)
+    b = (rng.standard_normal(n) * np.exp2(rng.integers(-140, 120, n))).astype(np.float32)
+    b[: n // 8] = -a[: n // 8]
+    b[n // 8: n // 4] = a[n // 8: n // 4]
+    b[n // 4: n // 4 + 1000] = np.float32(0.0)
+    a[n // 4 + 1000: n // 4 + 2000] = np.float32(-0.0)
+    with np.errstate(over="ignore"):
+        lhs = np.maximum(np.abs(a + b), np.abs(a - b))
+        rhs = np.abs(a) + np.abs(b)
+    assert lhs.dtype == np.float32 and rhs.dtype == np.float32
+    assert np.array_equal(lhs, rhs)
+
+
+def test_e4m3_fp16_bit_shift_decode():
+    for code in range(0x7F):  # the finite non-negative codes
+        bits = ((code & 0x7F) << 7) | ((code & 0x80) << 8)
+        half = np.array([bits], dtype=np.uint16).view(np.float16)[0]
+        assert float(half) == e4m3_value(code) * 2.0**-8, code
+
+
+def test_fp16_dequant_product_is_exact():
+    for code in range(0x7F):
+        d = e4m3_value(code)
+        dh = np.float16(d * 2.0**-8)
+        assert float(dh) == d * 2.0**-8
+        for i, x in enumerate(E2M1):
+            for sgn in (1.0, -1.0):
+                xs = np.float16(sgn * x * 256.0)  # the convert's output, exact
+                prod = xs * dh  # one fp16 multiply, round to nearest even
+                assert prod.dtype == np.float16
+                assert float(prod) == sgn * x * d, (code, i, sgn)
