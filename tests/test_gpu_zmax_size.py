@@ -4,8 +4,8 @@ fp4_rotate_quantize takes up to 2^31 - 1 chunks of 32 elements (rows * K / 32 mu
 31 bits). The first test runs an input just under that limit (X of 128 GiB, byte offsets far
 beyond 2^32) for MXFP4, and for NVFP4 with a given tensor scale. The second runs the NVFP4
 tensor-maximum pass over an 8 GiB input whose maximum is planted in a known row, so the
-sampled rows determine T exactly. The GEMM tests take an operand beyond 4 GiB, and K at the
-large-tile kernel's 32-bit offset limit and one step past it. Inputs come from torch's seeded
+sampled rows determine T exactly. The GEMM tests take an operand beyond 4 GiB (MXFP4 and
+NVFP4), and K at the large-tile MXFP4 kernel's 32-bit offset limit and one step past it. Inputs come from torch's seeded
 generator on the device; only the sampled rows are copied to the host for the oracle.
 """
 from __future__ import annotations
@@ -15,6 +15,7 @@ import pytest
 import torch
 
 from microscaling_fp4_quantized_amd import binding as B
+from oracle import fp4_oracle as O
 from parity import GEMM_REL_FRO_TOL, assert_quant_parity, compare_quant, gemm_reference, rel_fro, say
 
 pytestmark = pytest.mark.gpu
@@ -156,4 +157,47 @@ def test_gemm_k_at_the_offset_limit(K):
     assert np.count_nonzero(ref) == ref.size
     r = rel_fro(got, ref)
     say(f"GEMM K={K} sampled rel fro {r:.3e}")
+    assert r <= GEMM_REL_FRO_TOL
+
+
+def test_nv_gemm_operand_beyond_4gib():
+    # NVFP4: Xq of 131072 x 32768 bytes; the large-tile kernel's row offsets pass 2^32 bytes.
+    # A dominant value is planted in a sampled row of X and of W (as in the tensor-maximum test
+    # above), so the oracle's T over the sampled rows is T over each whole tensor.
+    M, K, N = 131072, 65536, 512
+    need = M * K * 2 + M * K // 2 + M * K // 16 + M * N * 4 + GIB
+    if _free_bytes() < need:
+        pytest.skip(f"needs {need / GIB:.0f} GiB of free device memory")
+    say(f"case NVFP4 GEMM operand beyond 4 GiB: M {M} K {K} N {N}, b16, Xq {M * K // 2 / GIB:.0f} GiB")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(13)
+    x = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    x.normal_(generator=gen)
+    w = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    w.normal_(mean=0.0, std=0.02, generator=gen)
+    rows = np.array([0, 255, 256, M // 2 + 17, M - 1])
+    cols = np.array([0, 1, 255, 256, N - 1])
+    # rotated by H16 / 4 these give |y| = 250 and 5, against about 7 and 0.15 elsewhere
+    x[int(rows[3]), 40000] = 1000.0
+    w[int(cols[2]), 123] = 20.0
+    xb, wb = _rows_bits(x, rows), _rows_bits(w, cols)
+    xq, xs, xts = B.fp4_rotate_quantize(x, 16, "nvfp4")
+    del x
+    wq, ws, wts = B.fp4_quantize_weights(w, 16, "nvfp4")
+    del w
+    y = B.fp4_linear(xq, xs, wq, ws, "nvfp4", x_ts=xts, w_ts=wts)
+    torch.cuda.synchronize()
+    got = y[torch.from_numpy(rows).to(y.device)][:, torch.from_numpy(cols).to(y.device)].cpu().numpy()
+    s_x, s_w = np.float32(xts.cpu()[0]), np.float32(wts.cpu()[0])
+    del xq, xs, wq, ws, y
+    torch.cuda.empty_cache()
+    ref = gemm_reference(xb, wb, 16, "nvfp4", np.arange(len(rows)), np.arange(len(cols)))
+    # the tensor scales: the oracle's, over the sampled rows, equal the GPU's bit for bit
+    _, _, ox = O.rotate_quantize(xb, 16, "nvfp4")
+    _, _, ow = O.rotate_quantize(wb, 16, "nvfp4")
+    assert np.float32(ox).view(np.uint32) == s_x.view(np.uint32), (ox, s_x)
+    assert np.float32(ow).view(np.uint32) == s_w.view(np.uint32), (ow, s_w)
+    assert np.count_nonzero(ref) == ref.size
+    r = rel_fro(got, ref)
+    say(f"NVFP4 GEMM beyond 4 GiB sampled rel fro {r:.3e} (|ref| {np.linalg.norm(ref):.3e}), s_x {s_x:.6e} s_w {s_w:.6e}")
     assert r <= GEMM_REL_FRO_TOL
