@@ -39,10 +39,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# headers every kernel source includes: a change in them changes the kernels too
+SHARED_HEADERS = ("common.hpp", "quant_device.hpp")
+
+
 def source_sha(name: str) -> str:
-    p = os.path.join(ROOT, "microscaling_fp4_quantized_amd", "csrc", name)
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source and the shared headers it is compiled with."""
+    h = hashlib.sha256()
+    for n in (name,) + SHARED_HEADERS:
+        with open(os.path.join(ROOT, "microscaling_fp4_quantized_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel_key: str, source: str, launches_per_unit: float = 1.0):
