@@ -80,11 +80,13 @@ def test_decode_kernel_random_scales():
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 512, 1024), (300, 520, 512), (256, 261, 512), (777, 1000, 1536),
-                                   (2048, 8192, 512), (2048, 12544, 512)])
+                                   (2048, 8192, 512), (2048, 12544, 512), (4000, 14272, 512)])
 def test_large_tile_kernel_unit_scales_exact(M, N, K):
     # shapes routed to the large-tile kernel (K % 512 == 0, M, N >= 256), ragged edges included.
     # On 256 CUs the column plan is: one round of 256x256 tiles for 2048 x 8192; 256x256 tiles
-    # then 256x192 tiles for 2048 x 12544; 256x192 tiles alone for the small shapes.
+    # then 256x192 tiles for 2048 x 12544; 256x192 tiles alone for the small shapes; for
+    # 4000 x 14272, 32 panels of 256 then 32 of 192 (the last one 128 columns wide) over 16 row
+    # tiles, the last one 160 rows.
     rng = np.random.default_rng(M + N + K)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
@@ -133,12 +135,13 @@ def dev_f32(v):
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 128), (512, 768, 1024), (300, 520, 384), (777, 1000, 1536),
-                                   (2048, 8192, 256), (2048, 12544, 256)])
+                                   (2048, 8192, 256), (2048, 12544, 256), (4000, 14272, 256)])
 def test_nv_large_tile_kernel_unit_scales_exact(M, N, K):
     # NVFP4 shapes routed to the large-tile kernel (M, N >= 256): group scales 1.0 (E4M3 code
     # 0x38) and tensor scales 1.0 make every product a multiple of 1/4 and every sum exact.
     # Column plans on 256 CUs: one round of 256x256 tiles for 2048 x 8192, 256x256 then 256x192
-    # tiles for 2048 x 12544, 256x192 tiles alone for the small shapes.
+    # tiles for 2048 x 12544 and for 4000 x 14272 (ragged in both: a last row tile of 160 rows,
+    # a last 192-wide panel of 128 columns), 256x192 tiles alone for the small shapes.
     rng = np.random.default_rng(5 * M + N + K)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
