@@ -236,11 +236,15 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
   run_stage(nst - 1, std::false_type{});
 
   // Epilogue: each wave stages one 32 x WN slab at a time in its own LDS region, then writes
-  // whole 16-byte pieces of its rows (WN / 4 of them per row; 64 per wave instruction).
+  // whole 16-byte pieces of its rows, 64 per wave instruction: 4 float32 values per piece, or
+  // 8 bf16 values (read back as two 16-byte halves of float32, rounded to nearest even).
   constexpr int EP = C::EP;
-  constexpr int CPR = WN / 4;
+  constexpr int VPP = OUT_BF16 ? 8 : 4;  // values per 16-byte piece of Y
+  constexpr int CPR = WN / VPP;          // pieces per row
   __syncthreads();  // every wave is done with the ring
   float* ep = reinterpret_cast<float*>(smem + wave * 32 * EP);
+  const bool vec = N % VPP == 0;  // every piece starts 16-byte aligned (Y itself is)
+  const bool vec4 = N % 4 == 0;   // bf16: every piece starts 8-byte aligned
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -251,34 +255,43 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
         ep[rr * (EP / 4) + j * 32 + fr] = acc[i][j][v];
       }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's slab is in LDS (wave-private region)
-    const bool vec = (N & 3) == 0;  // rows start 16-byte aligned (Y itself is)
 #pragma unroll
     for (int k = 0; k < 32 * CPR / 64; ++k) {
       const int cix = k * 64 + lane;
       const int rr = cix / CPR, cc = cix % CPR;
-      const v4f val = *reinterpret_cast<const v4f*>(&ep[rr * (EP / 4) + cc * 4]);
+      float val[VPP];
+#pragma unroll
+      for (int h = 0; h < VPP / 4; ++h) {
+        const v4f t = *reinterpret_cast<const v4f*>(&ep[rr * (EP / 4) + cc * VPP + 4 * h]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) val[4 * h + q] = t[q];
+      }
       const int row = m0 + wm0 + i * 32 + rr;
-      const int col = n0 + wn0 + cc * 4;
+      const int col = n0 + wn0 + cc * VPP;
       if (row >= M) continue;
       if constexpr (OUT_BF16) {
         __bf16* dst = reinterpret_cast<__bf16*>(Yv) + (size_t)row * N + col;
-        const __bf16 b0 = (__bf16)val[0], b1 = (__bf16)val[1], b2 = (__bf16)val[2], b3 = (__bf16)val[3];
-        if (vec && col + 3 < N) {
-          const uint2 pk = {(unsigned)__builtin_bit_cast(uint16_t, b0) | ((unsigned)__builtin_bit_cast(uint16_t, b1) << 16),
-                            (unsigned)__builtin_bit_cast(uint16_t, b2) | ((unsigned)__builtin_bit_cast(uint16_t, b3) << 16)};
-          __builtin_nontemporal_store(pk.x, reinterpret_cast<unsigned*>(dst));
-          __builtin_nontemporal_store(pk.y, reinterpret_cast<unsigned*>(dst) + 1);
+        v4u pk;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          pk[q] = (unsigned)__builtin_bit_cast(uint16_t, (__bf16)val[2 * q]) |
+                  ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)val[2 * q + 1]) << 16);
+        if (vec && col + VPP <= N) {
+          __builtin_nontemporal_store(pk, reinterpret_cast<v4u*>(dst));
+        } else if (vec4 && col + VPP <= N) {  // rows 8-byte aligned only: two 8-byte halves
+          typedef unsigned v2u_ __attribute__((ext_vector_type(2)));
+          __builtin_nontemporal_store(v2u_{pk[0], pk[1]}, reinterpret_cast<v2u_*>(dst));
+          __builtin_nontemporal_store(v2u_{pk[2], pk[3]}, reinterpret_cast<v2u_*>(dst) + 1);
         } else {
-          const __bf16 bv[4] = {b0, b1, b2, b3};
-          for (int q = 0; q < 4; ++q)
-            if (col + q < N) dst[q] = bv[q];
+          for (int q = 0; q < VPP; ++q)
+            if (col + q < N) dst[q] = (__bf16)val[q];
         }
       } else {
         float* dst = reinterpret_cast<float*>(Yv) + (size_t)row * N + col;
-        if (vec && col + 3 < N) {
-          __builtin_nontemporal_store(val, reinterpret_cast<v4f*>(dst));
+        if (vec && col + VPP <= N) {
+          __builtin_nontemporal_store(v4f{val[0], val[1], val[2], val[3]}, reinterpret_cast<v4f*>(dst));
         } else {
-          for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < VPP; ++q)
             if (col + q < N) dst[q] = val[q];
         }
       }

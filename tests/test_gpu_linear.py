@@ -79,14 +79,16 @@ def test_decode_kernel_random_scales():
     assert r <= 1e-6
 
 
-@pytest.mark.parametrize("M,N,K", [(512, 512, 1024), (300, 520, 512), (256, 261, 512), (777, 1000, 1536),
-                                   (2048, 8192, 512), (2048, 12544, 512), (4000, 14272, 512)])
+@pytest.mark.parametrize("M,N,K", [(512, 512, 1024), (300, 520, 512), (256, 261, 512), (512, 772, 512),
+                                   (777, 1000, 1536), (2048, 8192, 512), (2048, 12544, 512),
+                                   (4000, 14272, 512)])
 def test_large_tile_kernel_unit_scales_exact(M, N, K):
     # shapes routed to the large-tile kernel (K % 512 == 0, M, N >= 256), ragged edges included.
     # On 256 CUs the column plan is: one round of 256x256 tiles for 2048 x 8192; 256x256 tiles
     # then 256x192 tiles for 2048 x 12544; 256x192 tiles alone for the small shapes; for
     # 4000 x 14272, 32 panels of 256 then 32 of 192 (the last one 128 columns wide) over 16 row
-    # tiles, the last one 160 rows.
+    # tiles, the last one 160 rows. The bf16 output takes 16-byte pieces when N % 8 == 0, two
+    # 8-byte halves when N % 8 == 4 (772), and single elements otherwise (261).
     rng = np.random.default_rng(M + N + K)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
