@@ -18,8 +18,8 @@
 //    multiplied, stage s+1 is dequantized once per workgroup into an fp16 tile in the
 //    other LDS buffer (pitch 144 bytes: the fragment reads hit distinct banks).
 //  * W is the row operand and X the column operand of every MFMA, so each lane ends with
-//    four consecutive output features of one token and stores them with one 8- or 16-byte
-//    store.
+//    four consecutive output features of one token: one 16-byte LDS write when the output
+//    tile is staged for whole-row 16-byte stores of Y.
 //  * Workgroup i runs on XCD i % 8; each XCD takes a contiguous range of tiles, walked
 //    M-fastest within groups of 8 tile rows.
 //  * Two tile widths in one launch, as in the MXFP4 kernel: when 256x256 tiles would leave
@@ -48,12 +48,14 @@ struct Tile {
   static constexpr int BN = BN_, WGM = WGM_, WGN = WGN_;
   static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
   static constexpr int STAGE = (BM + BN) * PITCH;
+  static constexpr int EP = WN * 4 + 16;  // epilogue staging row pitch (bytes): 16 rows hit distinct banks
   static constexpr int CHUNKS = (BM + BN) * 2;         // 32-element chunks per stage
   static constexpr int CPT = (CHUNKS + NT - 1) / NT;   // chunks per thread (the last round may be partial)
   static_assert(WGM * WGN == WAVES, "wave layout");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "whole 32x32 fragments");
   static_assert(CHUNKS % 64 == 0, "whole waves per chunk round");
   static_assert(2 * STAGE <= LDS_BYTES, "two stages fit");
+  static_assert(WAVES * 32 * EP <= LDS_BYTES, "epilogue staging fits");
 };
 using Wide = Tile<256, 2, 4>;
 using Narrow = Tile<192, 4, 2>;
@@ -186,42 +188,70 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
     stage(P1{}, s + 1);
   }
 
-  // acc[i][j][4q + r] = Y[m][n + r] with m = wm0 + 32 i + l % 32, n = wn0 + 32 j + 8 q + 4 (l / 32)
+  // acc[i][j][4q + r] = Y[m][n + r] with m = wm0 + 32 i + l % 32, n = wn0 + 32 j + 8 q + 4 (l / 32).
+  // Epilogue: each wave stages one 32 x WN slab of float32 at a time in its own region of the
+  // (now idle) LDS ring, one 16-byte write per 4 values, then writes whole 16-byte pieces of its
+  // rows: 4 float32 values, or 8 bf16 values (two 8-byte halves when N % 8 == 4). Every value is
+  // scaled by s_tx * s_tw in float32 before the bf16 rounding (to nearest even).
+  constexpr int EP = C::EP;
+  constexpr int VPP = OUT_BF16 ? 8 : 4;  // values per 16-byte piece of Y
+  constexpr int CPR = WN / VPP;          // pieces per row
   const float ts = x_ts[0] * w_ts[0];
-  const bool vec = (N & 3) == 0;
+  const bool vec = N % VPP == 0;  // every piece starts 16-byte aligned (Y itself is)
+  const bool vec4 = N % 4 == 0;   // bf16: every piece starts 8-byte aligned
+  __syncthreads();                // every wave is done with the ring
+  float* ep = reinterpret_cast<float*>(smem + wave * 32 * EP);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm0 + i * 32 + fr;
-    if (m >= M) continue;
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn0 + j * 32 + 8 * q + 4 * fh;
-        const float y[4] = {acc[i][j][4 * q] * ts, acc[i][j][4 * q + 1] * ts, acc[i][j][4 * q + 2] * ts,
-                            acc[i][j][4 * q + 3] * ts};
-        if constexpr (OUT_BF16) {
-          __bf16* dst = reinterpret_cast<__bf16*>(Yv) + (size_t)m * N + n;
-          if (vec && n + 3 < N) {
-            const uint2 pk = {(unsigned)__builtin_bit_cast(uint16_t, (__bf16)y[0]) |
-                                  ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)y[1]) << 16),
-                              (unsigned)__builtin_bit_cast(uint16_t, (__bf16)y[2]) |
-                                  ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)y[3]) << 16)};
-            *reinterpret_cast<uint2*>(dst) = pk;
-          } else {
-            for (int r = 0; r < 4; ++r)
-              if (n + r < N) dst[r] = (__bf16)y[r];
-          }
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<v4f*>(&ep[fr * (EP / 4) + j * 32 + 8 * q + 4 * fh]) =
+            v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's slab is in LDS (wave-private region)
+#pragma unroll
+    for (int k = 0; k < 32 * CPR / 64; ++k) {
+      const int cix = k * 64 + lane;
+      const int rr = cix / CPR, cc = cix % CPR;
+      float y[VPP];
+#pragma unroll
+      for (int h = 0; h < VPP / 4; ++h) {
+        const v4f t = *reinterpret_cast<const v4f*>(&ep[rr * (EP / 4) + cc * VPP + 4 * h]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[4 * h + r] = t[r] * ts;
+      }
+      const int m = m0 + wm0 + i * 32 + rr;
+      const int n = n0 + wn0 + cc * VPP;
+      if (m >= M) continue;
+      if constexpr (OUT_BF16) {
+        __bf16* dst = reinterpret_cast<__bf16*>(Yv) + (size_t)m * N + n;
+        v4u pk;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          pk[r] = (unsigned)__builtin_bit_cast(uint16_t, (__bf16)y[2 * r]) |
+                  ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)y[2 * r + 1]) << 16);
+        if (vec && n + VPP <= N) {
+          __builtin_nontemporal_store(pk, reinterpret_cast<v4u*>(dst));
+        } else if (vec4 && n + VPP <= N) {  // rows 8-byte aligned only: two 8-byte halves
+          typedef unsigned v2u_ __attribute__((ext_vector_type(2)));
+          __builtin_nontemporal_store(v2u_{pk[0], pk[1]}, reinterpret_cast<v2u_*>(dst));
+          __builtin_nontemporal_store(v2u_{pk[2], pk[3]}, reinterpret_cast<v2u_*>(dst) + 1);
         } else {
-          float* dst = reinterpret_cast<float*>(Yv) + (size_t)m * N + n;
-          if (vec && n + 3 < N) {
-            *reinterpret_cast<v4f*>(dst) = v4f{y[0], y[1], y[2], y[3]};
-          } else {
-            for (int r = 0; r < 4; ++r)
-              if (n + r < N) dst[r] = y[r];
-          }
+          for (int r = 0; r < VPP; ++r)
+            if (n + r < N) dst[r] = (__bf16)y[r];
+        }
+      } else {
+        float* dst = reinterpret_cast<float*>(Yv) + (size_t)m * N + n;
+        if (vec && n + VPP <= N) {
+          __builtin_nontemporal_store(v4f{y[0], y[1], y[2], y[3]}, reinterpret_cast<v4f*>(dst));
+        } else {
+          for (int r = 0; r < VPP; ++r)
+            if (n + r < N) dst[r] = y[r];
         }
       }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // slab read back before the next one overwrites it
   }
 }
 
