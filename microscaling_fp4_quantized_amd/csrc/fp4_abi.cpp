@@ -43,7 +43,7 @@ int check_quantize(const char* who, const void* X, int64_t M, int64_t K, int64_t
   if (K % 32 || K % block)
     return fail(FP4_E_SHAPE, "%s: K=%lld must be a multiple of 32 and of the block %d", who, (long long)K, block);
   if (ld < K) return fail(FP4_E_SHAPE, "%s: leading dimension %lld < K=%lld", who, (long long)ld, (long long)K);
-  if (M * (K / 32) > 0x7FFFFFFFLL || ld > (int64_t)1 << 40)
+  if (M > 0x7FFFFFFFLL / (K / 32) || ld > (int64_t)1 << 40)  // K >= 32 here; no product can overflow
     return fail(FP4_E_SHAPE, "%s: tensor too large (rows*K/32 must fit in 31 bits)", who);
   if (!aligned(X, 16) || ld % 8) return fail(FP4_E_ALIGN, "%s: input must be 16-byte aligned, ld %% 8 == 0", who);
   if (!aligned(codes, 16)) return fail(FP4_E_ALIGN, "%s: codes must be 16-byte aligned", who);

@@ -98,6 +98,9 @@ def test_size_limits(lib):
     # rows * K / 32 must fit in 31 bits (chunk indices); rejected before anything is launched
     assert q(lib, M=1 << 26, K=1024, ldx=1024) == -2
     assert q(lib, M=(1 << 26) - 1, K=1024, ldx=1 << 41) == -2   # leading dimension out of range
+    # rows * K / 32 beyond 64 bits must not wrap around into an accepted size
+    assert q(lib, M=(1 << 40) + 1, K=1 << 30, ldx=1 << 30) == -2
+    assert q(lib, M=(1 << 62), K=1 << 12, ldx=1 << 12) == -2
     assert lib.fp4_linear(A16, A16, None, A16, A16, None, 1 << 31, 4, 128, 0, A16, 0, None) == -2
     assert lib.fp4_linear(A16, A16, None, A16, A16, None, 4, 1 << 31, 128, 0, A16, 0, None) == -2
 
