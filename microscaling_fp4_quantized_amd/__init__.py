@@ -11,8 +11,9 @@ raises if it is not built.
 
 
 def __getattr__(name):
-    if name in ("fp4_rotate_quantize", "fp4_quantize_weights", "fp4_linear", "fp4_abi_version",
-                "Fp4Error", "load_library", "library_path", "group_size", "FP4_MXFP4", "FP4_NVFP4"):
+    if name in ("fp4_rotate_quantize", "fp4_quantize_weights", "fp4_linear", "fp4_rotate_quantize_linear",
+                "fp4_abi_version", "Fp4Error", "load_library", "library_path", "group_size", "FP4_MXFP4",
+                "FP4_NVFP4"):
         from . import binding
         return getattr(binding, name)
     raise AttributeError(name)

@@ -21,6 +21,7 @@ __all__ = [
     "fp4_rotate_quantize",
     "fp4_quantize_weights",
     "fp4_linear",
+    "fp4_rotate_quantize_linear",
     "fp4_abi_version",
     "group_size",
 ]
