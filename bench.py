@@ -279,8 +279,26 @@ def extra_rows(B, WL, torch, dev):
                                "traffic": measured_traffic("gemm_mxfp4_ring_large", "gemm_mxfp4_ring.hip")}
     log(f"[bench] large MXFP4 GEMM {ms * 1e3:.1f} us = {tf:.0f} TFLOP/s ({tf / MFMA_FP4_PEAK_TFLOPS:.1%} of peak)")
     del xq, xs, wq, ws, y
+    # the headline layer at twice the tokens: M=4096 K=4096 N=14336, MXFP4 block 32, Y bf16
+    wl = WL.WORKLOADS["prefill_mx_m4096"]
+    xq, xs, _ = B.fp4_rotate_quantize(bf16_dev(WL.draw_x(wl), dev), wl.block, "mxfp4")
+    wq, ws, _ = B.fp4_quantize_weights(bf16_dev(WL.draw_w(wl), dev), wl.block, "mxfp4")
+    y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.25:  # 250 ms of this kernel first, as the headline step's ramp
+        for _ in range(20):
+            B.fp4_linear(xq, xs, wq, ws, "mxfp4", out_dtype=torch.bfloat16, out=y)
+        torch.cuda.synchronize()
+    ms = time_batch(lambda i: B.fp4_linear(xq, xs, wq, ws, "mxfp4", out_dtype=torch.bfloat16, out=y), 20, torch)
+    tf = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
+    out["gemm_mxfp4_m4096"] = {"workload": "prefill_mx_m4096: M=4096 K=4096 N=14336, block 32, Y bf16",
+                               "us": ms * 1e3, "TFLOP/s": tf, "frac_fp4_mfma_peak": tf / MFMA_FP4_PEAK_TFLOPS,
+                               "algorithmic_bytes": (wl.M + wl.N) * wl.K * (0.5 + 1.0 / 32) + wl.M * wl.N * 2,
+                               "traffic": measured_traffic("gemm_mxfp4_ring_m4096", "gemm_mxfp4_ring.hip")}
+    log(f"[bench] M=4096 MXFP4 GEMM {ms * 1e3:.1f} us = {tf:.0f} TFLOP/s ({tf / MFMA_FP4_PEAK_TFLOPS:.1%} of peak)")
+    del xq, xs, wq, ws, y
     # decode-shaped MXFP4 GEMM: W 4096x4096 streamed once per call
-    for name in ("decode1", "decode16"):
+    for name in ("decode1", "decode4", "decode16"):
         wl = WL.WORKLOADS[name]
         xq, xs, _ = B.fp4_rotate_quantize(bf16_dev(WL.draw_x(wl), dev), wl.block, "mxfp4")
         wq, ws, _ = B.fp4_quantize_weights(bf16_dev(WL.draw_w(wl), dev), wl.block, "mxfp4")

@@ -91,7 +91,7 @@ WORKLOADS = {
     "prefill_mx": Workload("prefill_mx", 6, 2048, 4096, 14336, 32, "mxfp4", "t5", 0.01, 30.0,
                            out_dtype="bf16"),
     "prefill_mx_m4096": Workload("prefill_mx_m4096", 7, 4096, 4096, 14336, 32, "mxfp4", "t5",
-                                 0.01, 30.0),
+                                 0.01, 30.0, out_dtype="bf16"),
     "large": Workload("large", 4, 8192, 8192, 28672, 128, "mxfp4", "normal", 0.005, 100.0),
     "stress_mx32": Workload("stress_mx32", 5, 16384, 8192, 0, 32, "mxfp4", "t3_lognormal", 0, 1.0),
     "stress_mx128": Workload("stress_mx128", 5, 16384, 8192, 0, 128, "mxfp4", "t3_lognormal", 0, 1.0),
