@@ -6,7 +6,8 @@ block-Hadamard rotate + MXFP4 quantize of the bf16 activations
 (fp4_rotate_quantize), then the W4A4 GEMM against weights rotated and
 quantized offline (fp4_linear). The default workload is the prefill linear
 layer K=4096, N=14336 with M=2048 tokens, MXFP4, Hadamard block 32, float32
-output. Weights are quantized once, before timing (offline in the method).
+accumulation and bf16 output. Weights are quantized once, before timing (offline
+in the method).
 
 Printed: ONE JSON line with the step throughput (TFLOP/s of the linear layer,
 2*M*N*K per step), the GEMM's roofline (MFMA FP4 peak), the rotate+quantize
