@@ -92,6 +92,8 @@ enum {
  *  X            device, bf16 [M, ldx] row-major; columns 0..K-1 are used.
  *               16-byte aligned; ldx >= K and ldx % 8 == 0.
  *  M            rows, M >= 1.   K: columns, K >= 1, K % block == 0, K % 32 == 0.
+ *               M * (K / 32) <= 2^31 - 1 (32-element chunks are indexed in 32 bits)
+ *               and ldx <= 2^40; larger shapes return FP4_E_SHAPE.
  *  block        16, 32, 64 or 128.
  *  fmt          FP4_MXFP4 or FP4_NVFP4.
  *  codes        device, uint8 [M, K/2]: byte j of a row holds element 2j in
