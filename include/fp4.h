@@ -183,7 +183,8 @@ FP4_API int fp4_quantize_weights_ex(const void *W, int64_t N, int64_t K, int64_t
  *  Xq  device uint8 [M, K/2], Xs device uint8 [M, K/g]  (fp4_rotate_quantize output)
  *  Wq  device uint8 [N, K/2], Ws device uint8 [N, K/g]  (fp4_quantize_weights output)
  *  x_ts, w_ts  NVFP4: device float[1] tensor scales (4-byte aligned); MXFP4: must be NULL.
- *  M, N >= 1; K >= 128 and K % 128 == 0.
+ *  M, N >= 1; K >= 128 and K % 128 == 0. M, N, K <= 2^31 - 1 and M * K / 2,
+ *  N * K / 2 <= 2^40 bytes; larger shapes return FP4_E_SHAPE.
  *  Xq, Wq 16-byte aligned; Xs, Ws 4-byte aligned.
  *  Y   device [M, N] row-major, float32 (FP4_OUT_F32) or bf16 (FP4_OUT_BF16,
  *      round-to-nearest-even); 16-byte aligned.
