@@ -6,8 +6,10 @@ product (the HIP library and its Python binding) never does. The oracle and
 the HIP path share no code; only the seeded input generators feed both.
 
 It is plain, slow and written to be checked against the pages by eye: NumPy
-only, float64 wherever the pages leave the precision open, float32 where a
-step is defined in float32 (the rotation and the NVFP4 element step).
+only, float64 wherever the pages leave the precision open, and float32 where
+a float decides an integer result (a code, a scale choice) and the pages fix no
+precision: the rotation (R3), the NVFP4 element step (R6) and scale fitting
+(R14) take that decision in float32, the precision of the rotated values.
 
 Pages (cited by title and section):
 
@@ -59,9 +61,16 @@ R5  NVFP4 tensor scale s_t = fl32(T / (6 * 448)) with T the absolute maximum of
     speaks of group and tensor scales). The E4M3 group code is the nearest
     E4M3FN value to alpha_max / (6 s_t) (ties to even, saturating at 448),
     decided exactly. s_t == 0 makes the whole tensor zero.
-R6  NVFP4 element step in float32, as the kernel computes it:
-    S = fl32(d * s_t), R = fl32(1 / S), u = fl32(y * R); a group with
-    S < 2^-126 (including d == 0) is all signed zeros.
+R6  NVFP4 element step. The pages give no precision for dividing an element by its
+    two scales, and here a float decides an integer code, so one float32 sequence is
+    fixed, in the precision of the rotated values (R3) and of the float32 tensor scale
+    (R5): the group's dequantization scale is the float32 number S = fl32(d * s_t)
+    (the two stored scales multiplied once), and a per-group scale is applied to the
+    group's elements through its float32 reciprocal, R = fl32(1 / S), u = fl32(y * R).
+    Three roundings separate u from the exact quotient y / (d s_t) (relative distance
+    below 2^-22), so the code differs from the one the exact quotient gives only for
+    elements that near_boundary_flags marks (a test checks this against the exact
+    quotient). A group with S < 2^-126 (including d == 0) is all signed zeros.
 R7  E2M1 rounding is round-to-nearest, ties to the even code, saturating at
     +-6, keeping the sign of the input (so -0 and small negatives give 0x8).
     Codes: bit 3 = sign, bits 2..0 index {0, .5, 1, 1.5, 2, 3, 4, 6}.
@@ -85,11 +94,14 @@ R14 Scale fitting ([BRIDGE-de] §2 "Einführung von MR-GPTQ", item 2: MXFP4 scal
     procedure; the reading taken is a data-free per-group search: among the standard
     scale and its two neighbours (MXFP4: e - 1, e + 1; NVFP4: the adjacent E4M3 codes,
     tensor scale unchanged) keep the one with the least squared error of the group.
-    The error is formed in float32, in element order: d_i = fl32(y_i - deq_i),
-    acc = fl32(acc + fl32(d_i * d_i)), with deq_i = e2m1 * 2^e (MX, exact) or
-    fl32(e2m1 * S) with S = fl32(d * s_t) (NV). Candidates are tried in the order
-    standard, smaller, larger and replace the current one only when strictly better.
-    Meant for weights (offline), where the extra work is paid once.
+    The pages give no precision either, and the choice is an integer decided by floats,
+    so the error is formed in float32, the precision of the rotated values, summed in
+    element order: d_i = fl32(y_i - deq_i), acc = fl32(acc + fl32(d_i * d_i)), with
+    deq_i = e2m1 * 2^e (MX, exact) or fl32(e2m1 * S), S = fl32(d * s_t) (NV, as R6).
+    Candidates are tried in the order standard, smaller, larger and replace the current
+    one only when strictly better. The chosen scale is within float32 rounding of the
+    exact least-squares choice (a test checks it with exact rationals). Meant for
+    weights (offline), where the extra work is paid once.
 R16 Given tensor scale (NVFP4, optional): s_t is supplied by the caller instead of being
     computed from this tensor (a calibrated static activation scale; [BRIDGE-es] §2.B treats
     the tensor scale as a quantity to optimise). Every step after the tensor maximum is the
@@ -501,27 +513,38 @@ def linear_f64(xq, xs, wq, ws, fmt: str, x_ts=None, w_ts=None) -> np.ndarray:
 
 
 def bf16_rne_f64(y: np.ndarray) -> np.ndarray:
-    """Round float64 values to bfloat16 (nearest, ties to even), returned as float64.
+    """Round float64 values to bfloat16 (nearest, ties to even, one rounding), returned as
+    float64. Values beyond the largest finite bfloat16 are outside its domain.
 
     Used only to form the reference of a bf16-output GEMM: the output dtype
     fixes the reference.
     """
     y = np.asarray(y, dtype=np.float64)
-    m, e = np.frexp(y)  # y = m 2^e, |m| in [0.5, 1): 8 significant bits -> m * 2^8 integer
-    r = np.ldexp(np.round(np.ldexp(m, 8)), e - 8)  # np.round rounds half to even
-    return r
+    _, e = np.frexp(y)  # |y| in [2^(e-1), 2^e): bf16 keeps 8 significant bits, so the step is 2^(e-8)
+    e = np.maximum(e, -125)  # below 2^-126 bf16 is subnormal: a fixed step of 2^-133
+    q = np.ldexp(1.0, e - 8)
+    return np.round(y / q) * q  # y / q and the product are exact; np.round rounds half to even
 
 
 # --------------------------------------------------------------------------
 # parity support: elements and groups next to a rounding boundary
 # --------------------------------------------------------------------------
 def near_boundary_flags(y32: np.ndarray, scales: np.ndarray, fmt: str, s_t=None, rel=1e-6):
-    """Elements whose float32 rotated value lies within ``rel`` (relative) of a
-    rounding boundary: an E2M1 midpoint times the group scale, or, for the whole
-    group, an MX exponent threshold 6*2^k / an E4M3 midpoint of the group scale.
+    """Elements whose float32 rotated value lies within ``rel`` (relative) of a rounding
+    boundary of its quantization.
 
-    Returns a bool array [rows, K]. Used only to report (never to excuse)
-    differences: the parity rule still demands bit equality everywhere else.
+    * Element boundary: |y| = t * S for an E2M1 midpoint t (0.25, 0.75, ... 5), with S the
+      group's dequantization scale in float64 (2^e for MXFP4, d * s_t for NVFP4). A group
+      whose scale is zero stores signed zeros and has no element boundary.
+    * Group boundary (flags every element of the group): the group maximum within ``rel``
+      of 6 * 2^k for an integer k (MXFP4: the shared exponent steps there), or alpha_max /
+      (6 s_t) within ``rel`` of a midpoint between two adjacent E4M3 values (NVFP4: the
+      group code changes there).
+
+    Returns a bool array [rows, K]. The parity tests count differences at flagged
+    elements apart from the others: the others must be zero, and the exact tests (inputs
+    whose rotation is exact, or the fixed float32 order on both sides) require zero
+    differences of both kinds.
     """
     rows, K = y32.shape
     g = MX_GROUP if fmt == "mxfp4" else NV_GROUP
@@ -531,12 +554,13 @@ def near_boundary_flags(y32: np.ndarray, scales: np.ndarray, fmt: str, s_t=None,
     else:
         scale = e4m3_value(scales) * np.float64(s_t)
     flags = np.zeros(grp.shape, dtype=bool)
+    live = (scale > 0)[..., None]
     for t in _E2M1_MIDPOINTS:
         bnd = t * scale[..., None]
-        flags |= np.abs(grp - bnd) <= rel * bnd
+        flags |= live & (np.abs(grp - bnd) <= rel * bnd)
     amax = grp.max(axis=2)
     if fmt == "mxfp4":
-        # exponent thresholds alpha_max = 6 * 2^k
+        # exponent thresholds alpha_max = 6 * 2^k, k the nearest integer to log2(alpha_max / 6)
         with np.errstate(divide="ignore"):
             k = np.round(np.log2(np.where(amax > 0, amax, 1.0) / 6.0))
         thr = 6.0 * np.ldexp(1.0, k.astype(np.int64))
@@ -548,7 +572,7 @@ def near_boundary_flags(y32: np.ndarray, scales: np.ndarray, fmt: str, s_t=None,
             q = amax / (6.0 * np.float64(s_t))
             j = np.clip(np.searchsorted(_E4M3_MIDPOINTS, q), 0, len(_E4M3_MIDPOINTS) - 1)
             gflag = np.zeros(amax.shape, dtype=bool)
-            for jj in (j - 1, j):
+            for jj in (j - 1, j):  # the midpoints just below and just above q
                 m = _E4M3_MIDPOINTS[np.clip(jj, 0, len(_E4M3_MIDPOINTS) - 1)]
                 gflag |= np.abs(q - m) <= rel * m
     flags |= gflag[..., None]

@@ -578,3 +578,184 @@ def test_given_tensor_scale():
     assert np.array_equal(q4[0], dyn[0]) and np.array_equal(q4[1], dyn[1])
     z = O.rotate_quantize(x, 16, "nvfp4", tensor_scale=np.float32(0))
     assert np.all(z[1] == 0) and np.all((O.unpack_nibbles(z[0]) & 7) == 0)
+
+
+# --------------------------------------------------------------------------
+# bf16 helpers against torch's bfloat16 (a library implementation of the format)
+# --------------------------------------------------------------------------
+def test_widen_bf16_matches_torch_on_every_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = O.widen_bf16(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    fin = np.isfinite(ref)
+    assert fin.sum() == (1 << 16) - 2 * 128  # exponent field all ones: 128 patterns per sign
+    assert np.array_equal(ours[fin].view(np.uint32), ref[fin].view(np.uint32))  # -0, subnormals included
+    assert np.array_equal(np.isnan(ours), np.isnan(ref)) and np.array_equal(np.isinf(ours), np.isinf(ref))
+
+
+def _bf16_neighbours_f32(n, seed):
+    """float32 values at, next to and halfway between bfloat16 values: random bf16 patterns
+    (normal and subnormal) with the low half of the float32 word set to 0x0000, 0x7FFF,
+    0x8000 (an exact tie), 0x8001 and random bits."""
+    g = rng(seed)
+    hi = g.integers(0, 0x7F7F, size=n, dtype=np.uint32)  # finite bf16 magnitudes below the largest
+    hi |= (g.integers(0, 2, size=n, dtype=np.uint32) << 15)  # both signs
+    lows = np.array([0x0000, 0x7FFF, 0x8000, 0x8001], dtype=np.uint32)
+    lo = np.concatenate([np.repeat(lows, n // 8), g.integers(0, 1 << 16, size=n - 4 * (n // 8), dtype=np.uint32)])
+    return ((hi << 16) | lo).view(np.float32)
+
+
+def test_bf16_rne_f64_matches_torch_cast_including_ties():
+    y = _bf16_neighbours_f32(40000, 31)
+    ours = O.bf16_rne_f64(y.astype(np.float64))
+    # float32 -> bfloat16 in torch is one round-to-nearest-even; the float32 inputs are exact in float64
+    ref = torch.from_numpy(y).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref)
+    ties = (y.view(np.uint32) & 0xFFFF) == 0x8000
+    assert ties.sum() >= 4000  # the exact ties are exercised
+
+
+def test_bf16_rne_f64_rounds_once_from_float64():
+    # float64 values a hair above / below a bf16 tie: one rounding must go to the nearer side, which a
+    # detour through float32 (rounding the tie first) would get wrong; checked with exact rationals
+    base = _bf16_neighbours_f32(64, 33)
+    base = base[np.isfinite(base) & (np.abs(base) > 1e-30)]
+    bits = (base.view(np.uint32) & np.uint32(0xFFFF0000)) | np.uint32(0x8000)  # exact ties in float32
+    tie = bits.view(np.float32).astype(np.float64)
+    for sgn in (1.0, -1.0):
+        y = tie * (1.0 + sgn * 2.0 ** -40)
+        got = O.bf16_rne_f64(y)
+        for yi, gi in zip(y[:32], got[:32]):
+            fy = Fraction(float(yi))
+            lo_bits = (np.float32(yi).view(np.uint32) & np.uint32(0xFFFF0000))
+            a = Fraction(float(lo_bits.view(np.float32)))                 # bf16 value truncated toward zero
+            step = Fraction(2) ** (math.frexp(float(a))[1] - 8)
+            b = a + (step if a > 0 else -step)                           # the next bf16 value away from zero
+            want = a if abs(fy - a) < abs(fy - b) else b
+            assert Fraction(float(gi)) == want, (yi, gi, want)
+
+
+# --------------------------------------------------------------------------
+# near-boundary flags: values placed at, just inside and just outside each boundary
+# --------------------------------------------------------------------------
+E2M1_TIES = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)  # midpoints of {0, .5, 1, 1.5, 2, 3, 4, 6}
+INSIDE = (1.0, 1 + 5e-7, 1 - 5e-7)   # within 1e-6 relative (float32 rounding moves them by < 1.2e-7)
+OUTSIDE = (1 + 2e-6, 1 - 2e-6)        # beyond it
+
+
+def _rows_of_groups(groups, g):
+    """Stack per-group value lists into one float32 row per group (zeros elsewhere)."""
+    out = np.zeros((len(groups), g), dtype=np.float32)
+    for i, vals in enumerate(groups):
+        out[i, :len(vals)] = np.asarray(vals, dtype=np.float32)
+    return out
+
+
+def test_flags_mx_element_ties():
+    groups, scales, want = [], [], []
+    for e in (-9, 0, 6):
+        for t in E2M1_TIES:
+            for f in INSIDE + OUTSIDE:
+                for sgn in (1, -1):
+                    # a maximum of 4.5 * 2^e (4.5 is 0.75 of 6 and 1.5 of 3: no exponent threshold near)
+                    groups.append([4.5 * 2.0 ** e, sgn * t * f * 2.0 ** e])
+                    scales.append(e + 127)
+                    want.append([False, f in INSIDE])
+    y = _rows_of_groups(groups, 32)
+    flags = O.near_boundary_flags(y, np.array(scales, np.uint8)[:, None], "mxfp4")
+    exp = np.zeros_like(flags)
+    exp[:, :2] = np.array(want)
+    assert np.array_equal(flags, exp)
+
+
+def test_flags_mx_exponent_thresholds():
+    groups, scales, want = [], [], []
+    for k in (-20, -1, 0, 3, 40):
+        for thr in (6.0 * 2.0 ** k, 3.0 * 2.0 ** k):  # 3 * 2^k is 6 * 2^(k-1)
+            for f in INSIDE + OUTSIDE:
+                a = thr * f
+                e = int(np.ceil(np.log2(thr / 6.0))) + (1 if f > 1 else 0)  # standard rule, by hand
+                groups.append([a, 0.1 * a])  # 0.1 a / 2^e lies in [0.3, 0.6): no E2M1 tie near
+                scales.append(e + 127)
+                want.append(f in INSIDE)
+    y = _rows_of_groups(groups, 32)
+    flags = O.near_boundary_flags(y, np.array(scales, np.uint8)[:, None], "mxfp4")
+    assert np.array_equal(flags, np.repeat(np.array(want)[:, None], 32, axis=1))
+
+
+# E4M3 codes of several magnitudes, subnormal ones included: 1.0, 1.375, 2^-6, 5 * 2^-9, 448
+E4M3_PROBE_CODES = (0x38, 0x3B, 0x08, 0x05, 0x7E)
+
+
+def test_flags_nv_element_ties():
+    s_t = np.float32(2.0 ** -3)
+    groups, scales, want = [], [], []
+    for c in E4M3_PROBE_CODES:
+        d = float(O.e4m3_value(np.array([c]))[0])
+        for t in E2M1_TIES:
+            for f in INSIDE + OUTSIDE:
+                for sgn in (1, -1):
+                    # maximum 6 d s_t: alpha / (6 s_t) = d, an E4M3 value (half a step from any midpoint)
+                    groups.append([6 * d * float(s_t), sgn * t * f * d * float(s_t)])
+                    scales.append(c)
+                    want.append([False, f in INSIDE])
+    y = _rows_of_groups(groups, 16)
+    flags = O.near_boundary_flags(y, np.array(scales, np.uint8)[:, None], "nvfp4", s_t)
+    exp = np.zeros_like(flags)
+    exp[:, :2] = np.array(want)
+    assert np.array_equal(flags, exp)
+
+
+def test_flags_nv_e4m3_midpoints():
+    s_t = np.float32(2.0 ** 5)
+    # E4M3FN values from torch's float8 type: subnormal, middle and top codes
+    codes = list(range(0, 12)) + list(range(52, 60)) + list(range(118, 127))
+    e4 = torch.tensor(codes, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    groups, scales, want = [], [], []
+    for i in range(len(codes) - 1):
+        if codes[i + 1] != codes[i] + 1:
+            continue
+        lo, hi = e4[i], e4[i + 1]
+        mid = (lo + hi) / 2
+        for f in INSIDE + OUTSIDE:
+            a = 6 * float(s_t) * mid * f
+            groups.append([a, 0.05 * a])  # 0.05 a / (d s_t) is at most 0.6: no E2M1 tie near
+            # the code of the standard rule: nearest E4M3 value, the even code at the midpoint itself
+            scales.append(codes[i] + (1 if f > 1 or (f == 1 and codes[i] % 2 == 1) else 0))
+            want.append(f in INSIDE)
+    y = _rows_of_groups(groups, 16)
+    flags = O.near_boundary_flags(y, np.array(scales, np.uint8)[:, None], "nvfp4", s_t)
+    assert len(want) > 100
+    assert np.array_equal(flags, np.repeat(np.array(want)[:, None], 16, axis=1))
+
+
+def test_flags_zero_scale_groups_and_zero_tensor():
+    # an NVFP4 group whose code decodes to 0 stores signed zeros: nothing to flag in it
+    y = _rows_of_groups([[1e-30, -2e-31, 0.0]], 16)
+    assert not O.near_boundary_flags(y, np.zeros((1, 1), np.uint8), "nvfp4", np.float32(1.0)).any()
+    assert not O.near_boundary_flags(np.zeros((2, 32), np.float32), np.zeros((2, 2), np.uint8), "nvfp4",
+                                     np.float32(0.0)).any()
+    assert not O.near_boundary_flags(np.zeros((2, 64), np.float32), np.zeros((2, 2), np.uint8), "mxfp4").any()
+
+
+# --------------------------------------------------------------------------
+# the tie rule through the whole quantizer: inputs whose rotation is exact put elements
+# exactly on every E2M1 midpoint; the codes must be the even neighbours (hand table)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("case", ["mx16", "mx64", "nv-3", "nv10"])
+def test_oracle_codes_on_exact_ties(case):
+    from exact_inputs import build_input, check_tie_codes, mx_rows, nv_rows
+
+    if case.startswith("mx"):
+        b = int(case[2:])
+        bits, U = build_input(mx_rows(b), b)
+        p, sc, _ = O.rotate_quantize(bits, b, "mxfp4")
+        scale = np.where(sc == 0, 0.0, np.ldexp(1.0, sc.astype(np.int64) - 127))
+        n = check_tie_codes(p, U, scale, 32)
+    else:
+        k = int(case[2:])
+        bits, U = build_input(nv_rows(k), 16)
+        p, sc, st = O.rotate_quantize(bits, 16, "nvfp4")
+        assert st == np.float32(2.0 ** k)
+        n = check_tie_codes(p, U, O.e4m3_value(sc) * 2.0 ** k, 16)
+    assert n > 50
