@@ -185,7 +185,9 @@ FP4_API int fp4_quantize_weights_ex(const void *W, int64_t N, int64_t K, int64_t
  *  x_ts, w_ts  NVFP4: device float[1] tensor scales (4-byte aligned); MXFP4: must be NULL.
  *  M, N >= 1; K >= 128 and K % 128 == 0. M, N, K <= 2^31 - 1 and M * K / 2,
  *  N * K / 2 <= 2^40 bytes; larger shapes return FP4_E_SHAPE.
- *  Xq, Wq 16-byte aligned; Xs, Ws 4-byte aligned.
+ *  Xq, Wq 16-byte aligned; Xs, Ws 4-byte aligned. (MXFP4 with 16-byte-aligned Xs and Ws
+ *  and K % 512 == 0 runs the decode kernel for M <= 16 and the 256-row-tile kernel for
+ *  M, N >= 256; other pointers or shapes run the general kernel.)
  *  Y   device [M, N] row-major, float32 (FP4_OUT_F32) or bf16 (FP4_OUT_BF16,
  *      round-to-nearest-even); 16-byte aligned.
  * No bias, no activation. One kernel launch on `stream`.
@@ -210,8 +212,8 @@ FP4_API int fp4_linear(const uint8_t *Xq, const uint8_t *Xs, const float *x_ts,
  *  X       device bf16 [M, ldx], 16-byte aligned, ldx >= K, ldx % 8 == 0.
  *  M       1..16 tokens.   K: a multiple of 512 with M * (K/2 + 16 + K/32) <= 160 KiB.
  *  block   16, 32, 64 or 128 (the block W was quantized with).
- *  Wq, Ws  MXFP4 weights from fp4_quantize_weights: uint8 [N, K/2] (16-byte aligned)
- *          and [N, K/32] (4-byte aligned).
+ *  Wq, Ws  MXFP4 weights from fp4_quantize_weights: uint8 [N, K/2] and [N, K/32], both
+ *          16-byte aligned (16 scale bytes of a row are read at once).
  *  Y       device [M, N], float32 or bf16 (y_dtype), 16-byte aligned.
  * Errors: FP4_E_BLOCK, FP4_E_FORMAT (y_dtype), FP4_E_NULLPTR, FP4_E_SHAPE (M, K, ldx or
  * the on-chip size), FP4_E_ALIGN. One kernel launch on `stream`.

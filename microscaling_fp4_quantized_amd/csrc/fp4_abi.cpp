@@ -148,8 +148,8 @@ int fp4_rotate_quantize_linear(const void* X, int64_t M, int64_t K, int64_t ldx,
     return fail(FP4_E_SHAPE, "%s: M * K too large for the workgroup's LDS; use fp4_rotate_quantize + fp4_linear", who);
   if (ldx < K || ldx > (int64_t)1 << 40) return fail(FP4_E_SHAPE, "%s: leading dimension %lld < K", who, (long long)ldx);
   if (!aligned(X, 16) || ldx % 8) return fail(FP4_E_ALIGN, "%s: X must be 16-byte aligned, ldx %% 8 == 0", who);
-  if (!aligned(Wq, 16) || !aligned(Ws, 4) || !aligned(Y, 16))
-    return fail(FP4_E_ALIGN, "%s: Wq and Y must be 16-byte aligned, Ws 4-byte aligned", who);
+  if (!aligned(Wq, 16) || !aligned(Ws, 16) || !aligned(Y, 16))
+    return fail(FP4_E_ALIGN, "%s: Wq, Ws and Y must be 16-byte aligned", who);
   return launched(who, fp4_launch_decode_fused(static_cast<const uint16_t*>(X), ldx, block, Wq, Ws, M, N, K, Y,
                                                y_dtype == FP4_OUT_BF16, static_cast<hipStream_t>(stream)));
 }

@@ -192,8 +192,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_mxfp4_kernel(
 hipError_t fp4_launch_gemm_mxfp4(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
                                  const uint8_t* Ws, int64_t M, int64_t N, int64_t K, void* Y,
                                  int out_bf16, hipStream_t st) {
-  if (fp4_gemm_mxfp4_decode_fits(M, N, K)) return fp4_launch_gemm_mxfp4_decode(Xq, Xs, Wq, Ws, M, N, K, Y, out_bf16, st);
-  if (fp4_gemm_mxfp4_ring_fits(M, N, K)) return fp4_launch_gemm_mxfp4_ring(Xq, Xs, Wq, Ws, M, N, K, Y, out_bf16, st);
+  // The decode and large-tile kernels read 16 scale bytes of a row at a time, which needs scale
+  // pointers aligned to 16 bytes (K % 512 == 0 keeps every row aligned then); the general kernel
+  // below reads 4-byte words and takes any 4-byte-aligned pair.
+  const bool scales16 = ((reinterpret_cast<uintptr_t>(Xs) | reinterpret_cast<uintptr_t>(Ws)) & 15) == 0;
+  if (scales16 && fp4_gemm_mxfp4_decode_fits(M, N, K))
+    return fp4_launch_gemm_mxfp4_decode(Xq, Xs, Wq, Ws, M, N, K, Y, out_bf16, st);
+  if (scales16 && fp4_gemm_mxfp4_ring_fits(M, N, K))
+    return fp4_launch_gemm_mxfp4_ring(Xq, Xs, Wq, Ws, M, N, K, Y, out_bf16, st);
   constexpr int BM = 128, BN = 128, WM = 64, WN = 64;
   using C = fp4::Cfg<BM, BN, WM, WN>;
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);

@@ -2,9 +2,11 @@
 
 Rule (codes and scales): bit equality. Elements whose float32 rotated value lies
 within 1e-6 (relative) of a rounding boundary are counted and reported; a
-difference there is reported as "flagged", anywhere else as "unflagged", and
-the tests demand zero unflagged differences (with the fixed float32 rotation
-order the expected number of differences is zero everywhere).
+difference there is reported as "flagged", anywhere else as "unflagged". The
+tolerance of the method's statement allows flagged differences; since the kernels
+and the oracle take every float decision in the same float32 sequence, the tests
+demand zero differences of either kind (exact=True, the default), and a flagged
+difference would fail them too.
 GEMM rule: relative Frobenius error <= 1e-3 against the float64 product of the
 oracle's dequantized operands (for bf16 output: against that product rounded to
 bf16).
@@ -82,7 +84,7 @@ def compare_quant(gpu, x_bits: np.ndarray, block: int, fmt: str, rows=None, t_am
     return res
 
 
-def assert_quant_parity(res, label="", exact=False):
+def assert_quant_parity(res, label="", exact=True):
     say(f"parity {label}: {res}")
     assert res["code_mismatch_unflagged"] == 0, res
     assert res["scale_mismatch_unflagged"] == 0, res

@@ -120,6 +120,7 @@ def test_fused_decode_validation(lib):
     assert fused(lib, ldx=256) == -2
     assert fused(lib, X=A16 + 2) == -5
     assert fused(lib, Y=A16 + 4) == -5
+    assert fused(lib, Ws=A16 + 4) == -5                # 16 scale bytes are read at once
     assert b"fp4_rotate_quantize_linear" in lib.fp4_last_error()
 
 

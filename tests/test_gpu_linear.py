@@ -117,6 +117,41 @@ def test_large_tile_kernel_random_scales(M, N, K):
     assert r <= 1e-6
 
 
+def offset_u8(a, off):
+    """A contiguous device copy of a whose data pointer sits `off` bytes past a 256-byte boundary."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    buf = torch.zeros(a.size + 256, dtype=torch.uint8, device="cuda")
+    v = buf[off:off + a.size].view(a.shape)
+    v.copy_(torch.from_numpy(a))
+    assert v.data_ptr() % 16 == off % 16
+    return v
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 300, 1024), (300, 520, 512)])
+def test_scales_only_4byte_aligned(M, N, K):
+    # Xs / Ws 4 bytes past a 16-byte boundary (allowed by the contract): the decode and large-tile
+    # kernels read 16 scale bytes at once, so these shapes must take the general kernel and stay exact
+    rng = np.random.default_rng(5 * M + N)
+    c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    xs = np.full((M, K // 32), 127, np.uint8)
+    ws = np.full((N, K // 32), 127, np.uint8)
+    ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "mxfp4")
+    for ox, ow in ((4, 0), (0, 4), (12, 8)):
+        say(f"case scales at byte offsets {ox}/{ow} M {M} N {N} K {K}")
+        y = B.fp4_linear(dev_u8(O.pack_nibbles(c)), offset_u8(xs, ox), dev_u8(O.pack_nibbles(d)), offset_u8(ws, ow),
+                         "mxfp4")
+        assert np.array_equal(host(y).astype(np.float64), ref)
+
+
+def test_fused_decode_refuses_unaligned_weight_scales():
+    K, N = 512, 64
+    x = dev_bf16(WL.draw_normal_bf16((2, K), 1.0, seed=4))
+    wq = torch.zeros((N, K // 2), dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.Fp4Error):
+        B.fp4_rotate_quantize_linear(x, wq, offset_u8(np.full((N, K // 32), 127, np.uint8), 4), 32)
+
+
 def test_scale_byte_extremes_exact():
     # per-group scales spread over a wide exponent range, still exact in float32
     rng = np.random.default_rng(3)
@@ -219,7 +254,7 @@ def test_ragged_shapes(fmt, block, M, N, K):
     assert r <= GEMM_REL_FRO_TOL
 
 
-@pytest.mark.parametrize("name", ["decode1", "decode4", "decode16"])
+@pytest.mark.parametrize("name", ["decode1", "decode4", "decode16", "decode_wide1", "decode_wide16"])
 def test_decode_full(name):
     w = WL.WORKLOADS[name]
     x, wt = WL.draw_x(w), WL.draw_w(w)
