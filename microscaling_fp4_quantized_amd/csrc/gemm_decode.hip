@@ -4,21 +4,27 @@
 // Quantization" (gist.science, German edition), Technische Zusammenfassung §2
 // "GPU-Kernel-Unterstützung (QuTLASS)": the 4-bit matmul of the online path,
 // here in its token-generation shape, where W (N x K codes + scales) is the only
-// large operand and the product is bound by HBM bandwidth on W.
+// large operand and the product is bound by reading W from HBM.
 //
-// Design for CDNA4:
-//  * One workgroup owns 16 output features (16 rows of W) and all of K; its 8 waves
-//    take batches of 4 consecutive 128-wide K steps round-robin and are reduced through
-//    LDS at the end, in a fixed order.
-//  * Each step is one v_mfma_scale_f32_16x16x128_f8f6f4 with W as the row operand and
-//    X as the column operand: lane l carries row l % 16 and the 32-element group l / 16
-//    of the step (16 bytes of codes, one E8M0 byte), so the output fragment gives each
-//    lane 4 consecutive features of one token.
-//  * Every load of a wave's batch is issued before its first MFMA (4 steps, 4 KB of W per
-//    wave, 32 KB per workgroup in flight), so the whole of W is requested at once for
-//    K <= 4096 and the kernel runs at the HBM rate instead of the MFMA rate. A batch's
-//    scales are 16 consecutive bytes of the row, read with one 16-byte load. X rows past M repeat row M-1
-//    (their outputs are discarded); W rows past N repeat row N-1 likewise.
+// Design for CDNA4 (measured on MI355X with W streamed from HBM):
+//  * One workgroup owns T tiles of 16 output features (16 rows of W each) and all of K. Its
+//    8 waves read each tile as whole 1 KB pieces of contiguous W bytes (one 16-byte load per
+//    lane), the pattern a plain HBM stream uses: loading W straight in the MFMA operand layout
+//    touches 16 rows x 64 bytes per instruction and streamed about 20% slower.
+//  * The loaded pieces go to LDS with 16-byte chunk c of row r stored at slot c ^ (r & 15) of its
+//    256-byte segment, so the MFMA reads of 16 rows (one chunk each) hit distinct banks. One
+//    workgroup barrier, then each wave multiplies its slice of K (4 steps of 128) with
+//    v_mfma_scale_f32_16x16x128_f8f6f4, W as the row operand and X as the column operand: lane l
+//    carries row l % 16 and the 32-element group l / 16 of the step (16 bytes of codes, one E8M0
+//    byte), so the output fragment gives each lane 4 consecutive features of one token. X (a few
+//    rows, resident in L2) is read per lane in that layout.
+//  * K is staged in chunks of at most 4096 elements; the next chunk's loads are in flight while
+//    the current one is multiplied. The waves' partial sums are reduced through LDS in a fixed
+//    order.
+//  * T = 2 when there are at least three tiles per CU: the two tiles share every X fragment the
+//    wave loads, which halves the X traffic that dominates at 16 tokens, and the half-size grid is
+//    resident at once (two workgroups per CU).
+//  X rows past M repeat row M-1 and W rows past N repeat row N-1; their outputs are discarded.
 #include <atomic>
 
 #include "quant_device.hpp"
@@ -28,7 +34,8 @@ namespace {
 
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * 64;
-constexpr int kDecBatch = 4;  // consecutive K steps per wave kept in flight
+constexpr int kDecBatch = 4;     // consecutive K steps of 128 per wave within a chunk
+constexpr int kDecMaxKC = 4096;  // K elements of a W chunk staged in LDS
 
 // Y[m][n .. n+3] = acc (four consecutive features of token m), bounds-checked.
 template <bool OUT_BF16>
@@ -57,64 +64,163 @@ __device__ __forceinline__ void store_out(void* __restrict__ Yv, int M, int N, i
   }
 }
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(kDecThreads) void gemm_mxfp4_decode(const uint8_t* __restrict__ Xq,
-                                                                 const uint8_t* __restrict__ Xs,
-                                                                 const uint8_t* __restrict__ Wq,
-                                                                 const uint8_t* __restrict__ Ws,
-                                                                 void* __restrict__ Yv, int M, int N, int K) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * 16;
-  const int r = lane & 15, g = lane >> 4;
-  const size_t KB = (size_t)K / 2, KS = (size_t)K / 32;
-  const int steps = K / 128;  // 128-element steps; step t, lane group g: group 4t + g of the row
-  const uint8_t* wp = Wq + (size_t)min(n0 + r, N - 1) * KB + 16 * g;
-  const uint8_t* xp = Xq + (size_t)min(r, M - 1) * KB + 16 * g;
-  const uint8_t* wsp = Ws + (size_t)min(n0 + r, N - 1) * KS;
-  const uint8_t* xsp = Xs + (size_t)min(r, M - 1) * KS;
-  const unsigned sh = 8u * (unsigned)g;
+// Raw buffer resource over [base, base + bytes): stride 0, last word 0x00020000 (32-bit data
+// format in the gfx9-family descriptor layout, which untyped loads need). Offsets at or past
+// `bytes` read as zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const uint8_t* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
+}
 
-  // the waves take consecutive batches of kDecBatch steps, round-robin over K
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  for (int t0 = wave * kDecBatch; t0 < steps; t0 += kDecWaves * kDecBatch) {
-    v4u wa[kDecBatch], xb[kDecBatch];
+// LDS bytes of one tile chunk of KC elements: 16 rows of KC/2 code bytes, then 16 rows of KC/32 scale bytes.
+__host__ __device__ constexpr int dec_tile_bytes(int kc) { return 16 * (kc / 2) + 16 * (kc / 32); }
+
+// Chunk size: the largest multiple of 512 that divides K and is at most kDecMaxKC.
+inline int dec_chunk(int64_t K) {
+  int d = kDecMaxKC / 512;
+  while ((K / 512) % d) --d;
+  return 512 * d;
+}
+
+// W of the workgroup's T tiles for one chunk of KC elements, on its way from HBM to LDS. Piece
+// p = wave + 8 j (1 KB) of a tile chunk: lane -> 16-byte slot p * 64 + lane, which holds global
+// chunk (slot-in-row) ^ (row & 15) of its row; the first KC/32 threads also carry 16 scale bytes
+// each. Buffer loads over each tile's rows (32-bit offsets; rows past N read as zero, and their
+// outputs are discarded).
+template <int T>
+struct DecodeW {
+  v4u wr[T][4], sr[T];
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Ws, int N, int K,
+                                       int KC, int nb, int ch, int wave, int lane) {
+    const unsigned KB = (unsigned)K / 2, KS = (unsigned)K / 32;
+    const int cb = KC / 2, cs = KC / 32, pieces = KC / 128;
 #pragma unroll
-    for (int u = 0; u < kDecBatch; ++u) {
-      const int t = min(t0 + u, steps - 1);  // in bounds; unused steps are skipped below
-      wa[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wp + 64 * (size_t)t));
-      xb[u] = *reinterpret_cast<const v4u*>(xp + 64 * (size_t)t);
-    }
-    // the batch's scale bytes 4 t0 .. 4 t0 + 15 of the row (steps % 4 == 0 keeps them in the row)
-    const int tb = min(t0, steps - kDecBatch);
-    const v4u wsv = *reinterpret_cast<const v4u*>(wsp + 4 * (size_t)tb);
-    const v4u xsv = *reinterpret_cast<const v4u*>(xsp + 4 * (size_t)tb);
+    for (int tt = 0; tt < T; ++tt) {
+      const int n0 = __builtin_amdgcn_readfirstlane(min(nb + 16 * tt, N - 1));
+      const unsigned rows = (unsigned)__builtin_amdgcn_readfirstlane(min(16, N - n0));
+      const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(Wq + (size_t)n0 * KB, rows * KB);
 #pragma unroll
-    for (int u = 0; u < kDecBatch; ++u) {
-      if (t0 + u < steps) {  // wave-uniform
-        const v8i a = v8i{(int)wa[u][0], (int)wa[u][1], (int)wa[u][2], (int)wa[u][3], 0, 0, 0, 0};
-        const v8i b = v8i{(int)xb[u][0], (int)xb[u][1], (int)xb[u][2], (int)xb[u][3], 0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 4, 0, (int)(wsv[u] >> sh), 0,
-                                                                (int)(xsv[u] >> sh));
+      for (int j = 0; j < 4; ++j) {
+        const int p = wave + 8 * j;
+        if (p < pieces) {  // wave-uniform
+          const int slot = p * 64 + lane, row = slot / (cb / 16), sl = slot % (cb / 16);
+          wr[tt][j] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
+              rw, (int)((unsigned)row * KB + (unsigned)(ch * cb + 16 * (sl ^ (row & 15)))), 0, 0));
+        }
+      }
+      if ((int)threadIdx.x < cs) {
+        const int row = (int)threadIdx.x / (cs / 16), c16 = (int)threadIdx.x % (cs / 16);
+        const int n = min(n0 + row, N - 1);
+        sr[tt] = *reinterpret_cast<const v4u*>(Ws + (size_t)n * KS + (size_t)ch * cs + 16 * c16);
       }
     }
   }
 
-  // fixed-order reduction over the waves' K slices
-  __shared__ v4f red[kDecWaves][64];
-  red[wave][lane] = acc;
-  __syncthreads();
-  if (wave != 0) return;
+  // tile tt's chunk at lds + tt * dec_tile_bytes(KC): 16 code rows of KC/2 bytes, then 16 scale rows
+  __device__ __forceinline__ void store(uint8_t* lds, int KC, int wave, int lane) const {
+    const int cb = KC / 2, cs = KC / 32, pieces = KC / 128, tile = dec_tile_bytes(KC);
 #pragma unroll
-  for (int w = 1; w < kDecWaves; ++w) acc += red[w][lane];
-  // lane holds D[n0 + 4g + i][m = r], i = 0..3: four consecutive features of token r
-  store_out<OUT_BF16>(Yv, M, N, r, n0 + 4 * g, acc);
+    for (int tt = 0; tt < T; ++tt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (wave + 8 * j < pieces) *reinterpret_cast<v4u*>(lds + tt * tile + (wave + 8 * j) * 1024 + lane * 16) = wr[tt][j];
+      if ((int)threadIdx.x < cs) {
+        const int row = (int)threadIdx.x / (cs / 16), c16 = (int)threadIdx.x % (cs / 16);
+        *reinterpret_cast<v4u*>(lds + tt * tile + 16 * cb + row * cs + 16 * c16) = sr[tt];
+      }
+    }
+  }
+};
+
+// This wave's 4 steps of one chunk for each tile: v_mfma_scale_f32_16x16x128_f8f6f4 with W (from LDS)
+// as the row operand: lane l carries row r = l % 16 and the 32-element group g = l / 16 of the step
+// (16 bytes of codes, one E8M0 byte); X fragments xb and scale dwords xsv as the column operand.
+template <int T>
+__device__ __forceinline__ void decode_chunk_mfma(const uint8_t* lds, int KC, int s0, int r, int g, const v4u (&xb)[kDecBatch],
+                                                  v4u xsv, v4f (&acc)[T]) {
+  const int cb = KC / 2, cs = KC / 32, tile = dec_tile_bytes(KC);
+  const unsigned sh = 8u * (unsigned)g;
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) {
+    const uint8_t* tl = lds + tt * tile;
+    const v4u wsv = *reinterpret_cast<const v4u*>(tl + 16 * cb + r * cs + 4 * s0);
+#pragma unroll
+    for (int u = 0; u < kDecBatch; ++u) {
+      const int c = 4 * (s0 + u) + g;  // 16-byte chunk of the row = 32-element group
+      const v4u w = *reinterpret_cast<const v4u*>(tl + r * cb + 16 * (c ^ r));
+      const v8i a = v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+      const v8i b = v8i{(int)xb[u][0], (int)xb[u][1], (int)xb[u][2], (int)xb[u][3], 0, 0, 0, 0};
+      acc[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[tt], 4, 4, 0, (int)(wsv[u] >> sh), 0,
+                                                                  (int)(xsv[u] >> sh));
+    }
+  }
+}
+
+// Fixed-order reduction of the waves' partial sums through LDS (8 KB per tile at lds), then store.
+template <bool OUT_BF16, int T>
+__device__ __forceinline__ void decode_reduce_store(uint8_t* lds, const v4f (&acc)[T], int wave, int lane, void* Yv,
+                                                    int M, int N, int nb) {
+  __syncthreads();
+  v4f* red = reinterpret_cast<v4f*>(lds);
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) red[(tt * kDecWaves + wave) * 64 + lane] = acc[tt];
+  __syncthreads();
+  if (wave >= T) return;
+  const int tt = wave;
+  v4f sum = red[(tt * kDecWaves) * 64 + lane];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) sum += red[(tt * kDecWaves + w) * 64 + lane];
+  // lane holds D[n + 4g + i][m = r], i = 0..3: four consecutive features of token r
+  store_out<OUT_BF16>(Yv, M, N, lane & 15, nb + 16 * tt + 4 * (lane >> 4), sum);
+}
+
+// At most 128 VGPRs (4 waves per SIMD), so that two workgroups share a CU.
+template <bool OUT_BF16, int T>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemm_mxfp4_decode(
+    const uint8_t* __restrict__ Xq, const uint8_t* __restrict__ Xs, const uint8_t* __restrict__ Wq,
+    const uint8_t* __restrict__ Ws, void* __restrict__ Yv, int M, int N, int K, int KC) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const size_t KB = (size_t)K / 2, KS = (size_t)K / 32;
+  const int cb = KC / 2, cs = KC / 32;
+  const int nch = K / KC, steps = KC / 128;
+  const int nb = blockIdx.x * 16 * T;
+  const uint8_t* xp = Xq + (size_t)min(r, M - 1) * KB + 16 * g;
+  const uint8_t* xsp = Xs + (size_t)min(r, M - 1) * KS;
+  const int s0 = wave * kDecBatch;  // this wave's first K step within a chunk (steps % 4 == 0)
+
+  DecodeW<T> w;
+  v4f acc[T];
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) acc[tt] = v4f{0.f, 0.f, 0.f, 0.f};
+  w.load(Wq, Ws, N, K, KC, nb, 0, wave, lane);
+  for (int ch = 0; ch < nch; ++ch) {
+    // this wave's X fragments of the chunk (a wave past the last step loads clamped ones it does not use)
+    v4u xb[kDecBatch];
+    const uint8_t* xc = xp + (size_t)ch * cb;
+#pragma unroll
+    for (int u = 0; u < kDecBatch; ++u) xb[u] = *reinterpret_cast<const v4u*>(xc + 64 * (size_t)min(s0 + u, steps - 1));
+    const v4u xsv = *reinterpret_cast<const v4u*>(xsp + (size_t)ch * cs + 4 * (size_t)min(s0, steps - kDecBatch));
+    if (ch > 0) __syncthreads();  // every wave is done reading the previous chunk
+    w.store(lds, KC, wave, lane);
+    __syncthreads();
+    if (ch + 1 < nch) w.load(Wq, Ws, N, K, KC, nb, ch + 1, wave, lane);  // in flight during this chunk
+    if (s0 < steps) decode_chunk_mfma<T>(lds, KC, s0, r, g, xb, xsv, acc);
+  }
+  decode_reduce_store<OUT_BF16, T>(lds, acc, wave, lane, Yv, M, N, nb);
 }
 
 // ---------------------------------------------------------------------------
 // Fused decode step: every workgroup first rotates and quantizes the (tiny) bf16 X into LDS
 // with the same device code as fp4_rotate_quantize (so the codes are the same bits), then
-// runs the decode product above with its X fragments read from LDS. One launch instead of
-// two; X (M <= 16 rows) is read from L2 by every workgroup.
+// multiplies 16 rows of W with its X fragments read from LDS. One launch instead of two; X
+// (M <= 16 rows) is read from L2 by every workgroup. W is read straight into registers in the
+// MFMA operand layout (lane l: row l % 16, 16 bytes of the 32-element group l / 16 of a 128-wide
+// K step), each wave taking batches of 4 steps round-robin over K; the first batch and its scales
+// are requested before X is quantized, so their HBM latency overlaps the quantization. (Staging W
+// through LDS in coalesced pieces, as gemm_mxfp4_decode does, measured slower here at one token:
+// the extra LDS pass and barrier fall after the quantization, on the critical path.)
 // ---------------------------------------------------------------------------
 template <int B, bool OUT_BF16>
 __global__ __launch_bounds__(kDecThreads) void decode_fused(const uint16_t* __restrict__ X, int64_t ldx,
@@ -126,6 +232,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_fused(const uint16_t* __re
   uint8_t* xq = lds;                                   // [M][pitch]
   uint8_t* xs = lds + (size_t)M * pitch;               // [M][KS]
   const int total = M * KS;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int r = lane & 15, g = lane >> 4;
+  const int steps = K / 128;
+  const uint8_t* wp = Wq + (size_t)min(n0 + r, N - 1) * KB + 16 * g;
+  const uint8_t* wsp = Ws + (size_t)min(n0 + r, N - 1) * KS;
+  // a batch of W: steps t0 .. t0 + 3 (clamped into the row; the MFMA loop skips steps past the end)
+  v4u wa[kDecBatch], wsv;
+  auto load_w = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < kDecBatch; ++u)
+      wa[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wp + 64 * (size_t)min(t0 + u, steps - 1)));
+    wsv = *reinterpret_cast<const v4u*>(wsp + 4 * (size_t)min(t0, steps - kDecBatch));
+  };
+  load_w(wave * kDecBatch);
 
   // phase 1: chunk c -> row c / KS, chunk c % KS. Quads of lanes hold the consecutive chunks of
   // one Hadamard block (KS % 16 == 0, and the loop base is a multiple of 512), and whole quads
@@ -138,11 +259,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_fused(const uint16_t* __re
       float v[32];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const v4u w = src[q];
+        const v4u x4 = src[q];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          v[8 * q + 2 * t] = bf16_lo(w[t]);
-          v[8 * q + 2 * t + 1] = bf16_hi(w[t]);
+          v[8 * q + 2 * t] = bf16_lo(x4[t]);
+          v[8 * q + 2 * t + 1] = bf16_hi(x4[t]);
         }
       }
       v4u out;
@@ -153,49 +274,35 @@ __global__ __launch_bounds__(kDecThreads) void decode_fused(const uint16_t* __re
   }
   __syncthreads();
 
-  // phase 2: the decode product (see gemm_mxfp4_decode) with X from LDS
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * 16;
-  const int r = lane & 15, g = lane >> 4;
-  const int steps = K / 128;
-  const uint8_t* wp = Wq + (size_t)min(n0 + r, N - 1) * KB + 16 * g;
-  const uint8_t* wsp = Ws + (size_t)min(n0 + r, N - 1) * KS;
+  // phase 2: v_mfma_scale_f32_16x16x128_f8f6f4 with W as the row operand, X from LDS
   const uint8_t* xp = xq + (size_t)min(r, M - 1) * pitch + 16 * g;
   const uint8_t* xsp = xs + (size_t)min(r, M - 1) * KS;
   const unsigned sh = 8u * (unsigned)g;
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  v4f acc[1] = {v4f{0.f, 0.f, 0.f, 0.f}};
   for (int t0 = wave * kDecBatch; t0 < steps; t0 += kDecWaves * kDecBatch) {
-    v4u wa[kDecBatch], xb[kDecBatch];
+    if (t0 != wave * kDecBatch) load_w(t0);  // the first batch is already in flight
+    v4u xb[kDecBatch];
 #pragma unroll
-    for (int u = 0; u < kDecBatch; ++u) {
-      const int t = min(t0 + u, steps - 1);
-      wa[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wp + 64 * (size_t)t));
-      xb[u] = *reinterpret_cast<const v4u*>(xp + 64 * t);
-    }
-    const int tb = min(t0, steps - kDecBatch);
-    const v4u wsv = *reinterpret_cast<const v4u*>(wsp + 4 * (size_t)tb);
-    const v4u xsv = *reinterpret_cast<const v4u*>(xsp + 4 * tb);
+    for (int u = 0; u < kDecBatch; ++u) xb[u] = *reinterpret_cast<const v4u*>(xp + 64 * min(t0 + u, steps - 1));
+    const v4u xsv = *reinterpret_cast<const v4u*>(xsp + 4 * min(t0, steps - kDecBatch));
 #pragma unroll
     for (int u = 0; u < kDecBatch; ++u) {
       if (t0 + u < steps) {
         const v8i a = v8i{(int)wa[u][0], (int)wa[u][1], (int)wa[u][2], (int)wa[u][3], 0, 0, 0, 0};
         const v8i b = v8i{(int)xb[u][0], (int)xb[u][1], (int)xb[u][2], (int)xb[u][3], 0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 4, 0, (int)(wsv[u] >> sh), 0,
-                                                                (int)(xsv[u] >> sh));
+        acc[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[0], 4, 4, 0, (int)(wsv[u] >> sh), 0,
+                                                                   (int)(xsv[u] >> sh));
       }
     }
   }
-  v4f* red = reinterpret_cast<v4f*>(lds);  // X in LDS is no longer read after this barrier
-  __syncthreads();
-  red[wave * 64 + lane] = acc;
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int w = 1; w < kDecWaves; ++w) acc += red[w * 64 + lane];
-  store_out<OUT_BF16>(Yv, M, N, r, n0 + 4 * g, acc);
+  decode_reduce_store<OUT_BF16, 1>(lds, acc, wave, lane, Yv, M, N, n0);  // X in LDS is dead after its first barrier
 }
 
-size_t fused_lds_bytes(int M, int K) { return (size_t)M * (K / 2 + 16) + (size_t)M * (K / 32); }
+// X codes and scales; at least the 8 KB the reduction reuses
+size_t fused_lds_bytes(int M, int K) {
+  const size_t x = (size_t)M * (K / 2 + 16) + (size_t)M * (K / 32);
+  return x > (size_t)kDecWaves * 64 * 16 ? x : (size_t)kDecWaves * 64 * 16;
+}
 
 std::atomic<int> g_fused_attr[4][64];
 
@@ -207,31 +314,71 @@ hipError_t launch_fused(const uint16_t* X, int64_t ldx, const uint8_t* Wq, const
   if (e != hipSuccess) return e;
   auto kern = out_bf16 ? decode_fused<B, true> : decode_fused<B, false>;
   const int bi = B == 16 ? 0 : B == 32 ? 1 : B == 64 ? 2 : 3;
-  const size_t lds = fused_lds_bytes(M, K) > (size_t)kDecWaves * 64 * 16 ? fused_lds_bytes(M, K)
-                                                                         : (size_t)kDecWaves * 64 * 16;
   const bool cached = dev >= 0 && dev < 64;
   if (!cached || (g_fused_attr[bi][dev].load(std::memory_order_acquire) & (1 + out_bf16)) == 0) {
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     if (cached) g_fused_attr[bi][dev].fetch_or(1 + out_bf16, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)((N + 15) / 16)), dim3(kDecThreads), lds, st, X, ldx, Wq, Ws, Y, M, N, K);
+  hipLaunchKernelGGL(kern, dim3((unsigned)((N + 15) / 16)), dim3(kDecThreads), fused_lds_bytes(M, K), st, X, ldx, Wq, Ws,
+                     Y, M, N, K);
   return hipGetLastError();
 }
 
 }  // namespace
 }  // namespace fp4
 
-bool fp4_gemm_mxfp4_decode_fits(int64_t M, int64_t N, int64_t K) { return M <= 16 && K % 512 == 0 && N >= 1; }
+// 16 rows of W and their 32-bit buffer offsets: 16 * K / 2 < 2^32
+bool fp4_gemm_mxfp4_decode_fits(int64_t M, int64_t N, int64_t K) {
+  return M <= 16 && K % 512 == 0 && N >= 1 && K < ((int64_t)1 << 28);
+}
+
+namespace fp4 {
+namespace {
+std::atomic<int> g_dec_attr[2][2][64];  // per output dtype, T and device: dynamic-LDS limit raised
+std::atomic<int> g_dec_cus[64];         // compute units per device, 0 until queried
+
+template <bool OUT_BF16, int T>
+hipError_t launch_decode(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws, int M, int N, int K,
+                         int KC, void* Y, int dev, hipStream_t st) {
+  auto kern = gemm_mxfp4_decode<OUT_BF16, T>;
+  const int lds = T * (dec_tile_bytes(KC) > kDecWaves * 64 * 16 ? dec_tile_bytes(KC) : kDecWaves * 64 * 16);
+  const bool cached = dev >= 0 && dev < 64;
+  if (!cached || !g_dec_attr[OUT_BF16][T - 1][dev].load(std::memory_order_acquire)) {
+    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    if (cached) g_dec_attr[OUT_BF16][T - 1][dev].store(1, std::memory_order_release);
+  }
+  const int tiles = (N + 15) / 16;
+  hipLaunchKernelGGL(kern, dim3((unsigned)((tiles + T - 1) / T)), dim3(kDecThreads), lds, st, Xq, Xs, Wq, Ws, Y, M, N, K,
+                     KC);
+  return hipGetLastError();
+}
+}  // namespace
+}  // namespace fp4
 
 hipError_t fp4_launch_gemm_mxfp4_decode(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
                                         int64_t M, int64_t N, int64_t K, void* Y, int out_bf16, hipStream_t st) {
-  const dim3 grid((unsigned)((N + 15) / 16)), block(fp4::kDecThreads);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < 64;
+  int cus = cached ? fp4::g_dec_cus[dev].load(std::memory_order_acquire) : 0;
+  if (cus == 0) {
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (cached) fp4::g_dec_cus[dev].store(cus, std::memory_order_release);
+  }
+  const int KC = fp4::dec_chunk(K);
+  // two tiles per workgroup once there are at least three tiles per CU: the tiles share the X
+  // fragments, and every workgroup is resident at once (two per CU at up to 128 VGPRs)
+  const bool two = (N + 15) / 16 >= 3 * (int64_t)cus;
+  const int m = (int)M, n = (int)N, k = (int)K;
   if (out_bf16)
-    hipLaunchKernelGGL(fp4::gemm_mxfp4_decode<true>, grid, block, 0, st, Xq, Xs, Wq, Ws, Y, (int)M, (int)N, (int)K);
-  else
-    hipLaunchKernelGGL(fp4::gemm_mxfp4_decode<false>, grid, block, 0, st, Xq, Xs, Wq, Ws, Y, (int)M, (int)N, (int)K);
-  return hipGetLastError();
+    return two ? fp4::launch_decode<true, 2>(Xq, Xs, Wq, Ws, m, n, k, KC, Y, dev, st)
+               : fp4::launch_decode<true, 1>(Xq, Xs, Wq, Ws, m, n, k, KC, Y, dev, st);
+  return two ? fp4::launch_decode<false, 2>(Xq, Xs, Wq, Ws, m, n, k, KC, Y, dev, st)
+             : fp4::launch_decode<false, 1>(Xq, Xs, Wq, Ws, m, n, k, KC, Y, dev, st);
 }
 
 bool fp4_decode_fused_fits(int64_t M, int64_t N, int64_t K) {

@@ -19,6 +19,7 @@ name       X (bf16)                                                     W
 =========  ==========================================================  =====
 tiny       16x256 N(0,1), 4 outlier channels x50                        256x256 N(0,0.02)
 decode     M in {1,4,16} x 4096, Student-t(5), 1% channels x30           4096x4096 N(0,0.02)
+           (decode_wide: the same X against W 14336x4096)
 prefill    2048x4096, Student-t(5), 1% channels x30                      14336x4096 N(0,0.02)
            (NVFP4 block 16 as stated; also run in MXFP4 block 32, Y bf16)
 large      8192x8192 N(0,1), 0.5% channels x100                          28672x8192 N(0,0.02)
@@ -92,6 +93,10 @@ WORKLOADS = {
                            out_dtype="bf16"),
     "prefill_mx_m4096": Workload("prefill_mx_m4096", 7, 4096, 4096, 14336, 32, "mxfp4", "t5",
                                  0.01, 30.0, out_dtype="bf16"),
+    # decode against the wider projection of the prefill layer (W 14336 x 4096, 31 MB of MXFP4)
+    "decode_wide1": Workload("decode_wide1", 8, 1, 4096, 14336, 32, "mxfp4", "t5", 0.01, 30.0),
+    "decode_wide4": Workload("decode_wide4", 8, 4, 4096, 14336, 32, "mxfp4", "t5", 0.01, 30.0),
+    "decode_wide16": Workload("decode_wide16", 8, 16, 4096, 14336, 32, "mxfp4", "t5", 0.01, 30.0),
     "large": Workload("large", 4, 8192, 8192, 28672, 128, "mxfp4", "normal", 0.005, 100.0),
     "stress_mx32": Workload("stress_mx32", 5, 16384, 8192, 0, 32, "mxfp4", "t3_lognormal", 0, 1.0),
     "stress_mx128": Workload("stress_mx128", 5, 16384, 8192, 0, 128, "mxfp4", "t3_lognormal", 0, 1.0),
