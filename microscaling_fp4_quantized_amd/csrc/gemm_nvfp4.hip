@@ -181,7 +181,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_nvfp4_kernel(
 hipError_t fp4_launch_gemm_nvfp4(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts,
                                  const uint8_t* Wq, const uint8_t* Ws, const float* w_ts, int64_t M,
                                  int64_t N, int64_t K, void* Y, int out_bf16, hipStream_t st) {
-  if (fp4_gemm_nvfp4_ring_fits(M, N, K))
+  // The large-tile kernel reads 16 scale bytes of a row at a time, which needs scale pointers
+  // aligned to 16 bytes (K % 256 == 0 keeps every row aligned then); the general kernel below
+  // reads 2-byte pieces.
+  const bool scales16 = ((reinterpret_cast<uintptr_t>(Xs) | reinterpret_cast<uintptr_t>(Ws)) & 15) == 0;
+  if (scales16 && fp4_gemm_nvfp4_ring_fits(M, N, K))
     return fp4_launch_gemm_nvfp4_ring(Xq, Xs, x_ts, Wq, Ws, w_ts, M, N, K, Y, out_bf16, st);
   constexpr int BM = 128, BN = 128, WM = 64, WN = 64;
   using C = fp4::NvCfg<BM, BN, WM, WN>;

@@ -8,23 +8,31 @@
 // NVFP4 group scale (E4M3, 16 elements) is folded into the operand instead: e2m1 * d
 // has at most 6 significant bits and lies in [2^-10, 2688], so it is exact in fp16, and
 // the product runs on v_mfma_f32_32x32x16_f16 with float32 accumulation. The two
-// tensor scales multiply the result in the epilogue. fp16 rather than bf16 (the products
-// are exact in both): one packed convert and one packed multiply make two operands.
+// tensor scales multiply the result in the epilogue.
 //
 // Design for CDNA4:
-//  * 8 waves (2 x 4), 128 x 64 outputs per wave as 4 x 2 fragments of 32 x 32.
-//  * K advances 64 per stage. The codes (16 bytes = 32 elements + their two scale bytes
-//    per thread and chunk) are loaded into registers two stages ahead; after stage s is
-//    multiplied, stage s+1 is dequantized once per workgroup into an fp16 tile in the
-//    other LDS buffer (pitch 144 bytes: the fragment reads hit distinct banks).
-//  * W is the row operand and X the column operand of every MFMA, so each lane ends with
-//    four consecutive output features of one token: one 16-byte LDS write when the output
-//    tile is staged for whole-row 16-byte stores of Y.
+//  * Codes and scales stay 4- and 8-bit in LDS. K advances 256 per stage; a 2-deep ring
+//    (144 KB) is filled by LDS DMA (buffer_load_dwordx4 ... lds) as in the MXFP4 kernel:
+//    16-byte chunks of a row XOR-swizzled so the 32 rows of a fragment read hit distinct
+//    banks, the 16 E4M3 bytes of each row and stage in their own buffer, one barrier per
+//    stage, the DMA of stage s+1 issued in four parts across the k-blocks of stage s.
+//  * Each wave reads its fragments as 16 bytes (32 codes of one row) per lane and
+//    dequantizes them in registers right before the MFMAs: one packed convert per code
+//    byte (v_cvt_scalef32_pk_f16_fp4, scale 256) and one packed multiply by the group
+//    scale d * 2^-8 as fp16 (the E4M3 magnitude bits shifted left by 7 are exactly that
+//    fp16 pattern, subnormals included; the sign goes to bit 15).
+//  * K order within a 64-element block: lane half h holds elements 32h .. 32h + 31, and
+//    MFMA k-step j takes elements 32h + 8j .. + 7 from lane half h, for both operands. Every
+//    product still pairs x_k with w_k, and the block's sum is unchanged up to the order of
+//    the float32 additions, which the MFMA does not fix in any case.
+//  * 8 waves (2 x 4), 128 x 64 outputs per wave as 4 x 2 fragments of 32 x 32; W is the row
+//    operand and X the column operand of every MFMA, so each lane ends with four consecutive
+//    output features of one token, staged through LDS for whole-row 16-byte stores of Y.
 //  * Workgroup i runs on XCD i % 8; each XCD takes a contiguous range of tiles, walked
-//    M-fastest within groups of 8 tile rows.
-//  * Two tile widths in one launch, as in the MXFP4 kernel: when 256x256 tiles would leave
-//    the last round part-filled, the columns after whole rounds of them are covered by
-//    256x192 tiles (4 x 2 waves of 64 x 96).
+//    M-fastest within groups of 8 tile rows. Two tile widths in one launch, as in the MXFP4
+//    kernel: when 256x256 tiles would leave the last round part-filled, the columns after
+//    whole rounds of them are covered by 256x192 tiles (4 x 2 waves of 64 x 96).
+// Requires K % 256 == 0 and K < 2^25 (32-bit buffer offsets); other shapes use the general kernel.
 #include <atomic>
 #include <type_traits>
 
@@ -33,55 +41,83 @@
 namespace fp4 {
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void;
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
-constexpr int BM = 256;                       // tile rows (both widths)
+constexpr int BM = 256;                  // tile rows (both widths)
 constexpr int WAVES = 8, NT = WAVES * 64;
-constexpr int BKE = 64;                       // K elements per stage
-constexpr int KSTEPS = BKE / 16;              // 32x32x16 steps per stage
-constexpr int PITCH = BKE * 2 + 16;           // bytes per fp16 row in LDS (padded)
-constexpr int LDS_BYTES = 2 * (BM + 256) * PITCH;  // sized for the wide tile: 144 KB
+constexpr int BKB = 128;                 // code bytes of a row per stage (256 elements)
+constexpr int SCB = 16;                  // E4M3 bytes of a row per stage (16 groups of 16)
+constexpr int KBLK = 4;                  // 64-element blocks per stage (one DMA part each)
+constexpr int NS = 2;                    // ring depth
+constexpr int LDS_BYTES = NS * (BM + 256) * (BKB + SCB);  // sized for the wide tile: 144 KB
 
 // One tile shape: BN columns, WGM x WGN waves.
 template <int BN_, int WGM_, int WGN_>
 struct Tile {
   static constexpr int BN = BN_, WGM = WGM_, WGN = WGN_;
   static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
-  static constexpr int STAGE = (BM + BN) * PITCH;
-  static constexpr int EP = WN * 4 + 16;  // epilogue staging row pitch (bytes): 16 rows hit distinct banks
-  static constexpr int CHUNKS = (BM + BN) * 2;         // 32-element chunks per stage
-  static constexpr int CPT = (CHUNKS + NT - 1) / NT;   // chunks per thread (the last round may be partial)
+  static constexpr int STAGE = (BM + BN) * BKB;                   // codes of one stage
+  static constexpr int SC = (BM + BN) * SCB;                      // scales of one stage
+  static constexpr int A_WL = BM / 8 / WAVES, B_WL = BN / 8 / WAVES;  // 1 KB code wave-loads per wave
+  static constexpr int SC_LOADS = (BM + BN) / 64;                 // 64-row scale wave-loads
+  static constexpr int SC_WL = (SC_LOADS + WAVES - 1) / WAVES;
+  static constexpr int EP = WN * 4 + 16;                          // epilogue row pitch (bytes)
   static_assert(WGM * WGN == WAVES, "wave layout");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "whole 32x32 fragments");
-  static_assert(CHUNKS % 64 == 0, "whole waves per chunk round");
-  static_assert(2 * STAGE <= LDS_BYTES, "two stages fit");
+  static_assert(A_WL * 8 * WAVES == BM && B_WL * 8 * WAVES == BN, "row split");
+  static_assert(SC_LOADS * 64 == BM + BN, "scale split");
+  static_assert(NS * (STAGE + SC) <= LDS_BYTES, "ring fits");
   static_assert(WAVES * 32 * EP <= LDS_BYTES, "epilogue staging fits");
 };
 using Wide = Tile<256, 2, 4>;
 using Narrow = Tile<192, 4, 2>;
 constexpr float kNvNarrowCost = 0.84f;  // measured time of a 256x192 tile over a 256x256 one
 
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+}
 
-// 32 E2M1 codes (16 bytes) with their two E4M3 group scales (low byte first) -> 32 exact fp16
-// (64 bytes). The E4M3 code's seven magnitude bits, shifted left by 7, are the fp16 bit
-// pattern of d * 2^-8 (the E4M3 exponent bias is 7, fp16's is 15; E4M3 subnormals land on
-// fp16 subnormals, exactly), and the sign goes to bit 15. The packed convert's power-of-two
-// scale 256 restores the factor: (e2m1 * 256) * (d * 2^-8) = e2m1 * d, exact in fp16.
-__device__ __forceinline__ void dequant32(const v4u codes, unsigned sc2, v4u out[4]) {
-  const unsigned lo = ((sc2 & 0x7Fu) << 7) | ((sc2 & 0x80u) << 8);
-  const unsigned hi = ((sc2 & 0x7F00u) >> 1) | (sc2 & 0x8000u);
-  const h2 dd0 = __builtin_bit_cast(h2, lo | (lo << 16)), dd1 = __builtin_bit_cast(h2, hi | (hi << 16));
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const h2 dd = w < 2 ? dd0 : dd1;  // words 0-1 are the first 16 elements (group 2c), 2-3 the second
-    // byte q of the word holds elements 2q (low nibble) and 2q+1
-    out[w][0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[w], 256.0f, 0) * dd);
-    out[w][1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[w], 256.0f, 1) * dd);
-    out[w][2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[w], 256.0f, 2) * dd);
-    out[w][3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[w], 256.0f, 3) * dd);
-  }
+// Barrier of the LDS ring: wait for this wave's LDS reads (lgkmcnt(0)) but not for its
+// in-flight DMA loads, then synchronise the workgroup.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Raw buffer resource over [base, base + bytes): stride 0, last word 0x00020000 (32-bit data
+// format in the gfx9-family descriptor layout, which untyped loads need). Offsets at or past
+// `bytes` read as zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const uint8_t* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// Two E4M3 scale bytes (bits 0-7 and 8-15 of b) -> the fp16 pair (d0 * 2^-8, d1 * 2^-8): an E4M3
+// code's seven magnitude bits shifted left by 7 are the fp16 bit pattern of d * 2^-8 (E4M3's
+// exponent bias is 7, fp16's is 15; E4M3 subnormals land on fp16 subnormals), its sign goes to
+// bit 15. Both halves at once: the second byte moves up to bit 16 first.
+__device__ __forceinline__ h2 e4m3_pair2(unsigned b) {
+  const unsigned y = (b & 0xFFu) | ((b & 0xFF00u) << 8);
+  return __builtin_bit_cast(h2, ((y & 0x007F007Fu) << 7) | ((y & 0x00800080u) << 8));
+}
+
+// Eight E2M1 codes (one dword, element 2q in the low nibble of byte q) -> eight exact fp16
+// e2m1 * d: (e2m1 * 256) * (d * 2^-8).
+__device__ __forceinline__ v8h dequant8(unsigned codes, h2 dd) {
+  v4u o;
+  o[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * dd);
+  o[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * dd);
+  o[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * dd);
+  o[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * dd);
+  return __builtin_bit_cast(v8h, o);
 }
 
 // One output tile [m0, m0 + 256) x [n0, n0 + C::BN) over all of K.
@@ -91,54 +127,62 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
                                         const uint8_t* __restrict__ Ws, const float* __restrict__ w_ts,
                                         void* __restrict__ Yv, int M, int N, int K, int m0, int n0) {
   constexpr int WGN = C::WGN, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
-  constexpr int STAGE = C::STAGE, CHUNKS = C::CHUNKS, CPT = C::CPT;
+  constexpr int STAGE = C::STAGE, SC = C::SC, A_WL = C::A_WL, B_WL = C::B_WL, SC_WL = C::SC_WL;
+  uint8_t* scl = smem + NS * STAGE;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
-  const size_t KB = (size_t)K / 2, KS = (size_t)K / 16;
-  const int nst = K / BKE;
+  const int KB = K / 2, KS = K / 16;
+  const int nst = K / 256;
 
-  // chunk c of a stage: tile row c / 2 (A rows first, then B rows), half c % 2 of the row's 64
-  // elements. When CHUNKS is not a multiple of the thread count, the waves past the end of the
-  // last round (a whole number of waves) skip it; their clamped chunk keeps every address valid.
-  const uint8_t* csrc[CPT];
-  const uint8_t* ssrc[CPT];
-  int ldst[CPT];
-  unsigned shs[CPT];
+  // DMA sources: 8 rows x 128 bytes per code wave-load, 64 rows x 16 bytes per scale wave-load;
+  // rows past M / N repeat the last row. Buffer form: a wave-uniform resource at the tile's first
+  // row of each operand and a 32-bit per-lane offset (below 256 * K / 2 < 2^32: K < 2^25).
+  const int rows_a = min(M - m0, BM), rows_b = min(N - n0, C::BN);
+  const __amdgpu_buffer_rsrc_t rsA = buffer_rsrc(Xq + (size_t)m0 * KB, (unsigned)rows_a * KB);
+  const __amdgpu_buffer_rsrc_t rsB = buffer_rsrc(Wq + (size_t)n0 * KB, (unsigned)rows_b * KB);
+  const __amdgpu_buffer_rsrc_t rsXs = buffer_rsrc(Xs + (size_t)m0 * KS, (unsigned)rows_a * KS);
+  const __amdgpu_buffer_rsrc_t rsWs = buffer_rsrc(Ws + (size_t)n0 * KS, (unsigned)rows_b * KS);
+  unsigned offA[A_WL], offB[B_WL], offS[SC_WL];
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int c = min(tid + i * NT, CHUNKS - 1), r = c >> 1, h = c & 1;
-    const bool isA = r < BM;
-    const size_t row = isA ? (size_t)min(m0 + r, M - 1) : (size_t)min(n0 + r - BM, N - 1);
-    csrc[i] = (isA ? Xq : Wq) + row * KB + h * 16;
-    ssrc[i] = (isA ? Xs : Ws) + row * KS;  // the row's 4 scale bytes of a stage; this chunk's are 2h, 2h+1
-    ldst[i] = r * PITCH + h * 64;
-    shs[i] = 16 * h;
+  for (int i = 0; i < A_WL; ++i) {
+    const int r = (wave * A_WL + i) * 8 + (lane >> 3), q = lane & 7;
+    offA[i] = (unsigned)min(r, rows_a - 1) * KB + ((q ^ swz(r)) << 4);
   }
-  // two stages of codes in registers: stage s+2 is requested while stage s is multiplied
-  v4u cr[2][CPT];
-  unsigned sr[2][CPT];
-  // register set P holds the stages with parity P (the stage count is even, so the loop below
-  // is unrolled by two and every index into the register arrays is a constant)
-  // The loads are unconditional (a skipped chunk loads its clamped, valid address) and the
-  // scales come as whole dwords: a load under a branch, or a 16-bit load the compiler re-masks
-  // where the two register sets meet, makes it wait for loads issued just before.
-  auto gload = [&](auto P, int s) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      cr[P][i] = *reinterpret_cast<const v4u*>(csrc[i] + (size_t)s * (BKE / 2));
-      sr[P][i] = *reinterpret_cast<const unsigned*>(ssrc[i] + (size_t)s * (BKE / 16));
+  for (int i = 0; i < B_WL; ++i) {
+    const int r = (wave * B_WL + i) * 8 + (lane >> 3), q = lane & 7;
+    offB[i] = (unsigned)min(r, rows_b - 1) * KB + ((q ^ swz(r)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < SC_WL; ++i) {
+    const int rb = min(wave * SC_WL + i, C::SC_LOADS - 1) * 64;  // wave-uniform; waves past the last load skip
+    const int r = rb + lane;
+    offS[i] = rb < BM ? (unsigned)min(r, rows_a - 1) * KS : (unsigned)min(r - BM, rows_b - 1) * KS;
+  }
+
+  // Part p (0..KBLK-1) of the DMA of stage s: code wave-load i goes with part i % KBLK, and the
+  // stage's scales (16 bytes per row) with part 0.
+  auto issue_part = [&](int s, int p) {
+    if (p == 0) {
+      uint8_t* dst = scl + (s & 1) * SC;
+#pragma unroll
+      for (int i = 0; i < SC_WL; ++i)
+        if (wave * SC_WL + i < C::SC_LOADS)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds((wave * SC_WL + i) * 64 < BM ? rsXs : rsWs,
+                                                   (lds_void*)(dst + (wave * SC_WL + i) * 1024), 16,
+                                                   offS[i] + (unsigned)s * SCB, 0, 0, 0);
     }
-  };
-  auto lstore = [&](auto P) {  // dequantize register set P into LDS buffer P
+    uint8_t* buf = smem + (s & 1) * STAGE;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      if ((i + 1) * NT > CHUNKS && wave * 64 + i * NT >= CHUNKS) continue;  // wave-uniform
-      v4u o[4];
-      dequant32(cr[P][i], sr[P][i] >> shs[i], o);
-      v4u* dst = reinterpret_cast<v4u*>(smem + P * STAGE + ldst[i]);
+    for (int i = 0; i < A_WL; ++i)
+      if (i % KBLK == p)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(buf + (wave * A_WL + i) * 1024), 16,
+                                                 offA[i] + (unsigned)s * BKB, 0, 0, 0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dst[q] = o[q];
-    }
+    for (int i = 0; i < B_WL; ++i)
+      if (i % KBLK == p)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void*)(buf + BM * BKB + (wave * B_WL + i) * 1024), 16,
+                                                 offB[i] + (unsigned)s * BKB, 0, 0, 0);
   };
 
   v16f acc[FM][FN];
@@ -150,43 +194,66 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int fr = lane & 31, fh = lane >> 5;
-  auto stage = [&](auto P, int s) {  // multiply stage s (LDS buffer P = s & 1)
-    const uint8_t* buf = smem + P * STAGE;
-    // Register set P was stored to LDS before the last barrier. The prefetch and the store below
-    // run unconditionally (the stage index is clamped, and the last stage's extra store lands in
-    // a buffer nobody reads again) so the whole stage is one block in which the compiler can
-    // interleave the dequantization with the MFMAs.
-    gload(P, min(s + 2, nst - 1));
+  const unsigned sh = 16u * (unsigned)fh;  // lane half h uses scale bytes 2h, 2h + 1 of each block's dword
+
+  // Stage s: wait for its DMA (this wave's, then everyone's at the barrier), then multiply it
+  // while the parts of stage s+1 refill the buffers of stage s-1, which every wave has finished
+  // reading once past the barrier. The last stage is peeled off so that the loop body issues its
+  // DMA unconditionally.
+  auto run_stage = [&](int s, auto with_dma) {
+    wait_vmcnt<0>();
+    ring_barrier();
+    const uint8_t* buf = smem + (s & 1) * STAGE;
+    const uint8_t* sbuf = scl + (s & 1) * SC;
+    v4u sg_a[FM], sg_b[FN];  // the rows' 16 scale bytes of the stage (4 per 64-element block)
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      // lane l: row l % 32 of the fragment, K elements 16 ks + 8 (l / 32) .. + 7
-      const int off = ks * 32 + fh * 16;
-      v8h a[FM], b[FN];
+    for (int i = 0; i < FM; ++i) sg_a[i] = *reinterpret_cast<const v4u*>(sbuf + (wm0 + i * 32 + fr) * SCB);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        a[i] = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(buf + (wm0 + i * 32 + fr) * PITCH + off));
+    for (int j = 0; j < FN; ++j) sg_b[j] = *reinterpret_cast<const v4u*>(sbuf + (BM + wn0 + j * 32 + fr) * SCB);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        b[j] = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(buf + (BM + wn0 + j * 32 + fr) * PITCH + off));
+    for (int kb = 0; kb < KBLK; ++kb) {
+      if constexpr (decltype(with_dma)::value) issue_part(s + 1, kb);
+      const int c = 2 * kb + fh;  // 16-byte chunk of the row: elements 32h .. 32h + 31 of block kb
+      v4u ca[FM], cb[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm0 + i * 32 + fr;
+        ca[i] = *reinterpret_cast<const v4u*>(buf + r * BKB + ((c ^ swz(r)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn0 + j * 32 + fr;
+        cb[j] = *reinterpret_cast<const v4u*>(buf + BM * BKB + r * BKB + ((c ^ swz(r)) << 4));
+      }
+      // group scales of the lane's two 16-element groups of block kb (groups 4 kb + 2h and + 1)
+      h2 da[FM], db[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) da[i] = e4m3_pair2(sg_a[i][kb] >> sh);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) db[j] = e4m3_pair2(sg_b[j][kb] >> sh);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {  // k-step t: dword t of the chunk (elements 32h + 8t .. + 7)
+        v8h a[FM], b[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          a[i] = dequant8(ca[i][t], t < 2 ? __builtin_shufflevector(da[i], da[i], 0, 0)
+                                          : __builtin_shufflevector(da[i], da[i], 1, 1));
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[j], a[i], acc[i][j], 0, 0, 0);  // D[n][m]
+          b[j] = dequant8(cb[j][t], t < 2 ? __builtin_shufflevector(db[j], db[j], 0, 0)
+                                          : __builtin_shufflevector(db[j], db[j], 1, 1));
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[j], a[i], acc[i][j], 0, 0, 0);  // D[n][m]
+      }
     }
-    lstore(std::integral_constant<int, 1 - P>{});
-    __syncthreads();
   };
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  gload(P0{}, 0);
-  gload(P1{}, 1);
-  lstore(P0{});
-  __syncthreads();
-  for (int s = 0; s < nst; s += 2) {
-    stage(P0{}, s);
-    stage(P1{}, s + 1);
-  }
+#pragma unroll
+  for (int p = 0; p < KBLK; ++p) issue_part(0, p);
+  for (int s = 0; s + 1 < nst; ++s) run_stage(s, std::true_type{});
+  run_stage(nst - 1, std::false_type{});
 
   // acc[i][j][4q + r] = Y[m][n + r] with m = wm0 + 32 i + l % 32, n = wn0 + 32 j + 8 q + 4 (l / 32).
   // Epilogue: each wave stages one 32 x WN slab of float32 at a time in its own region of the
@@ -323,7 +390,9 @@ hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const
 }  // namespace
 }  // namespace fp4
 
-bool fp4_gemm_nvfp4_ring_fits(int64_t M, int64_t N, int64_t K) { return K % 64 == 0 && M >= 256 && N >= 256; }
+bool fp4_gemm_nvfp4_ring_fits(int64_t M, int64_t N, int64_t K) {
+  return K % 256 == 0 && K < ((int64_t)1 << 25) && M >= 256 && N >= 256;
+}
 
 hipError_t fp4_launch_gemm_nvfp4_ring(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const uint8_t* Wq,
                                       const uint8_t* Ws, const float* w_ts, int64_t M, int64_t N, int64_t K, void* Y,

@@ -174,11 +174,13 @@ def dev_f32(v):
     return torch.tensor([v], dtype=torch.float32).cuda()
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (512, 768, 1024), (300, 520, 384), (777, 1000, 1536),
-                                   (2048, 8192, 256), (2048, 12544, 256), (4000, 14272, 256)])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (512, 768, 1024), (300, 520, 768), (777, 1000, 1536),
+                                   (2048, 8192, 256), (2048, 12544, 256), (4000, 14272, 256), (256, 256, 128),
+                                   (300, 520, 384)])
 def test_nv_large_tile_kernel_unit_scales_exact(M, N, K):
-    # NVFP4 shapes routed to the large-tile kernel (M, N >= 256): group scales 1.0 (E4M3 code
-    # 0x38) and tensor scales 1.0 make every product a multiple of 1/4 and every sum exact.
+    # NVFP4 shapes routed to the large-tile kernel (M, N >= 256, K % 256 == 0; K = 128 and 384 take
+    # the general kernel): group scales 1.0 (E4M3 code 0x38) and tensor scales 1.0 make every
+    # product a multiple of 1/4 and every sum exact.
     # Column plans on 256 CUs: one round of 256x256 tiles for 2048 x 8192, 256x256 then 256x192
     # tiles for 2048 x 12544 and for 4000 x 14272 (ragged in both: a last row tile of 160 rows,
     # a last 192-wide panel of 128 columns), 256x192 tiles alone for the small shapes.
@@ -196,7 +198,7 @@ def test_nv_large_tile_kernel_unit_scales_exact(M, N, K):
     assert np.array_equal(host(yb.float()).astype(np.float64), O.bf16_rne_f64(ref))
 
 
-@pytest.mark.parametrize("M,N,K", [(512, 768, 2048), (259, 300, 512)])
+@pytest.mark.parametrize("M,N,K", [(512, 768, 2048), (259, 300, 512), (2048, 12544, 768)])
 def test_nv_large_tile_kernel_random_scales(M, N, K):
     rng = np.random.default_rng(11 * M + N)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
