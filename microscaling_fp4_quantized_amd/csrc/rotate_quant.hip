@@ -234,7 +234,9 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_nv(const uint16_t* __re
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
   __shared__ __attribute__((aligned(16))) v4u stage[kThreads / 64][kStage];
-  const uint32_t gc = blockIdx.x * kThreads + threadIdx.x;
+  // mode bit 2: workgroups take the chunks in reverse order (see launch_b)
+  const uint32_t blk = (load_mode & 4) ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
+  const uint32_t gc = blk * kThreads + threadIdx.x;
   float v[32];
   load_chunk(X, ldx, gc, total, rm, load_mode, stage[threadIdx.x >> 6], v);
   if (gc >= total) return;
@@ -322,15 +324,19 @@ hipError_t launch_b(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int fm
   }
   constexpr int NV_RULE = RULE == kRuleFit ? kRuleFit : kRuleStandard;  // other rules are MXFP4 only
   unsigned* amax = reinterpret_cast<unsigned*>(ts);
+  // With the tensor maximum computed here, X is read twice. Both passes then use cached loads and
+  // the quantize pass walks X backwards: it starts on the chunks the max pass read last, which
+  // are still in the 256 MB Infinity Cache when X is not much larger than that.
+  const int nv_mode = given_ts ? load_mode : (load_mode & 1) | 4;
   if (!given_ts) {  // otherwise the caller's s_t is already in the word
     const dim3 grid_max(grid.x < kMaxPassGrid ? grid.x : kMaxPassGrid);
     // The per-workgroup maxima live in the codes buffer until the quantize pass overwrites it:
     // 4 bytes per workgroup against 16 bytes of codes per chunk, and grid_max <= chunks.
     float* partial = reinterpret_cast<float*>(codes);
-    hipLaunchKernelGGL(rotate_amax<B>, grid_max, block, 0, st, X, ldx, rm, total, load_mode, signs, partial);
+    hipLaunchKernelGGL(rotate_amax<B>, grid_max, block, 0, st, X, ldx, rm, total, load_mode & 1, signs, partial);
     hipLaunchKernelGGL(amax_finish, dim3(1), block, 0, st, partial, (int)grid_max.x, ts);
   }
-  hipLaunchKernelGGL((rotate_quant_nv<B, NV_RULE>), grid, block, 0, st, X, ldx, rm, total, load_mode, signs, amax,
+  hipLaunchKernelGGL((rotate_quant_nv<B, NV_RULE>), grid, block, 0, st, X, ldx, rm, total, nv_mode, signs, amax,
                      codes, scales);
   return hipGetLastError();
 }
