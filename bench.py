@@ -67,6 +67,21 @@ def measured_traffic(kernel_key: str, source: str, launches_per_unit: float = 1.
     return e["bytes_per_launch"] * launches_per_unit
 
 
+def gemm_kernel_for(fmt: str, M: int, N: int, K: int):
+    """(source file, kernel name) of the kernel fp4_linear runs for this shape when the scale
+    buffers are 16-byte aligned (torch's allocations are): the library's dispatch predicates, in
+    its order."""
+    if fmt == "mxfp4":
+        if M <= 16 and K % 512 == 0:
+            return "gemm_decode.hip", "gemm_mxfp4_decode"
+        if K % 512 == 0 and K < (1 << 25) and M >= 256 and N >= 256:
+            return "gemm_mxfp4_ring.hip", "gemm_mxfp4_ring"
+        return "gemm_mxfp4.hip", "gemm_mxfp4_kernel"
+    if K % 64 == 0 and M >= 256 and N >= 256:
+        return "gemm_nvfp4_ring.hip", "gemm_nvfp4_ring"
+    return "gemm_nvfp4.hip", "gemm_nvfp4_kernel"
+
+
 def bf16_dev(bits, dev):
     import numpy as np
     import torch
@@ -138,8 +153,77 @@ def time_cold(fn, iters, torch, dev):
             "launches": iters}
 
 
-def cpu_baseline(wl, x_bits, w_bits):
-    """The oracle (plain NumPy, untuned) on one full step of the workload."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rq_worker(args):
+    """One pool worker of the CPU rotate+quantize baseline: the oracle on a block of rows."""
+    lo, hi = args
+    from oracle import fp4_oracle as O
+
+    O.rotate_quantize(_CPU_RQ["x"][lo:hi], _CPU_RQ["block"], _CPU_RQ["fmt"])
+    return hi - lo
+
+
+_CPU_RQ = {}
+
+
+def cpu_rotate_quantize(wl, rows_per_worker=1024, max_workers=16):
+    """The oracle's rotate+quantize (float32 FWHT, exact scale and rounding, NumPy) on the first
+    rows of a workload's X, split by rows over a pool of host processes, one per core up to
+    max_workers. Runs before the GPU is touched (the pool forks), and reports GB/s of the same
+    algorithmic bytes as the GPU figure."""
+    import multiprocessing as mp
+
+    from microscaling_fp4_quantized_amd import workloads as WL
+
+    P = max(1, min(max_workers, os.cpu_count() or 1))
+    rows = min(wl.M, rows_per_worker * P)
+    _CPU_RQ.update(x=WL.draw_x(wl, M=rows), block=wl.block, fmt=wl.fmt)
+    bounds = [(rows * i // P, rows * (i + 1) // P) for i in range(P)]
+    with mp.get_context("fork").Pool(P) as pool:
+        pool.map(abs, range(P))  # every worker is up before the clock starts
+        t0 = time.perf_counter()
+        done = sum(pool.map(_oracle_rq_worker, bounds))
+        dt = time.perf_counter() - t0
+    _CPU_RQ.clear()
+    g = 32 if wl.fmt == "mxfp4" else 16
+    nbytes = done * wl.K * (2 + 0.5 + 1.0 / g)
+    return {"GB/s": nbytes / dt / 1e9, "unit": "GB/s", "cores": P, "seconds": dt, "algorithmic_bytes": nbytes,
+            "sample": f"the first {done} rows of {wl.name} ({wl.M}x{wl.K} bf16, block {wl.block}, "
+                      f"{wl.fmt.upper()}), {P} processes of {done // P} rows each, oracle rotate+quantize "
+                      f"(single-threaded NumPy per process)"}
+
+
+def quant_parity_counts(O, x_bits, block, fmt, codes, scales, rows):
+    """Near-boundary and mismatch counts of the GPU's codes and scales on sampled rows against the
+    oracle (MXFP4; the rule of the parity tests: differences at flagged elements are reported apart
+    from the others)."""
+    xr = x_bits[rows]
+    o_packed, o_scales, o_ts = O.rotate_quantize(xr, block, fmt)
+    y32 = O.rotate_fwht_f32(O.widen_bf16(xr), block)
+    flags = O.near_boundary_flags(y32, o_scales, fmt, o_ts)
+    diff = O.unpack_nibbles(o_packed) != O.unpack_nibbles(codes[rows])
+    g = 32 if fmt == "mxfp4" else 16
+    gflags = flags.reshape(flags.shape[0], -1, g).any(axis=2)
+    sdiff = o_scales != scales[rows]
+    return {"rows_checked": int(len(rows)), "elements": int(diff.size), "flagged": int(flags.sum()),
+            "code_mismatch_flagged": int((diff & flags).sum()), "code_mismatch_unflagged": int((diff & ~flags).sum()),
+            "scale_mismatch_flagged": int((sdiff & gflags).sum()),
+            "scale_mismatch_unflagged": int((sdiff & ~gflags).sum())}
+
+
+def cpu_baseline(wl, x_bits, w_bits, rq_cpu=None, parity=None):
+    """The oracle (plain NumPy, untuned) on whole steps of the workload, with the rotate+quantize
+    baseline in GB/s and the parity counts measured beside it."""
     from threadpoolctl import threadpool_info
 
     from oracle import fp4_oracle as O
@@ -154,194 +238,245 @@ def cpu_baseline(wl, x_bits, w_bits):
     dt = (time.perf_counter() - t0) / steps
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     flops = 2.0 * wl.M * wl.N * wl.K
-    return {
+    out = {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(max(blas) if blas else 1),
         "kind": "oracle",
         "sample": f"{steps} full steps of {wl.name} (M={wl.M}, K={wl.K}, N={wl.N}), averaged: oracle "
                   f"rotate+quantize of X (float32 FWHT, single-threaded NumPy) + float64 dequantized product "
-                  f"(BLAS dgemm); {dt:.2f} s per step, {os.cpu_count()} host threads visible",
+                  f"(BLAS dgemm on the BLAS threads counted in cores); {dt:.2f} s per step",
         "seconds": dt,
+        "host": {"cpu_model": cpu_model(), "cpu_count": os.cpu_count()},
     }
+    if rq_cpu is not None:
+        out["rotate_quantize"] = rq_cpu
+    if parity is not None:
+        out["parity_counts"] = parity
+    return out
 
 
-def extra_rows(B, WL, torch, dev):
-    """The other rows of the path, each timed over back-to-back launches on the library's stream:
-    NVFP4 rotate+quantize on the bandwidth-stress shape (two passes over X), the NVFP4 prefill
-    GEMM (bf16 MFMA after exact dequantization), the large MXFP4 GEMM, and the decode-shaped MXFP4
-    GEMM (HBM-bound on W)."""
+EXTRA_ROWS = ("nv_stress", "variants", "block128", "nv_gemm", "large", "m4096", "decode")
+
+
+def extra_rows(B, WL, torch, dev, groups=EXTRA_ROWS):
+    """The other rows of the path, each timed over back-to-back launches on the library's stream
+    (groups: nv_stress, variants, block128 on the 16384x8192 stress input; nv_gemm, large, m4096
+    GEMMs; decode, see decode_rows)."""
     out = {}
-    # NVFP4 rotate+quantize, 16384 x 8192, block 32
     sw = WL.WORKLOADS["stress_nv32"]
-    sx = WL.draw_x(sw)
-    bufs = [bf16_dev(sx, dev) for _ in range(3)]
-    del sx
-    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    torch.sum(flush, dim=(0,))
-    del flush
-    o = (torch.empty((sw.M, sw.K // 2), dtype=torch.uint8, device=dev),
-         torch.empty((sw.M, sw.K // 16), dtype=torch.uint8, device=dev),
-         torch.empty((1,), dtype=torch.float32, device=dev))
-    for i in range(3):
-        B.fp4_rotate_quantize(bufs[i % 3], sw.block, "nvfp4", out=o)
-    ms = time_batch(lambda i: B.fp4_rotate_quantize(bufs[i % 3], sw.block, "nvfp4", out=o), 21, torch)
-    nbytes = sw.M * sw.K * (2 + 2 + 0.5 + 1.0 / 16) + 8
-    t_max = measured_traffic("rotate_amax_b32", "rotate_quant.hip")
-    t_nv = measured_traffic("rotate_quant_nv_b32", "rotate_quant.hip")
-    out["rotate_quantize_nvfp4"] = {
-        "workload": "stress_nv32: X 16384x8192 bf16, block 32, NVFP4 (max pass + quantize pass)",
-        "us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "algorithmic_bytes": nbytes,
-        "traffic": None if t_max is None or t_nv is None else t_max + t_nv}
-    log(f"[bench] NVFP4 stress rotate+quantize {ms * 1e3:.1f} us = {out['rotate_quantize_nvfp4']['GB/s']:.0f} GB/s")
-    # quantizer variants on the same 16384 x 8192 input (block 32)
-    signs = torch.from_numpy(WL.draw_signs(sw.K, 1)).to(dev)
-    var = {}
-    given = torch.tensor([float(o[2].item())], dtype=torch.float32, device=dev)  # the computed s_t, reused
-    for fmt, rule, sg in (("nvfp4", "fit", None), ("nvfp4", "given_scale", None), ("mxfp4", "oas", None),
-                          ("mxfp4", "ocp_floor", None), ("mxfp4", "fit", None), ("mxfp4", "standard", signs)):
-        g = 32 if fmt == "mxfp4" else 16
-        oo = (torch.empty((sw.M, sw.K // 2), dtype=torch.uint8, device=dev),
-              torch.empty((sw.M, sw.K // g), dtype=torch.uint8, device=dev),
-              torch.empty((1,), dtype=torch.float32, device=dev) if fmt == "nvfp4" else None)
-
-        def call(i, fmt=fmt, rule=rule, sg=sg, oo=oo):
-            if rule == "given_scale":
-                B.fp4_rotate_quantize(bufs[i % 3], sw.block, fmt, out=oo, tensor_scale=given)
-            else:
-                B.fp4_rotate_quantize(bufs[i % 3], sw.block, fmt, out=oo, rule=rule, signs=sg)
-
-        for i in range(2):
-            call(i)
-        ms = time_batch(call, 12, torch)
-        nb = sw.M * sw.K * ((2 if fmt == "nvfp4" and rule != "given_scale" else 0) + 2 + 0.5 + 1.0 / g)
-        name = f"{fmt}_{rule}" + ("_signs" if sg is not None else "")
-        var[name] = {"us": ms * 1e3, "GB/s": nb / (ms * 1e-3) / 1e9, "frac_hbm": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        log(f"[bench] variant {name}: {ms * 1e3:.1f} us = {var[name]['GB/s']:.0f} GB/s")
-    out["rotate_quantize_variants"] = {"workload": "16384x8192 bf16, block 32 (stress_nv32 input)", **var}
-    # the same input with the 128-element Hadamard block, both formats
-    b128 = {}
-    for fmt, key in (("mxfp4", "rotate_quant_mx_b128"), ("nvfp4", None)):
-        g = 32 if fmt == "mxfp4" else 16
-        oo = (torch.empty((sw.M, sw.K // 2), dtype=torch.uint8, device=dev),
-              torch.empty((sw.M, sw.K // g), dtype=torch.uint8, device=dev),
-              torch.empty((1,), dtype=torch.float32, device=dev) if fmt == "nvfp4" else None)
-
-        def call128(i, fmt=fmt, oo=oo):
-            B.fp4_rotate_quantize(bufs[i % 3], 128, fmt, out=oo)
-
+    if {"nv_stress", "variants", "block128"} & set(groups):
+        sx = WL.draw_x(sw)
+        bufs = [bf16_dev(sx, dev) for _ in range(3)]
+        del sx
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        torch.sum(flush, dim=(0,))
+        del flush
+        o = (torch.empty((sw.M, sw.K // 2), dtype=torch.uint8, device=dev),
+             torch.empty((sw.M, sw.K // 16), dtype=torch.uint8, device=dev),
+             torch.empty((1,), dtype=torch.float32, device=dev))
         for i in range(3):
-            call128(i)
-        ms = time_batch(call128, 21, torch)
-        nb = sw.M * sw.K * ((2 if fmt == "nvfp4" else 0) + 2 + 0.5 + 1.0 / g) + (8 if fmt == "nvfp4" else 0)
-        if fmt == "mxfp4":
-            tr = measured_traffic("rotate_quant_mx_b128", "rotate_quant.hip")
-        else:
-            t1 = measured_traffic("rotate_amax_b128", "rotate_quant.hip")
-            t2 = measured_traffic("rotate_quant_nv_b128", "rotate_quant.hip")
-            tr = None if t1 is None or t2 is None else t1 + t2
-        b128[fmt] = {"us": ms * 1e3, "GB/s": nb / (ms * 1e-3) / 1e9, "frac_hbm": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "algorithmic_bytes": nb, "traffic": tr}
-        log(f"[bench] block 128 {fmt} stress rotate+quantize {ms * 1e3:.1f} us = {b128[fmt]['GB/s']:.0f} GB/s "
-            f"({b128[fmt]['frac_hbm']:.1%} of HBM)")
-    out["rotate_quantize_block128"] = {
-        "workload": "stress_mx128 / stress_nv128: X 16384x8192 bf16 (the stress_nv32 input), block 128; NVFP4 "
-                    "counts its max pass as a second read of X", **b128}
-    del bufs, o
-    # NVFP4 prefill GEMM, M=2048 K=4096 N=14336, Y bf16
-    wl = WL.WORKLOADS["prefill_nv"]
-    xq, xs, xts = B.fp4_rotate_quantize(bf16_dev(WL.draw_x(wl), dev), wl.block, "nvfp4")
-    wq, ws, wts = B.fp4_quantize_weights(bf16_dev(WL.draw_w(wl), dev), wl.block, "nvfp4")
-    y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
-    for _ in range(3):
-        B.fp4_linear(xq, xs, wq, ws, "nvfp4", x_ts=xts, w_ts=wts, out_dtype=torch.bfloat16, out=y)
-    ms = time_batch(lambda i: B.fp4_linear(xq, xs, wq, ws, "nvfp4", x_ts=xts, w_ts=wts,
-                                           out_dtype=torch.bfloat16, out=y), 20, torch)
-    tf = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
-    out["gemm_nvfp4"] = {"workload": "prefill_nv: M=2048 K=4096 N=14336, block 16, Y bf16",
-                         "us": ms * 1e3, "TFLOP/s": tf, "frac_bf16_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
-                         "frac_fp4_mfma_peak": tf / MFMA_FP4_PEAK_TFLOPS,
-                         "traffic": measured_traffic("gemm_nvfp4_ring", "gemm_nvfp4_ring.hip")}
-    log(f"[bench] NVFP4 GEMM {ms * 1e3:.1f} us = {tf:.0f} TFLOP/s")
-    del xq, xs, wq, ws, y
-    # the large MXFP4 configuration: M=8192 K=8192 N=28672, block 128, Y fp32 (whole rounds of tiles)
-    wl = WL.WORKLOADS["large"]
-    xq, xs, _ = B.fp4_rotate_quantize(bf16_dev(WL.draw_x(wl), dev), wl.block, "mxfp4")
-    wq, ws, _ = B.fp4_quantize_weights(bf16_dev(WL.draw_w(wl), dev), wl.block, "mxfp4")
-    y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
-    for _ in range(20):  # about 20 ms of this kernel first, so that it is timed at its own steady clocks
-        B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y)
-    ms = time_batch(lambda i: B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y), 10, torch)
-    tf = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
-    out["gemm_mxfp4_large"] = {"workload": "large: M=8192 K=8192 N=28672, block 128, Y fp32",
-                               "us": ms * 1e3, "TFLOP/s": tf, "frac_fp4_mfma_peak": tf / MFMA_FP4_PEAK_TFLOPS,
-                               "algorithmic_bytes": (wl.M + wl.N) * wl.K * (0.5 + 1.0 / 32) + wl.M * wl.N * 4,
-                               "traffic": measured_traffic("gemm_mxfp4_ring_large", "gemm_mxfp4_ring.hip")}
-    log(f"[bench] large MXFP4 GEMM {ms * 1e3:.1f} us = {tf:.0f} TFLOP/s ({tf / MFMA_FP4_PEAK_TFLOPS:.1%} of peak)")
-    del xq, xs, wq, ws, y
-    # the headline layer at twice the tokens: M=4096 K=4096 N=14336, MXFP4 block 32, Y bf16
-    wl = WL.WORKLOADS["prefill_mx_m4096"]
-    xq, xs, _ = B.fp4_rotate_quantize(bf16_dev(WL.draw_x(wl), dev), wl.block, "mxfp4")
-    wq, ws, _ = B.fp4_quantize_weights(bf16_dev(WL.draw_w(wl), dev), wl.block, "mxfp4")
-    y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < 0.25:  # 250 ms of this kernel first, as the headline step's ramp
-        for _ in range(20):
-            B.fp4_linear(xq, xs, wq, ws, "mxfp4", out_dtype=torch.bfloat16, out=y)
-        torch.cuda.synchronize()
-    ms = time_batch(lambda i: B.fp4_linear(xq, xs, wq, ws, "mxfp4", out_dtype=torch.bfloat16, out=y), 20, torch)
-    tf = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
-    out["gemm_mxfp4_m4096"] = {"workload": "prefill_mx_m4096: M=4096 K=4096 N=14336, block 32, Y bf16",
-                               "us": ms * 1e3, "TFLOP/s": tf, "frac_fp4_mfma_peak": tf / MFMA_FP4_PEAK_TFLOPS,
-                               "algorithmic_bytes": (wl.M + wl.N) * wl.K * (0.5 + 1.0 / 32) + wl.M * wl.N * 2,
-                               "traffic": measured_traffic("gemm_mxfp4_ring_m4096", "gemm_mxfp4_ring.hip")}
-    log(f"[bench] M=4096 MXFP4 GEMM {ms * 1e3:.1f} us = {tf:.0f} TFLOP/s ({tf / MFMA_FP4_PEAK_TFLOPS:.1%} of peak)")
-    del xq, xs, wq, ws, y
-    # decode-shaped MXFP4 GEMM: W 4096x4096 streamed once per call
-    for name in ("decode1", "decode4", "decode16"):
-        wl = WL.WORKLOADS[name]
+            B.fp4_rotate_quantize(bufs[i % 3], sw.block, "nvfp4", out=o)
+    if "nv_stress" in groups:
+        # NVFP4 rotate+quantize, 16384 x 8192, block 32: the max pass and the quantize pass
+        ms = time_batch(lambda i: B.fp4_rotate_quantize(bufs[i % 3], sw.block, "nvfp4", out=o), 21, torch)
+        nbytes = sw.M * sw.K * (2 + 2 + 0.5 + 1.0 / 16) + 8
+        t_max = measured_traffic("rotate_amax@stress_nv32", "rotate_quant.hip")
+        t_nv = measured_traffic("rotate_quant_nv@stress_nv32", "rotate_quant.hip")
+        out["rotate_quantize_nvfp4"] = {
+            "workload": "stress_nv32: X 16384x8192 bf16, block 32, NVFP4 (max pass + quantize pass)",
+            "us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+            "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+            "traffic": None if t_max is None or t_nv is None else t_max + t_nv}
+        log(f"[bench] NVFP4 stress rotate+quantize {ms * 1e3:.1f} us = {out['rotate_quantize_nvfp4']['GB/s']:.0f} GB/s")
+    if "variants" in groups:
+        # quantizer variants on the same 16384 x 8192 input (block 32)
+        signs = torch.from_numpy(WL.draw_signs(sw.K, 1)).to(dev)
+        var = {}
+        given = torch.tensor([float(o[2].item())], dtype=torch.float32, device=dev)  # the computed s_t, reused
+        for fmt, rule, sg in (("nvfp4", "fit", None), ("nvfp4", "given_scale", None), ("mxfp4", "oas", None),
+                              ("mxfp4", "ocp_floor", None), ("mxfp4", "fit", None), ("mxfp4", "standard", signs)):
+            g = 32 if fmt == "mxfp4" else 16
+            oo = (torch.empty((sw.M, sw.K // 2), dtype=torch.uint8, device=dev),
+                  torch.empty((sw.M, sw.K // g), dtype=torch.uint8, device=dev),
+                  torch.empty((1,), dtype=torch.float32, device=dev) if fmt == "nvfp4" else None)
+
+            def call(i, fmt=fmt, rule=rule, sg=sg, oo=oo):
+                if rule == "given_scale":
+                    B.fp4_rotate_quantize(bufs[i % 3], sw.block, fmt, out=oo, tensor_scale=given)
+                else:
+                    B.fp4_rotate_quantize(bufs[i % 3], sw.block, fmt, out=oo, rule=rule, signs=sg)
+
+            for i in range(2):
+                call(i)
+            ms = time_batch(call, 12, torch)
+            nb = sw.M * sw.K * ((2 if fmt == "nvfp4" and rule != "given_scale" else 0) + 2 + 0.5 + 1.0 / g)
+            name = f"{fmt}_{rule}" + ("_signs" if sg is not None else "")
+            var[name] = {"us": ms * 1e3, "GB/s": nb / (ms * 1e-3) / 1e9,
+                         "frac_hbm": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            log(f"[bench] variant {name}: {ms * 1e3:.1f} us = {var[name]['GB/s']:.0f} GB/s")
+        out["rotate_quantize_variants"] = {"workload": "16384x8192 bf16, block 32 (stress_nv32 input)", **var}
+    if "block128" in groups:
+        # the same input with the 128-element Hadamard block, both formats
+        b128 = {}
+        for fmt in ("mxfp4", "nvfp4"):
+            g = 32 if fmt == "mxfp4" else 16
+            oo = (torch.empty((sw.M, sw.K // 2), dtype=torch.uint8, device=dev),
+                  torch.empty((sw.M, sw.K // g), dtype=torch.uint8, device=dev),
+                  torch.empty((1,), dtype=torch.float32, device=dev) if fmt == "nvfp4" else None)
+
+            def call128(i, fmt=fmt, oo=oo):
+                B.fp4_rotate_quantize(bufs[i % 3], 128, fmt, out=oo)
+
+            for i in range(3):
+                call128(i)
+            ms = time_batch(call128, 21, torch)
+            nb = sw.M * sw.K * ((2 if fmt == "nvfp4" else 0) + 2 + 0.5 + 1.0 / g) + (8 if fmt == "nvfp4" else 0)
+            if fmt == "mxfp4":
+                tr = measured_traffic("rotate_quant_mx@stress_mx128", "rotate_quant.hip")
+            else:
+                t1 = measured_traffic("rotate_amax@stress_nv128", "rotate_quant.hip")
+                t2 = measured_traffic("rotate_quant_nv@stress_nv128", "rotate_quant.hip")
+                tr = None if t1 is None or t2 is None else t1 + t2
+            b128[fmt] = {"us": ms * 1e3, "GB/s": nb / (ms * 1e-3) / 1e9,
+                         "frac_hbm": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": nb, "traffic": tr}
+            log(f"[bench] block 128 {fmt} stress rotate+quantize {ms * 1e3:.1f} us = {b128[fmt]['GB/s']:.0f} GB/s "
+                f"({b128[fmt]['frac_hbm']:.1%} of HBM)")
+        out["rotate_quantize_block128"] = {
+            "workload": "stress_mx128 / stress_nv128: X 16384x8192 bf16 (the stress_nv32 input), block 128; NVFP4 "
+                        "counts its max pass as a second read of X", **b128}
+    if {"nv_stress", "variants", "block128"} & set(groups):
+        del bufs, o
+    if "nv_gemm" in groups:
+        # NVFP4 prefill GEMM, M=2048 K=4096 N=14336, Y bf16
+        wl = WL.WORKLOADS["prefill_nv"]
+        xq, xs, xts = B.fp4_rotate_quantize(bf16_dev(WL.draw_x(wl), dev), wl.block, "nvfp4")
+        wq, ws, wts = B.fp4_quantize_weights(bf16_dev(WL.draw_w(wl), dev), wl.block, "nvfp4")
+        y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.25:  # 250 ms of this kernel first, at its own steady clocks
+            for _ in range(10):
+                B.fp4_linear(xq, xs, wq, ws, "nvfp4", x_ts=xts, w_ts=wts, out_dtype=torch.bfloat16, out=y)
+            torch.cuda.synchronize()
+        ms = time_batch(lambda i: B.fp4_linear(xq, xs, wq, ws, "nvfp4", x_ts=xts, w_ts=wts,
+                                               out_dtype=torch.bfloat16, out=y), 20, torch)
+        tf = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
+        out["gemm_nvfp4"] = {"workload": "prefill_nv: M=2048 K=4096 N=14336, block 16, Y bf16",
+                             "us": ms * 1e3, "TFLOP/s": tf, "frac_bf16_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+                             "frac_fp4_mfma_peak": tf / MFMA_FP4_PEAK_TFLOPS,
+                             "traffic": measured_traffic("gemm_nvfp4_ring@prefill_nv", "gemm_nvfp4_ring.hip")}
+        log(f"[bench] NVFP4 GEMM {ms * 1e3:.1f} us = {tf:.0f} TFLOP/s ({tf / MFMA_BF16_PEAK_TFLOPS:.1%} of the 16-bit peak)")
+        del xq, xs, wq, ws, y
+    if "large" in groups:
+        # the large MXFP4 configuration: M=8192 K=8192 N=28672, block 128, Y fp32 (whole rounds of tiles)
+        wl = WL.WORKLOADS["large"]
         xq, xs, _ = B.fp4_rotate_quantize(bf16_dev(WL.draw_x(wl), dev), wl.block, "mxfp4")
         wq, ws, _ = B.fp4_quantize_weights(bf16_dev(WL.draw_w(wl), dev), wl.block, "mxfp4")
         y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
-        for _ in range(3):
+        for _ in range(20):  # about 20 ms of this kernel first, so that it is timed at its own steady clocks
             B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y)
-        ref = y.clone()
-        ms_calls = time_batch(lambda i: B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y), 50, torch)
-        y.zero_()
-        ms = time_graph(lambda i: B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y), 50, torch)
-        graph_ok = bool(torch.equal(y, ref))
-        wbytes = wl.N * wl.K * (0.5 + 1.0 / 32)
-        nbytes = wbytes + wl.M * wl.K * (0.5 + 1.0 / 32) + wl.M * wl.N * 4
-        out[f"gemm_{name}"] = {"workload": f"{name}: M={wl.M} K={wl.K} N={wl.N} MXFP4, Y fp32",
-                               "us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
-                               "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
-                               "us_per_python_call": ms_calls * 1e3, "graph_replay_matches_eager": graph_ok,
-                               "traffic": measured_traffic("gemm_mxfp4_decode", "gemm_decode.hip"),
-                               "note": "50 calls captured in one HIP graph; W (8.9 MB) stays in the 256 MB "
-                                       "Infinity Cache across calls"}
-        log(f"[bench] {name} GEMM {ms * 1e3:.2f} us in a graph = {out[f'gemm_{name}']['GB/s']:.0f} GB/s "
-            f"({ms_calls * 1e3:.2f} us per Python call; graph result matches eager: {graph_ok})")
-        # the whole decode step from bf16 X: two calls, or the one-launch fused kernel
+        ms = time_batch(lambda i: B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y), 10, torch)
+        tf = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
+        out["gemm_mxfp4_large"] = {"workload": "large: M=8192 K=8192 N=28672, block 128, Y fp32",
+                                   "us": ms * 1e3, "TFLOP/s": tf, "frac_fp4_mfma_peak": tf / MFMA_FP4_PEAK_TFLOPS,
+                                   "algorithmic_bytes": (wl.M + wl.N) * wl.K * (0.5 + 1.0 / 32) + wl.M * wl.N * 4,
+                                   "traffic": measured_traffic("gemm_mxfp4_ring@large", "gemm_mxfp4_ring.hip")}
+        log(f"[bench] large MXFP4 GEMM {ms * 1e3:.1f} us = {tf:.0f} TFLOP/s ({tf / MFMA_FP4_PEAK_TFLOPS:.1%} of peak)")
+        del xq, xs, wq, ws, y
+    if "m4096" in groups:
+        # the headline layer at twice the tokens: M=4096 K=4096 N=14336, MXFP4 block 32, Y bf16
+        wl = WL.WORKLOADS["prefill_mx_m4096"]
+        xq, xs, _ = B.fp4_rotate_quantize(bf16_dev(WL.draw_x(wl), dev), wl.block, "mxfp4")
+        wq, ws, _ = B.fp4_quantize_weights(bf16_dev(WL.draw_w(wl), dev), wl.block, "mxfp4")
+        y = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.25:  # 250 ms of this kernel first, as the headline step's ramp
+            for _ in range(20):
+                B.fp4_linear(xq, xs, wq, ws, "mxfp4", out_dtype=torch.bfloat16, out=y)
+            torch.cuda.synchronize()
+        ms = time_batch(lambda i: B.fp4_linear(xq, xs, wq, ws, "mxfp4", out_dtype=torch.bfloat16, out=y), 20, torch)
+        tf = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
+        out["gemm_mxfp4_m4096"] = {"workload": "prefill_mx_m4096: M=4096 K=4096 N=14336, block 32, Y bf16",
+                                   "us": ms * 1e3, "TFLOP/s": tf, "frac_fp4_mfma_peak": tf / MFMA_FP4_PEAK_TFLOPS,
+                                   "algorithmic_bytes": (wl.M + wl.N) * wl.K * (0.5 + 1.0 / 32) + wl.M * wl.N * 2,
+                                   "traffic": measured_traffic("gemm_mxfp4_ring@prefill_mx_m4096",
+                                                               "gemm_mxfp4_ring.hip")}
+        log(f"[bench] M=4096 MXFP4 GEMM {ms * 1e3:.1f} us = {tf:.0f} TFLOP/s ({tf / MFMA_FP4_PEAK_TFLOPS:.1%} of peak)")
+        del xq, xs, wq, ws, y
+    if "decode" in groups:
+        out.update(decode_rows(B, WL, torch, dev))
+    return out
+
+
+def decode_rows(B, WL, torch, dev, names=("decode1", "decode4", "decode16", "decode_wide1", "decode_wide4",
+                                            "decode_wide16")):
+    """Decode-shaped MXFP4 layers (M in {1, 4, 16} tokens, K=4096; W 4096x4096 or 14336x4096),
+    bound by reading W from HBM. Each row is timed as a HIP graph of calls that cycle over copies of
+    W totalling more than 512 MB, so that no call finds its W in the 256 MB Infinity Cache (as in a
+    model whose weights do not fit in it); the graph's result is checked against an eager call. The
+    same call with one W, resident in the cache, is reported as warm_us. The whole decode step from
+    bf16 X (two calls, or the one-launch fused call) is timed the same way."""
+    import math
+
+    out = {}
+    for name in names:
+        wl = WL.WORKLOADS[name]
         xb = bf16_dev(WL.draw_x(wl), dev)
+        wq, ws, _ = B.fp4_quantize_weights(bf16_dev(WL.draw_w(wl), dev), wl.block, "mxfp4")
+        wbytes = wl.N * wl.K * (0.5 + 1.0 / 32)
+        n_sets = int(math.ceil(512e6 / wbytes))
+        sets = [(wq.clone(), ws.clone()) for _ in range(n_sets)]
+        xq, xs, _ = B.fp4_rotate_quantize(xb, wl.block, "mxfp4")
+        y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
+        B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y)
+        ref = y.clone()
+        calls = 2 * n_sets
+
+        def gemm(i):
+            w_i = sets[i % n_sets]
+            B.fp4_linear(xq, xs, w_i[0], w_i[1], "mxfp4", out=y)
+
+        y.zero_()
+        ms = time_graph(gemm, calls, torch)
+        graph_ok = bool(torch.equal(y, ref))
+        ms_warm = time_graph(lambda i: B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y), 50, torch)
+        ms_call = time_batch(lambda i: B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y), 50, torch)
+        nbytes = wbytes + wl.M * wl.K * (0.5 + 1.0 / 32) + wl.M * wl.N * 4
+        row = {"workload": f"{name}: M={wl.M} K={wl.K} N={wl.N} MXFP4, Y fp32",
+               "us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+               "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+               "w_copies": n_sets, "graph_replay_matches_eager": graph_ok,
+               "warm_us": ms_warm * 1e3, "warm_GB/s": nbytes / (ms_warm * 1e-3) / 1e9,
+               "us_per_python_call": ms_call * 1e3,
+               "traffic": measured_traffic("gemm_mxfp4_decode@" + ("decode_wide" if wl.N > 4096 else "decode"),
+                                          "gemm_decode.hip"),
+               "note": f"{calls} calls in one HIP graph over {n_sets} copies of W ({n_sets * wbytes / 1e6:.0f} MB), "
+                       "so W comes from HBM; warm_us: one W, resident in the Infinity Cache"}
+        log(f"[bench] {name} GEMM {ms * 1e3:.2f} us with W from HBM = {row['GB/s']:.0f} GB/s "
+            f"({row['frac_hbm']:.1%} of HBM); W in cache {ms_warm * 1e3:.2f} us; graph matches eager: {graph_ok}")
+        # the whole decode step from bf16 X: two calls, or the one-launch fused kernel
         xqo = (torch.empty((wl.M, wl.K // 2), dtype=torch.uint8, device=dev),
                torch.empty((wl.M, wl.K // 32), dtype=torch.uint8, device=dev), None)
         y2 = torch.empty_like(y)
 
         def two_calls(i):
+            w_i = sets[i % n_sets]
             B.fp4_rotate_quantize(xb, wl.block, "mxfp4", out=xqo)
-            B.fp4_linear(xqo[0], xqo[1], wq, ws, "mxfp4", out=y2)
+            B.fp4_linear(xqo[0], xqo[1], w_i[0], w_i[1], "mxfp4", out=y2)
 
         def fused(i):
-            B.fp4_rotate_quantize_linear(xb, wq, ws, wl.block, out=y)
+            w_i = sets[i % n_sets]
+            B.fp4_rotate_quantize_linear(xb, w_i[0], w_i[1], wl.block, out=y)
 
-        ms_two = time_graph(two_calls, 50, torch)
-        ms_fused = time_graph(fused, 50, torch)
+        ms_two = time_graph(two_calls, calls, torch)
+        ms_fused = time_graph(fused, calls, torch)
         same = bool(torch.equal(y, y2))
-        out[f"gemm_{name}"]["step_from_bf16_x"] = {"two_calls_us": ms_two * 1e3, "fused_us": ms_fused * 1e3,
-                                                   "fused_equals_two_calls": same}
-        log(f"[bench] {name} step from bf16 X in a graph: two calls {ms_two * 1e3:.2f} us, "
+        row["step_from_bf16_x"] = {"two_calls_us": ms_two * 1e3, "fused_us": ms_fused * 1e3,
+                                   "fused_equals_two_calls": same}
+        log(f"[bench] {name} step from bf16 X, W from HBM: two calls {ms_two * 1e3:.2f} us, "
             f"fused {ms_fused * 1e3:.2f} us (same result: {same})")
+        out[f"gemm_{name}"] = row
+        del sets, wq, ws
     return out
 
 
@@ -359,6 +494,8 @@ def main():
                     help="skip the NVFP4 and decode-shaped measurements reported beside the headline")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--rows", default=",".join(EXTRA_ROWS),
+                    help="comma-separated groups of other rows to run (default: all of %s)" % ",".join(EXTRA_ROWS))
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -366,11 +503,19 @@ def main():
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
+    from microscaling_fp4_quantized_amd import workloads as WL
+
+    # CPU baseline of rotate+quantize first: its process pool forks before anything touches the GPU
+    rq_cpu = None
+    if not args.no_cpu and not args.copy_probe:
+        log("[bench] CPU oracle rotate+quantize baseline ...")
+        rq_cpu = cpu_rotate_quantize(WL.WORKLOADS[args.stress or "stress_mx32"])
+        log(f"[bench] CPU oracle rotate+quantize: {rq_cpu['GB/s']:.3f} GB/s on {rq_cpu['cores']} processes")
+
     import numpy as np
     import torch
 
     from microscaling_fp4_quantized_amd import binding as B
-    from microscaling_fp4_quantized_amd import workloads as WL
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -435,18 +580,14 @@ def main():
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
+    step_codes, step_scales = xq.cpu().numpy(), xs.cpu().numpy()
     rq_ms = sum(a.elapsed_time(b) for a, b in zip(ev["a"], ev["b"])) / args.steps
     gemm_ms = sum(b.elapsed_time(c) for b, c in zip(ev["b"], ev["c"])) / args.steps
     flops = 2.0 * wl.M * wl.N * wl.K
     step_tflops = flops / (ms_step * 1e-3) / 1e12
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     peak = MFMA_FP4_PEAK_TFLOPS if wl.fmt == "mxfp4" else MFMA_BF16_PEAK_TFLOPS
-    if wl.fmt == "mxfp4" and wl.K % 512 == 0 and wl.M >= 256 and wl.N >= 256:
-        gemm_src, gemm_kernel = "gemm_mxfp4_ring.hip", "gemm_mxfp4_ring"
-    elif wl.fmt == "mxfp4":
-        gemm_src, gemm_kernel = "gemm_mxfp4.hip", "gemm_mxfp4_kernel"
-    else:
-        gemm_src, gemm_kernel = "gemm_nvfp4.hip", "gemm_nvfp4_kernel"
+    gemm_src, gemm_kernel = gemm_kernel_for(wl.fmt, wl.M, wl.N, wl.K)
     rq_bytes = wl.M * wl.K * (2 + 0.5 + 1.0 / g) + (8 if wl.fmt == "nvfp4" else 0)
     if wl.fmt == "nvfp4":
         rq_bytes += wl.M * wl.K * 2  # the tensor-maximum pass reads X a second time
@@ -462,6 +603,23 @@ def main():
     roof_ms = time_batch(gemm_only, max(args.steps, 20), torch)
     roof_tflops = flops / (roof_ms * 1e-3) / 1e12
     log(f"[bench] GEMM back-to-back {roof_ms * 1e3:.1f} us = {roof_tflops:.0f} TFLOP/s ({roof_tflops / peak:.1%} of peak)")
+    # the same, back to back, with W read from HBM: calls cycle over copies of W totalling more than
+    # 512 MB (a model's layers do not share one W that stays in the 256 MB Infinity Cache)
+    w_bytes = wq.numel() + ws.numel()
+    n_w = -(-512 * 10 ** 6 // w_bytes)
+    w_sets = [(wq.clone(), ws.clone(), None if wts is None else wts.clone()) for _ in range(n_w)]
+
+    def gemm_w_hbm(i):
+        q, sc, t = w_sets[i % n_w]
+        B.fp4_linear(xq, xs, q, sc, wl.fmt, x_ts=xts, w_ts=t, out_dtype=out_dtype, out=y)
+
+    for i in range(n_w):
+        gemm_w_hbm(i)
+    hbm_ms = time_batch(gemm_w_hbm, 2 * n_w, torch)
+    hbm_tflops = flops / (hbm_ms * 1e-3) / 1e12
+    del w_sets
+    log(f"[bench] GEMM back-to-back, W from HBM ({n_w} copies): {hbm_ms * 1e3:.1f} us = {hbm_tflops:.0f} TFLOP/s "
+        f"({hbm_tflops / peak:.1%} of peak)")
     cold = time_cold(gemm_only, 30, torch, dev)
     log(f"[bench] GEMM cold (1 GiB read between launches): median {cold['median_us']:.1f} us "
         f"(p10 {cold['p10_us']:.1f}, p90 {cold['p90_us']:.1f})")
@@ -495,10 +653,14 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": roof_tflops / peak,
-            "traffic": measured_traffic(gemm_kernel, gemm_src),
+            "traffic": measured_traffic(f"{gemm_kernel}@{wl.name}", gemm_src),
             "algorithmic_flops": flops,
             "algorithmic_bytes": gemm_alg_bytes,
             "avg_launch_us": roof_ms * 1e3,
+            "w_from_hbm": {"avg_launch_us": hbm_ms * 1e3, "achieved": hbm_tflops, "frac": hbm_tflops / peak,
+                           "w_copies": n_w,
+                           "note": "back-to-back launches cycling over copies of W totalling more than 512 MB, "
+                                   "so every launch reads its W from HBM"},
             "cold": {**cold, "TFLOP/s_median": flops / (cold["median_us"] * 1e-6) / 1e12,
                      "note": "each launch timed alone after reading a 1 GiB buffer, so W and X come from HBM "
                              "instead of the 256 MB Infinity Cache"},
@@ -521,6 +683,8 @@ def main():
         # finds its X in the 256 MB Infinity Cache (streaming loads may leave lines that were
         # resident before the first launch in place)
         bufs = [bf16_dev(sx, dev) for _ in range(3)]
+        stress_rows = np.unique(np.random.default_rng(17).choice(sw.M, 64, replace=False))
+        stress_x_rows = sx[stress_rows].copy()
         del sx
         flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         torch.sum(flush, dim=(0,))
@@ -554,21 +718,34 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": gbs / HBM_PEAK_GBS,
-            "traffic": measured_traffic("rotate_quant_mx_b%d" % sw.block, "rotate_quant.hip")
+            "traffic": measured_traffic(f"rotate_quant_mx@{sw.name}", "rotate_quant.hip")
             if sw.fmt == "mxfp4" else None,
             "algorithmic_bytes": s_bytes,
             "avg_launch_us": s_ms * 1e3,
             "cold": {**s_cold, "GB/s_median": cold_gbs, "frac_median": cold_gbs / HBM_PEAK_GBS,
                      "note": "each launch timed alone after reading a 1 GiB buffer (no Infinity Cache residency)"},
         }
+        stress_out = (sw, stress_rows, stress_x_rows, outs[0].cpu().numpy()[stress_rows],
+                      outs[1].cpu().numpy()[stress_rows])
         del bufs, outs
 
     if not args.no_extra:
-        result["other_rows"] = extra_rows(B, WL, torch, dev)
+        result["other_rows"] = extra_rows(B, WL, torch, dev, [r for r in args.rows.split(",") if r])
 
     if not args.no_cpu:
         log("[bench] CPU oracle baseline ...")
-        result["cpu_baseline"] = cpu_baseline(wl, x_bits, w_bits)
+        from oracle import fp4_oracle as O
+
+        parity = {}
+        if wl.fmt == "mxfp4":
+            rows = np.unique(np.random.default_rng(19).choice(wl.M, min(wl.M, 64), replace=False))
+            parity[wl.name] = quant_parity_counts(O, x_bits, wl.block, wl.fmt, step_codes, step_scales, rows)
+        if args.stress and stress_out[0].fmt == "mxfp4":
+            sw, srows, sxr, scodes, sscales = stress_out
+            parity[sw.name] = quant_parity_counts(O, sxr, sw.block, sw.fmt, scodes, sscales, np.arange(len(srows)))
+            parity[sw.name]["rows"] = "64 rows drawn with seed 17"
+        log(f"[bench] parity counts on sampled rows: {parity}")
+        result["cpu_baseline"] = cpu_baseline(wl, x_bits, w_bits, rq_cpu, parity)
         log(f"[bench] CPU oracle: {result['cpu_baseline']['seconds']:.2f} s per step")
 
     print(json.dumps(result), flush=True)

@@ -31,23 +31,55 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in json.loads(r.stdout.strip())["error"]
 
 
-def traffic_keys():
-    with open(os.path.join(ROOT, "bench.py")) as f:
-        return re.findall(r'measured_traffic\("(\w+)", "([\w.]+)"', f.read())
-
-
 def test_committed_traffic_is_current():
     # every traffic figure the bench reports comes from counters taken on the kernel source as it is now
+    import bench_profiles
+
     table = load("traffic.json")
-    pairs = traffic_keys()
-    assert len(pairs) >= 8
-    for key, src in pairs:
+    assert len(bench_profiles.TRAFFIC_MAP) >= 10
+    for kernel, grid, key, src, _ in bench_profiles.TRAFFIC_MAP:
         assert key in table, key
         e = table[key]
+        assert (e["kernel"], e["grid"]) == (kernel, grid)
         assert e["source_sha"] == bench.source_sha(src), f"{key}: counters taken on another {src}"
         assert e["bytes_per_launch"] == pytest.approx(e["read_bytes"] + e["write_bytes"])
         assert bench.measured_traffic(key, src) == pytest.approx(e["bytes_per_launch"])
     assert bench.measured_traffic("no_such_kernel", "gemm_mxfp4_ring.hip") is None
+
+
+def test_bench_traffic_lookups_are_in_the_map():
+    # the literal keys bench.py looks up are ones the profiling pipeline measures
+    import bench_profiles
+
+    keys = {k for _, _, k, _, _ in bench_profiles.TRAFFIC_MAP}
+    with open(os.path.join(ROOT, "bench.py")) as f:
+        lits = re.findall(r'measured_traffic\("([\w@]+)",', f.read())
+    assert len(lits) >= 6
+    assert set(lits) <= keys, set(lits) - keys
+    assert {"gemm_mxfp4_ring@prefill_mx", "rotate_quant_mx@stress_mx32", "gemm_mxfp4_decode@decode",
+            "gemm_mxfp4_decode@decode_wide"} <= keys
+
+
+def test_roofline_kernel_follows_the_library_dispatch():
+    # the kernel fp4_linear runs for each workload (16-byte-aligned scales): decode kernel for M <= 16
+    # with K % 512 == 0, the 256-row-tile kernels for M, N >= 256, the general kernels otherwise
+    from microscaling_fp4_quantized_amd import workloads as WL
+
+    want = {"tiny": "gemm_mxfp4_kernel", "decode1": "gemm_mxfp4_decode", "decode4": "gemm_mxfp4_decode",
+            "decode16": "gemm_mxfp4_decode", "decode_wide1": "gemm_mxfp4_decode",
+            "decode_wide4": "gemm_mxfp4_decode", "decode_wide16": "gemm_mxfp4_decode",
+            "prefill_nv": "gemm_nvfp4_ring", "prefill_mx": "gemm_mxfp4_ring", "prefill_mx_m4096": "gemm_mxfp4_ring",
+            "large": "gemm_mxfp4_ring"}
+    for name, w in WL.WORKLOADS.items():
+        if w.N == 0:
+            continue
+        src, kern = bench.gemm_kernel_for(w.fmt, w.M, w.N, w.K)
+        assert kern == want[name], name
+        assert os.path.exists(os.path.join(ROOT, "microscaling_fp4_quantized_amd", "csrc", src))
+    assert bench.gemm_kernel_for("mxfp4", 16, 4096, 4224)[1] == "gemm_mxfp4_kernel"   # K % 512 != 0
+    assert bench.gemm_kernel_for("mxfp4", 17, 4096, 4096)[1] == "gemm_mxfp4_kernel"   # neither
+    assert bench.gemm_kernel_for("nvfp4", 16, 4096, 4096)[1] == "gemm_nvfp4_kernel"
+    assert bench.gemm_kernel_for("nvfp4", 256, 256, 64)[1] == "gemm_nvfp4_ring"
 
 
 def test_committed_bench_line_contract():
@@ -67,7 +99,9 @@ def test_committed_bench_line_contract():
     assert r["algorithmic_flops"] == pytest.approx(flops)
     assert r["achieved"] == pytest.approx(flops / (r["avg_launch_us"] * 1e-6) / 1e12, rel=1e-9)
     assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], rel=1e-9)
-    assert r["traffic"] == pytest.approx(load("traffic.json")["gemm_mxfp4_ring"]["bytes_per_launch"])
+    assert r["traffic"] == pytest.approx(load("traffic.json")["gemm_mxfp4_ring@prefill_mx"]["bytes_per_launch"])
+    h = r["w_from_hbm"]
+    assert h["frac"] == pytest.approx(flops / (h["avg_launch_us"] * 1e-6) / 1e12 / r["peak"], rel=1e-9)
     rq = d["roofline_rotate_quantize"]
     assert (rq["bound"], rq["unit"], rq["peak"]) == ("hbm", "GB/s", bench.HBM_PEAK_GBS)
     assert rq["algorithmic_bytes"] == 16384 * 8192 * (2 + 0.5 + 1 / 32)
@@ -75,6 +109,12 @@ def test_committed_bench_line_contract():
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["unit"] == "TFLOP/s" and c["cores"] >= 1 and c["sample"]
     assert c["value"] == pytest.approx(flops / c["seconds"] / 1e12, rel=1e-6)
+    assert c["host"]["cpu_model"] and c["host"]["cpu_count"] >= 1
+    q = c["rotate_quantize"]
+    assert q["unit"] == "GB/s" and q["cores"] >= 1 and q["GB/s"] == pytest.approx(
+        q["algorithmic_bytes"] / q["seconds"] / 1e9, rel=1e-9)
+    for name, p in c["parity_counts"].items():  # the bench input's sampled rows: no unflagged difference
+        assert p["rows_checked"] > 0 and p["code_mismatch_unflagged"] == 0 and p["scale_mismatch_unflagged"] == 0
 
 
 def trace_line(kernel, grid):
