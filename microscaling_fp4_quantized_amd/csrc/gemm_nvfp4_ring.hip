@@ -18,9 +18,9 @@
 //    stage, the DMA of stage s+1 issued in four parts across the k-blocks of stage s.
 //  * Each wave reads its fragments as 16 bytes (32 codes of one row) per lane and
 //    dequantizes them in registers right before the MFMAs: one packed convert per code
-//    byte (v_cvt_scalef32_pk_f16_fp4, scale 256) and one packed multiply by the group
-//    scale d * 2^-8 as fp16 (the E4M3 magnitude bits shifted left by 7 are exactly that
-//    fp16 pattern, subnormals included; the sign goes to bit 15).
+//    byte (v_cvt_scalef32_pk_f16_fp4) and one packed multiply by the group scale d, itself
+//    converted exactly from E4M3 to an fp16 pair by one v_cvt_scalef32_pk_f16_fp8 per two
+//    groups (the lane's two scale bytes of two blocks are gathered into one dword per stage).
 //  * K order within a 64-element block: lane half h holds elements 32h .. 32h + 31, and
 //    MFMA k-step j takes elements 32h + 8j .. + 7 from lane half h, for both operands. Every
 //    product still pairs x_k with w_k, and the block's sum is unchanged up to the order of
@@ -100,23 +100,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const uint8_t* bas
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// Two E4M3 scale bytes (bits 0-7 and 8-15 of b) -> the fp16 pair (d0 * 2^-8, d1 * 2^-8): an E4M3
-// code's seven magnitude bits shifted left by 7 are the fp16 bit pattern of d * 2^-8 (E4M3's
-// exponent bias is 7, fp16's is 15; E4M3 subnormals land on fp16 subnormals), its sign goes to
-// bit 15. Both halves at once: the second byte moves up to bit 16 first.
-__device__ __forceinline__ h2 e4m3_pair2(unsigned b) {
-  const unsigned y = (b & 0xFFu) | ((b & 0xFF00u) << 8);
-  return __builtin_bit_cast(h2, ((y & 0x007F007Fu) << 7) | ((y & 0x00800080u) << 8));
+// Two E4M3 scale bytes (word W of w) -> the exact fp16 pair (d0, d1): every E4M3FN value,
+// subnormals included, is an fp16 number, and the gfx950 FP8 convert with a unit scale gives it.
+template <bool W>
+__device__ __forceinline__ h2 e4m3_pair(unsigned w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, W);
 }
 
 // Eight E2M1 codes (one dword, element 2q in the low nibble of byte q) -> eight exact fp16
-// e2m1 * d: (e2m1 * 256) * (d * 2^-8).
+// e2m1 * d: a packed convert per code byte, then a packed multiply by the group scale (the
+// product has at most 6 significant bits and lies in [2^-10, 2688]).
 __device__ __forceinline__ v8h dequant8(unsigned codes, h2 dd) {
   v4u o;
-  o[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * dd);
-  o[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * dd);
-  o[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * dd);
-  o[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * dd);
+  o[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * dd);
+  o[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * dd);
+  o[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * dd);
+  o[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * dd);
   return __builtin_bit_cast(v8h, o);
 }
 
@@ -194,7 +193,7 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int fr = lane & 31, fh = lane >> 5;
-  const unsigned sh = 16u * (unsigned)fh;  // lane half h uses scale bytes 2h, 2h + 1 of each block's dword
+  const unsigned psel = fh ? 0x07060302u : 0x05040100u;  // bytes 2h, 2h + 1 of two dwords
 
   // Stage s: wait for its DMA (this wave's, then everyone's at the barrier), then multiply it
   // while the parts of stage s+1 refill the buffers of stage s-1, which every wave has finished
@@ -205,11 +204,21 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
     ring_barrier();
     const uint8_t* buf = smem + (s & 1) * STAGE;
     const uint8_t* sbuf = scl + (s & 1) * SC;
-    v4u sg_a[FM], sg_b[FN];  // the rows' 16 scale bytes of the stage (4 per 64-element block)
+    // the lane's scale bytes of the stage: of each block's four (one dword), the two of its lane
+    // half, gathered as word kb % 2 of dword kb / 2
+    unsigned sg_a[FM][2], sg_b[FN][2];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) sg_a[i] = *reinterpret_cast<const v4u*>(sbuf + (wm0 + i * 32 + fr) * SCB);
+    for (int i = 0; i < FM; ++i) {
+      const v4u t = *reinterpret_cast<const v4u*>(sbuf + (wm0 + i * 32 + fr) * SCB);
+      sg_a[i][0] = __builtin_amdgcn_perm(t[1], t[0], psel);
+      sg_a[i][1] = __builtin_amdgcn_perm(t[3], t[2], psel);
+    }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) sg_b[j] = *reinterpret_cast<const v4u*>(sbuf + (BM + wn0 + j * 32 + fr) * SCB);
+    for (int j = 0; j < FN; ++j) {
+      const v4u t = *reinterpret_cast<const v4u*>(sbuf + (BM + wn0 + j * 32 + fr) * SCB);
+      sg_b[j][0] = __builtin_amdgcn_perm(t[1], t[0], psel);
+      sg_b[j][1] = __builtin_amdgcn_perm(t[3], t[2], psel);
+    }
 #pragma unroll
     for (int kb = 0; kb < KBLK; ++kb) {
       if constexpr (decltype(with_dma)::value) issue_part(s + 1, kb);
@@ -228,9 +237,9 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
       // group scales of the lane's two 16-element groups of block kb (groups 4 kb + 2h and + 1)
       h2 da[FM], db[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) da[i] = e4m3_pair2(sg_a[i][kb] >> sh);
+      for (int i = 0; i < FM; ++i) da[i] = (kb & 1) ? e4m3_pair<true>(sg_a[i][kb / 2]) : e4m3_pair<false>(sg_a[i][kb / 2]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) db[j] = e4m3_pair2(sg_b[j][kb] >> sh);
+      for (int j = 0; j < FN; ++j) db[j] = (kb & 1) ? e4m3_pair<true>(sg_b[j][kb / 2]) : e4m3_pair<false>(sg_b[j][kb / 2]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {  // k-step t: dword t of the chunk (elements 32h + 8t .. + 7)
         v8h a[FM], b[FN];
