@@ -7,23 +7,26 @@
 // large operand and the product is bound by reading W from HBM.
 //
 // Design for CDNA4 (measured on MI355X with W streamed from HBM):
-//  * One workgroup owns T tiles of 16 output features (16 rows of W each) and all of K. Its
-//    8 waves read each tile as whole 1 KB pieces of contiguous W bytes (one 16-byte load per
-//    lane), the pattern a plain HBM stream uses: loading W straight in the MFMA operand layout
-//    touches 16 rows x 64 bytes per instruction and streamed about 20% slower.
-//  * The loaded pieces go to LDS with 16-byte chunk c of row r stored at slot c ^ (r & 15) of its
-//    256-byte segment, so the MFMA reads of 16 rows (one chunk each) hit distinct banks. One
-//    workgroup barrier, then each wave multiplies its slice of K (4 steps of 128) with
+//  * One workgroup owns T tiles of 16 output features (16 rows of W each) and all of K; its 8
+//    waves split K into slices of 512 elements (256 code bytes of a row), slice s going to wave
+//    s % 8. Each wave fetches its own slices straight into its own LDS area with the LDS DMA
+//    (buffer_load_dwordx4 ... lds): one instruction per 4 rows x 256 contiguous bytes, a pattern
+//    that streams from HBM nearly as well as whole 1 KB rows (loading W in the MFMA operand
+//    layout, 16 rows x 64 bytes per instruction, streamed about 20% slower). Lane l of an
+//    instruction fetches chunk (l % 16) ^ row of its row, so the fragment reads hit distinct banks.
+//  * As soon as its own slices have landed, the wave multiplies them with
 //    v_mfma_scale_f32_16x16x128_f8f6f4, W as the row operand and X as the column operand: lane l
-//    carries row l % 16 and the 32-element group l / 16 of the step (16 bytes of codes, one E8M0
-//    byte), so the output fragment gives each lane 4 consecutive features of one token. X (a few
-//    rows, resident in L2) is read per lane in that layout.
-//  * K is staged in chunks of at most 4096 elements; the next chunk's loads are in flight while
-//    the current one is multiplied. The waves' partial sums are reduced through LDS in a fixed
-//    order.
+//    carries row l % 16 and the 32-element group l / 16 of a 128-wide K step (16 bytes of codes,
+//    one E8M0 byte), so the output fragment gives each lane 4 consecutive features of one token.
+//    X (a few rows, resident in L2) and the E8M0 bytes are read per lane in that layout. No
+//    workgroup barrier stands between a wave's data and its products; the waves' partial sums
+//    meet once, through LDS, in a fixed order.
 //  * T = 2 when there are at least three tiles per CU: the two tiles share every X fragment the
 //    wave loads, which halves the X traffic that dominates at 16 tokens, and the half-size grid is
 //    resident at once (two workgroups per CU).
+//  * Layers whose slices do not fit the LDS area (K above 8192 / T) take a chunked variant: the
+//    workgroup stages W through LDS in chunks of at most 4096 elements as whole 1 KB row pieces,
+//    the next chunk's loads in flight while the current one is multiplied.
 //  X rows past M repeat row M-1 and W rows past N repeat row N-1; their outputs are discarded.
 #include <atomic>
 
@@ -174,9 +177,103 @@ __device__ __forceinline__ void decode_reduce_store(uint8_t* lds, const v4f (&ac
   store_out<OUT_BF16>(Yv, M, N, lane & 15, nb + 16 * tt + 4 * (lane >> 4), sum);
 }
 
-// At most 128 VGPRs (4 waves per SIMD), so that two workgroups share a CU.
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kDecSlice = 512;  // K elements of a wave's slice: 256 code bytes and 16 E8M0 bytes of a row
+constexpr int kDecMaxSlices = 2;  // tile-slices (4 KB each) a wave holds in LDS at once
+
+// At most 128 VGPRs (4 waves per SIMD), so that two workgroups share a CU. NPER (1 or 2): slices
+// per wave; wave w takes slices w and w + 8. LDS: 8 waves x NPER x T x 4 KB.
 template <bool OUT_BF16, int T>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemm_mxfp4_decode(
+    const uint8_t* __restrict__ Xq, const uint8_t* __restrict__ Xs, const uint8_t* __restrict__ Wq,
+    const uint8_t* __restrict__ Ws, void* __restrict__ Yv, int M, int N, int K, int NPER) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const unsigned KB = (unsigned)K / 2, KS = (unsigned)K / 32;
+  const int nsl = K / kDecSlice;
+  const int nb = blockIdx.x * 16 * T;
+  const int area_bytes = NPER * T * 4096;
+  uint8_t* area = lds + wave * area_bytes;  // tile-slice (j, tt) at (j * T + tt) * 4 KB: 16 rows x 256 bytes
+  const size_t xrow = (size_t)min(r, M - 1);
+
+  // W of the wave's slices into its area: instruction i of a tile-slice carries rows 4i .. 4i+3;
+  // lane l lands at byte 16 * (l % 16) of row 4i + l / 16 and fetches the row's 16-byte chunk
+  // (l % 16) ^ row there. Buffer loads over each tile's rows (32-bit offsets; rows past N read as
+  // zero, and their outputs are discarded). The rows' E8M0 bytes of a slice go to registers.
+  v4u wsv[kDecMaxSlices][T];
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) {
+    const int n0 = __builtin_amdgcn_readfirstlane(min(nb + 16 * tt, N - 1));
+    const unsigned rows = (unsigned)__builtin_amdgcn_readfirstlane(min(16, N - n0));
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(Wq + (size_t)n0 * KB, rows * KB);
+    const size_t wrow = (size_t)min(n0 + r, N - 1);
+#pragma unroll
+    for (int j = 0; j < kDecMaxSlices; ++j) {
+      const int sl = wave + 8 * j;
+      if (j < NPER && sl < nsl) {  // wave-uniform
+        uint8_t* dst = area + (j * T + tt) * 4096;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 4 * i + (lane >> 4), q = lane & 15;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(dst + i * 1024), 16,
+                                                   (unsigned)row * KB + (unsigned)sl * 256u + 16u * (unsigned)(q ^ row),
+                                                   0, 0, 0);
+        }
+        wsv[j][tt] = *reinterpret_cast<const v4u*>(Ws + wrow * KS + (size_t)sl * 16);
+      }
+    }
+  }
+  v4f acc[T];
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) acc[tt] = v4f{0.f, 0.f, 0.f, 0.f};
+  const unsigned sh = 8u * (unsigned)g;
+#pragma unroll
+  for (int j = 0; j < kDecMaxSlices; ++j) {
+    const int sl = wave + 8 * j;
+    if (j < NPER && sl < nsl) {
+      v4u xb[kDecBatch];
+#pragma unroll
+      for (int u = 0; u < kDecBatch; ++u)
+        xb[u] = *reinterpret_cast<const v4u*>(Xq + xrow * KB + (size_t)sl * 256 + 64 * u + 16 * g);
+      const v4u xsv = *reinterpret_cast<const v4u*>(Xs + xrow * KS + (size_t)sl * 16);
+      // this wave's DMA has landed (its area is read by no other wave until the reduction)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      asm volatile("" ::: "memory");
+      v4u wf[T][kDecBatch];  // every fragment read first, then the products
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+        for (int u = 0; u < kDecBatch; ++u)
+          wf[tt][u] = *reinterpret_cast<const v4u*>(area + (j * T + tt) * 4096 + r * 256 + 16 * (((4 * u + g) ^ r) & 15));
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+        for (int u = 0; u < kDecBatch; ++u) {
+          const v8i a = v8i{(int)wf[tt][u][0], (int)wf[tt][u][1], (int)wf[tt][u][2], (int)wf[tt][u][3], 0, 0, 0, 0};
+          const v8i b = v8i{(int)xb[u][0], (int)xb[u][1], (int)xb[u][2], (int)xb[u][3], 0, 0, 0, 0};
+          acc[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[tt], 4, 4, 0, (int)(wsv[j][tt][u] >> sh), 0,
+                                                                      (int)(xsv[u] >> sh));
+        }
+    }
+  }
+  // partial sums into the wave's own area (its fragment reads are done), then the fixed-order sum
+  v4f* red = reinterpret_cast<v4f*>(area);
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) red[tt * 64 + lane] = acc[tt];
+  __syncthreads();
+  if (wave >= T) return;
+  const int tt = wave;
+  v4f sum = reinterpret_cast<const v4f*>(lds)[tt * 64 + lane];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) sum += reinterpret_cast<const v4f*>(lds + w * area_bytes)[tt * 64 + lane];
+  // lane holds D[n + 4g + i][m = r], i = 0..3: four consecutive features of token r
+  store_out<OUT_BF16>(Yv, M, N, lane & 15, nb + 16 * tt + 4 * (lane >> 4), sum);
+}
+
+// The chunked variant for long K. At most 128 VGPRs (4 waves per SIMD).
+template <bool OUT_BF16, int T>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemm_mxfp4_decode_chunked(
     const uint8_t* __restrict__ Xq, const uint8_t* __restrict__ Xs, const uint8_t* __restrict__ Wq,
     const uint8_t* __restrict__ Ws, void* __restrict__ Yv, int M, int N, int K, int KC) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -340,18 +437,26 @@ std::atomic<int> g_dec_cus[64];         // compute units per device, 0 until que
 
 template <bool OUT_BF16, int T>
 hipError_t launch_decode(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws, int M, int N, int K,
-                         int KC, void* Y, int dev, hipStream_t st) {
-  auto kern = gemm_mxfp4_decode<OUT_BF16, T>;
-  const int lds = T * (dec_tile_bytes(KC) > kDecWaves * 64 * 16 ? dec_tile_bytes(KC) : kDecWaves * 64 * 16);
+                         void* Y, int dev, hipStream_t st) {
+  const int nper = (K / kDecSlice + kDecWaves - 1) / kDecWaves;  // slices per wave
+  const bool sliced = nper <= kDecMaxSlices / T;
+  const int KC = dec_chunk(K);
+  auto kern = sliced ? gemm_mxfp4_decode<OUT_BF16, T> : gemm_mxfp4_decode_chunked<OUT_BF16, T>;
+  const int lds = sliced ? kDecWaves * nper * T * 4096
+                         : T * (dec_tile_bytes(KC) > kDecWaves * 64 * 16 ? dec_tile_bytes(KC) : kDecWaves * 64 * 16);
   const bool cached = dev >= 0 && dev < 64;
   if (!cached || !g_dec_attr[OUT_BF16][T - 1][dev].load(std::memory_order_acquire)) {
-    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_mxfp4_decode<OUT_BF16, T>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)gemm_mxfp4_decode_chunked<OUT_BF16, T>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     if (cached) g_dec_attr[OUT_BF16][T - 1][dev].store(1, std::memory_order_release);
   }
   const int tiles = (N + 15) / 16;
   hipLaunchKernelGGL(kern, dim3((unsigned)((tiles + T - 1) / T)), dim3(kDecThreads), lds, st, Xq, Xs, Wq, Ws, Y, M, N, K,
-                     KC);
+                     sliced ? nper : KC);
   return hipGetLastError();
 }
 }  // namespace
@@ -369,16 +474,15 @@ hipError_t fp4_launch_gemm_mxfp4_decode(const uint8_t* Xq, const uint8_t* Xs, co
     if (e != hipSuccess) return e;
     if (cached) fp4::g_dec_cus[dev].store(cus, std::memory_order_release);
   }
-  const int KC = fp4::dec_chunk(K);
   // two tiles per workgroup once there are at least three tiles per CU: the tiles share the X
   // fragments, and every workgroup is resident at once (two per CU at up to 128 VGPRs)
   const bool two = (N + 15) / 16 >= 3 * (int64_t)cus;
   const int m = (int)M, n = (int)N, k = (int)K;
   if (out_bf16)
-    return two ? fp4::launch_decode<true, 2>(Xq, Xs, Wq, Ws, m, n, k, KC, Y, dev, st)
-               : fp4::launch_decode<true, 1>(Xq, Xs, Wq, Ws, m, n, k, KC, Y, dev, st);
-  return two ? fp4::launch_decode<false, 2>(Xq, Xs, Wq, Ws, m, n, k, KC, Y, dev, st)
-             : fp4::launch_decode<false, 1>(Xq, Xs, Wq, Ws, m, n, k, KC, Y, dev, st);
+    return two ? fp4::launch_decode<true, 2>(Xq, Xs, Wq, Ws, m, n, k, Y, dev, st)
+               : fp4::launch_decode<true, 1>(Xq, Xs, Wq, Ws, m, n, k, Y, dev, st);
+  return two ? fp4::launch_decode<false, 2>(Xq, Xs, Wq, Ws, m, n, k, Y, dev, st)
+             : fp4::launch_decode<false, 1>(Xq, Xs, Wq, Ws, m, n, k, Y, dev, st);
 }
 
 bool fp4_decode_fused_fits(int64_t M, int64_t N, int64_t K) {

@@ -47,13 +47,16 @@ def test_unit_scales_bit_exact(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 77, 512), (5, 300, 1536), (16, 4096, 4096), (3, 130, 8192), (16, 18, 2560),
-                                   (9, 12300, 1024), (16, 12289, 4608), (8, 14336, 4096)])
+                                   (9, 12300, 1024), (16, 12289, 4608), (8, 14336, 4096), (4, 200, 12288),
+                                   (2, 33, 9216)])
 def test_decode_kernel_unit_scales_exact(M, N, K):
-    # M <= 16 with K % 512 == 0 runs the weight-streaming decode kernel: W staged through LDS in
-    # chunks of at most 4096 K (K = 8192: two chunks; K = 4608: three of 1536), 8 waves of 4 K
-    # steps each (K = 1536, 2560 leave some waves idle), LDS reduction; N % 16 != 0 leaves ragged
-    # weight rows; M >= 8 with N >= 3 * 16 * 256 puts two 16-row tiles in a workgroup (12300,
-    # 12289: the last workgroup's second tile is partly or wholly past N)
+    # M <= 16 with K % 512 == 0 runs the weight-streaming decode kernel: 8 waves, each fetching
+    # its own 512-wide K slices into LDS (K = 8192: two slices per wave; K = 512, 1536, 2560 leave
+    # some waves idle), LDS reduction; N % 16 != 0 leaves ragged weight rows; M >= 8 with
+    # N >= 3 * 16 * 256 puts two 16-row tiles in a workgroup (12300, 12289: the last workgroup's
+    # second tile is partly or wholly past N). Longer K takes the chunked variant: W staged
+    # through LDS in chunks of at most 4096 K (4608 with two tiles: three chunks of 1536; 12288:
+    # three of 4096; 9216: three of 3072).
     rng = np.random.default_rng(3 * M + N + K)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
