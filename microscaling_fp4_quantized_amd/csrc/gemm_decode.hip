@@ -395,30 +395,198 @@ __global__ __launch_bounds__(kDecThreads) void decode_fused(const uint16_t* __re
   decode_reduce_store<OUT_BF16, 1>(lds, acc, wave, lane, Yv, M, N, n0);  // X in LDS is dead after its first barrier
 }
 
+// Fused decode step for K up to 8192 / T: each wave first sends its W slices (as in
+// gemm_mxfp4_decode) to its LDS area with the LDS DMA, after requesting its first X chunks, so W
+// streams in while X is quantized; then every wave multiplies its slices with X fragments read from
+// LDS. With T = 2 a workgroup owns two 16-row tiles and quantizes X once for both.
+constexpr int kFusedPre = 2;  // phase-1 iterations whose X loads are issued before the W DMA
+
+template <int B, bool OUT_BF16, int T, int NPER>
+__global__ __launch_bounds__(kDecThreads) void decode_fused_sliced(const uint16_t* __restrict__ X, int64_t ldx,
+                                                                   const uint8_t* __restrict__ Wq,
+                                                                   const uint8_t* __restrict__ Ws, void* __restrict__ Yv,
+                                                                   int M, int N, int K) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const unsigned KB = (unsigned)K / 2, KS = (unsigned)K / 32;
+  const int pitch = (int)KB + 16;  // padded X code rows: distinct banks per row
+  const int nsl = K / kDecSlice;
+  const int nb = blockIdx.x * 16 * T;
+  constexpr int area_bytes = NPER * T * 4096;
+  uint8_t* area = lds + wave * area_bytes;
+  uint8_t* xq = lds + kDecWaves * area_bytes;  // [M][pitch]
+  uint8_t* xs = xq + (size_t)M * pitch;        // [M][KS]
+  const int total = M * (int)KS;
+
+  // phase-1 chunk c -> row c / KS, chunk c % KS. Quads of lanes hold the consecutive chunks of
+  // one Hadamard block (KS % 16 == 0, and the loop base is a multiple of 512), and whole quads
+  // are in or out of range together (total % 4 == 0). The first iterations' X loads go out
+  // before the W DMA, and every load below is issued unconditionally (lanes past the end load a
+  // clamped chunk, waves past the last slice an out-of-range one, which reads zeros without
+  // touching memory), so the wait for X counts exactly the later W loads and lets them fly.
+  v4u xr[kFusedPre][4];
+#pragma unroll
+  for (int it = 0; it < kFusedPre; ++it) {
+    const int c = min(it * kDecThreads + (int)threadIdx.x, total - 1);
+    const int row = c / (int)KS, cc = c - row * (int)KS;
+    const v4u* src = reinterpret_cast<const v4u*>(X + (size_t)row * (size_t)ldx + (size_t)cc * 32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xr[it][q] = src[q];
+  }
+  v4u wsv[NPER][T];
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) {
+    const int n0 = __builtin_amdgcn_readfirstlane(min(nb + 16 * tt, N - 1));
+    const unsigned rows = (unsigned)__builtin_amdgcn_readfirstlane(min(16, N - n0));
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(Wq + (size_t)n0 * KB, rows * KB);
+    const size_t wrow = (size_t)min(n0 + r, N - 1);
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+      const int sl = wave + 8 * j;
+      uint8_t* dst = area + (j * T + tt) * 4096;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * i + (lane >> 4), q = lane & 15;
+        const unsigned off = sl < nsl ? (unsigned)row * KB + (unsigned)sl * 256u + 16u * (unsigned)(q ^ row) : 0xFFFFFFF0u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(dst + i * 1024), 16, off, 0, 0, 0);
+      }
+      wsv[j][tt] = *reinterpret_cast<const v4u*>(Ws + wrow * KS + (size_t)min(sl, nsl - 1) * 16);
+    }
+  }
+
+  // phase 1: rotate and quantize X into LDS with the quantizer's own device code
+  for (int c0 = 0; c0 < total; c0 += kDecThreads) {
+    const int c = c0 + (int)threadIdx.x;
+    const int it = c0 / kDecThreads;
+    if (c < total) {
+      const int row = c / (int)KS, cc = c - row * (int)KS;
+      v4u x4[4];
+      if (it < kFusedPre) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x4[q] = it == 0 ? xr[0][q] : xr[kFusedPre - 1][q];
+      } else {
+        const v4u* src = reinterpret_cast<const v4u*>(X + (size_t)row * (size_t)ldx + (size_t)cc * 32);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x4[q] = src[q];
+      }
+      float v[32];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[8 * q + 2 * t] = bf16_lo(x4[q][t]);
+          v[8 * q + 2 * t + 1] = bf16_hi(x4[q][t]);
+        }
+      v4u out;
+      const int code = mx_rotate_quantize_chunk<B, kRuleStandard>(v, out);
+      *reinterpret_cast<v4u*>(xq + (size_t)row * pitch + (size_t)cc * 16) = out;
+      xs[(size_t)row * KS + cc] = (uint8_t)code;
+    }
+  }
+  __syncthreads();  // X is in LDS
+
+  // phase 2: this wave's slices once its DMA has landed
+  const uint8_t* xp = xq + (size_t)min(r, M - 1) * pitch + 16 * g;
+  const uint8_t* xsp = xs + (size_t)min(r, M - 1) * KS;
+  const unsigned sh = 8u * (unsigned)g;
+  v4f acc[T];
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) acc[tt] = v4f{0.f, 0.f, 0.f, 0.f};
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const int sl = wave + 8 * j;
+    if (sl < nsl) {
+      v4u xb[kDecBatch], wf[T][kDecBatch];
+#pragma unroll
+      for (int u = 0; u < kDecBatch; ++u) xb[u] = *reinterpret_cast<const v4u*>(xp + (size_t)sl * 256 + 64 * u);
+      const v4u xsv = *reinterpret_cast<const v4u*>(xsp + (size_t)sl * 16);
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+        for (int u = 0; u < kDecBatch; ++u)
+          wf[tt][u] = *reinterpret_cast<const v4u*>(area + (j * T + tt) * 4096 + r * 256 + 16 * (((4 * u + g) ^ r) & 15));
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+        for (int u = 0; u < kDecBatch; ++u) {
+          const v8i a = v8i{(int)wf[tt][u][0], (int)wf[tt][u][1], (int)wf[tt][u][2], (int)wf[tt][u][3], 0, 0, 0, 0};
+          const v8i b = v8i{(int)xb[u][0], (int)xb[u][1], (int)xb[u][2], (int)xb[u][3], 0, 0, 0, 0};
+          acc[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[tt], 4, 4, 0, (int)(wsv[j][tt][u] >> sh), 0,
+                                                                      (int)(xsv[u] >> sh));
+        }
+    }
+  }
+  v4f* red = reinterpret_cast<v4f*>(area);
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) red[tt * 64 + lane] = acc[tt];
+  __syncthreads();
+  if (wave >= T) return;
+  const int tt = wave;
+  v4f sum = reinterpret_cast<const v4f*>(lds)[tt * 64 + lane];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) sum += reinterpret_cast<const v4f*>(lds + w * area_bytes)[tt * 64 + lane];
+  store_out<OUT_BF16>(Yv, M, N, lane & 15, nb + 16 * tt + 4 * (lane >> 4), sum);
+}
+
 // X codes and scales; at least the 8 KB the reduction reuses
 size_t fused_lds_bytes(int M, int K) {
   const size_t x = (size_t)M * (K / 2 + 16) + (size_t)M * (K / 32);
   return x > (size_t)kDecWaves * 64 * 16 ? x : (size_t)kDecWaves * 64 * 16;
 }
 
-std::atomic<int> g_fused_attr[4][64];
+std::atomic<int> g_fused_attr[4][64];  // per block size and device: dynamic-LDS limits raised
+std::atomic<int> g_cus[64];            // compute units per device, 0 until queried
+
+hipError_t device_cus(int dev, int& cus) {
+  const bool cached = dev >= 0 && dev < 64;
+  cus = cached ? g_cus[dev].load(std::memory_order_acquire) : 0;
+  if (cus != 0) return hipSuccess;
+  const hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && cached) g_cus[dev].store(cus, std::memory_order_release);
+  return e;
+}
 
 template <int B>
 hipError_t launch_fused(const uint16_t* X, int64_t ldx, const uint8_t* Wq, const uint8_t* Ws, int M, int N, int K,
                         void* Y, int out_bf16, hipStream_t st) {
-  int dev = 0;
+  int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = device_cus(dev, cus);
   if (e != hipSuccess) return e;
-  auto kern = out_bf16 ? decode_fused<B, true> : decode_fused<B, false>;
   const int bi = B == 16 ? 0 : B == 32 ? 1 : B == 64 ? 2 : 3;
   const bool cached = dev >= 0 && dev < 64;
-  if (!cached || (g_fused_attr[bi][dev].load(std::memory_order_acquire) & (1 + out_bf16)) == 0) {
-    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    if (cached) g_fused_attr[bi][dev].fetch_or(1 + out_bf16, std::memory_order_acq_rel);
+  if (!cached || g_fused_attr[bi][dev].load(std::memory_order_acquire) == 0) {
+    const void* kerns[8] = {(const void*)decode_fused<B, false>, (const void*)decode_fused<B, true>,
+                            (const void*)decode_fused_sliced<B, false, 1, 1>, (const void*)decode_fused_sliced<B, true, 1, 1>,
+                            (const void*)decode_fused_sliced<B, false, 2, 1>, (const void*)decode_fused_sliced<B, true, 2, 1>,
+                            (const void*)decode_fused_sliced<B, false, 1, 2>, (const void*)decode_fused_sliced<B, true, 1, 2>};
+    for (const void* k : kerns) {
+      e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (e != hipSuccess) return e;
+    }
+    if (cached) g_fused_attr[bi][dev].store(1, std::memory_order_release);
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)((N + 15) / 16)), dim3(kDecThreads), fused_lds_bytes(M, K), st, X, ldx, Wq, Ws,
-                     Y, M, N, K);
+  // the sliced kernel when every wave's slices fit its LDS area beside X; two tiles per workgroup
+  // once there are at least three tiles per CU and two workgroups still fit a CU
+  const size_t xb = (size_t)M * (K / 2 + 16) + (size_t)M * (K / 32);
+  const int nper = (K / kDecSlice + kDecWaves - 1) / kDecWaves;
+  const int tiles = (N + 15) / 16;
+  if (nper <= kDecMaxSlices && (size_t)kDecWaves * nper * 4096 + xb <= 160 * 1024) {
+    const bool two = nper == 1 && tiles >= 3 * cus && (size_t)kDecWaves * 2 * 4096 + xb <= 80 * 1024;
+    const int T = two ? 2 : 1;
+    const size_t lds = (size_t)kDecWaves * nper * T * 4096 + xb;
+    auto kern = two         ? (out_bf16 ? decode_fused_sliced<B, true, 2, 1> : decode_fused_sliced<B, false, 2, 1>)
+                : nper == 1 ? (out_bf16 ? decode_fused_sliced<B, true, 1, 1> : decode_fused_sliced<B, false, 1, 1>)
+                            : (out_bf16 ? decode_fused_sliced<B, true, 1, 2> : decode_fused_sliced<B, false, 1, 2>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)((tiles + T - 1) / T)), dim3(kDecThreads), lds, st, X, ldx, Wq, Ws, Y, M, N, K);
+    return hipGetLastError();
+  }
+  auto kern = out_bf16 ? decode_fused<B, true> : decode_fused<B, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kDecThreads), fused_lds_bytes(M, K), st, X, ldx, Wq, Ws, Y, M, N,
+                     K);
   return hipGetLastError();
 }
 
@@ -433,7 +601,6 @@ bool fp4_gemm_mxfp4_decode_fits(int64_t M, int64_t N, int64_t K) {
 namespace fp4 {
 namespace {
 std::atomic<int> g_dec_attr[2][2][64];  // per output dtype, T and device: dynamic-LDS limit raised
-std::atomic<int> g_dec_cus[64];         // compute units per device, 0 until queried
 
 template <bool OUT_BF16, int T>
 hipError_t launch_decode(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws, int M, int N, int K,
@@ -467,13 +634,9 @@ hipError_t fp4_launch_gemm_mxfp4_decode(const uint8_t* Xq, const uint8_t* Xs, co
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  const bool cached = dev >= 0 && dev < 64;
-  int cus = cached ? fp4::g_dec_cus[dev].load(std::memory_order_acquire) : 0;
-  if (cus == 0) {
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    if (cached) fp4::g_dec_cus[dev].store(cus, std::memory_order_release);
-  }
+  int cus = 0;
+  e = fp4::device_cus(dev, cus);
+  if (e != hipSuccess) return e;
   // two tiles per workgroup once there are at least three tiles per CU: the tiles share the X
   // fragments, and every workgroup is resident at once (two per CU at up to 128 VGPRs)
   const bool two = (N + 15) / 16 >= 3 * (int64_t)cus;

@@ -301,7 +301,8 @@ def test_full_size_sampled(name):
 
 
 @pytest.mark.parametrize("M,N,K,block", [(1, 4096, 4096, 32), (4, 300, 512, 128), (16, 4096, 4096, 32),
-                                         (7, 77, 2048, 16), (16, 520, 1536, 64), (3, 64, 8192, 128)])
+                                         (7, 77, 2048, 16), (16, 520, 1536, 64), (3, 64, 8192, 128),
+                                         (2, 14336, 4096, 32), (5, 12300, 4096, 64), (2, 100, 9216, 32)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_fused_decode_equals_two_calls(M, N, K, block, out_dtype):
     # the one-launch decode step gives the same bits as fp4_rotate_quantize + fp4_linear, and
