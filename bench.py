@@ -464,9 +464,11 @@ def decode_rows(B, WL, torch, dev, names=("decode1", "decode4", "decode16", "dec
             B.fp4_rotate_quantize(xb, wl.block, "mxfp4", out=xqo)
             B.fp4_linear(xqo[0], xqo[1], w_i[0], w_i[1], "mxfp4", out=y2)
 
+        ws_buf = torch.empty(B.linear_workspace_bytes(wl.M, wl.K), dtype=torch.uint8, device=dev)
+
         def fused(i):
             w_i = sets[i % n_sets]
-            B.fp4_rotate_quantize_linear(xb, w_i[0], w_i[1], wl.block, out=y)
+            B.fp4_rotate_quantize_linear(xb, w_i[0], w_i[1], wl.block, out=y, workspace=ws_buf)
 
         ms_two = time_graph(two_calls, calls, torch)
         ms_fused = time_graph(fused, calls, torch)

@@ -33,6 +33,7 @@
 #ifndef FP4_MI355X_H
 #define FP4_MI355X_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -198,16 +199,19 @@ FP4_API int fp4_linear(const uint8_t *Xq, const uint8_t *Xs, const float *x_ts,
                void *Y, int y_dtype, void *stream);
 
 /*
- * fp4_rotate_quantize_linear - one launch for the decode step of an MXFP4 linear layer:
+ * fp4_rotate_quantize_linear - the decode step of an MXFP4 linear layer:
  * Y = fp4_linear(fp4_rotate_quantize(X, block, MXFP4), Wq, Ws), bit for bit the same as
- * the two calls (the same device code quantizes X, into on-chip memory instead of HBM).
- * Every workgroup quantizes the whole of X, so it is meant for a few tokens: on
- * MI355X (K = N = 4096) one token takes 4.1 us against 5.6 us for the two calls,
- * while at 16 tokens the redundant quantization makes it slower (8.2 against 7.5 us).
- * "Bridging the Gap Between Promise and Performance for Microscaling FP4 Quantization"
- * (gist.science, German edition), Technische Zusammenfassung §2
+ * the two calls. "Bridging the Gap Between Promise and Performance for Microscaling FP4
+ * Quantization" (gist.science, German edition), Technische Zusammenfassung §2
  * "GPU-Kernel-Unterstützung (QuTLASS)": the online rotation fused with quantization,
  * feeding the 4-bit matmul.
+ * Normally one launch: every workgroup quantizes the whole of X into on-chip memory with
+ * the quantizer's own device code, while its W streams in. That pays off for a few tokens
+ * (MI355X, W from HBM: 1 token on N = 14336, K = 4096 in 8.8 us against 10.7 us for the two
+ * calls). With many rows of X per CU (M times the workgroups per CU, above about 14) the
+ * repeated quantization costs more than a second launch; given a workspace, the call then
+ * quantizes X once into it and runs the decode GEMM (two launches on `stream`; 16 tokens on
+ * N = 14336: 12.1 us instead of 20.9 us for one launch).
  *
  *  X       device bf16 [M, ldx], 16-byte aligned, ldx >= K, ldx % 8 == 0.
  *  M       1..16 tokens.   K: a multiple of 512 with M * (K/2 + 16 + K/32) <= 160 KiB.
@@ -215,12 +219,18 @@ FP4_API int fp4_linear(const uint8_t *Xq, const uint8_t *Xs, const float *x_ts,
  *  Wq, Ws  MXFP4 weights from fp4_quantize_weights: uint8 [N, K/2] and [N, K/32], both
  *          16-byte aligned (16 scale bytes of a row are read at once).
  *  Y       device [M, N], float32 or bf16 (y_dtype), 16-byte aligned.
- * Errors: FP4_E_BLOCK, FP4_E_FORMAT (y_dtype), FP4_E_NULLPTR, FP4_E_SHAPE (M, K, ldx or
- * the on-chip size), FP4_E_ALIGN. One kernel launch on `stream`.
+ *  workspace, workspace_bytes  NULL (always one launch), or a 16-byte-aligned device buffer
+ *          of at least FP4_LINEAR_WORKSPACE_BYTES(M, K) bytes, owned by the caller and
+ *          free for the call's duration on `stream` (its contents afterwards: X's codes,
+ *          then its scales at FP4_LINEAR_WORKSPACE_CODES(M, K), when two launches ran).
+ * Errors: FP4_E_BLOCK, FP4_E_FORMAT (y_dtype), FP4_E_NULLPTR, FP4_E_SHAPE (M, K, ldx, the
+ * on-chip size or a short workspace), FP4_E_ALIGN.
  */
+#define FP4_LINEAR_WORKSPACE_CODES(M, K) ((((M) * (K) / 2 + 255) / 256) * 256)
+#define FP4_LINEAR_WORKSPACE_BYTES(M, K) (FP4_LINEAR_WORKSPACE_CODES(M, K) + (M) * (K) / 32)
 FP4_API int fp4_rotate_quantize_linear(const void *X, int64_t M, int64_t K, int64_t ldx, int block,
                                        const uint8_t *Wq, const uint8_t *Ws, int64_t N, void *Y, int y_dtype,
-                                       void *stream);
+                                       void *workspace, size_t workspace_bytes, void *stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 FP4_API const char *fp4_last_error(void);

@@ -22,6 +22,7 @@ __all__ = [
     "fp4_quantize_weights",
     "fp4_linear",
     "fp4_rotate_quantize_linear",
+    "linear_workspace_bytes",
     "fp4_abi_version",
     "group_size",
 ]
@@ -66,7 +67,7 @@ def load_library() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = qx_args
         f.restype = i32
-    lib.fp4_rotate_quantize_linear.argtypes = [vp, i64, i64, i64, i32, vp, vp, i64, vp, i32, vp]
+    lib.fp4_rotate_quantize_linear.argtypes = [vp, i64, i64, i64, i32, vp, vp, i64, vp, i32, vp, ctypes.c_size_t, vp]
     lib.fp4_rotate_quantize_linear.restype = i32
     lib.fp4_linear.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32, vp]
     lib.fp4_linear.restype = i32
@@ -217,8 +218,19 @@ def fp4_linear(xq, xs, wq, ws, fmt="mxfp4", x_ts=None, w_ts=None, out_dtype=torc
     return y
 
 
-def fp4_rotate_quantize_linear(x: torch.Tensor, wq, ws, block: int, out_dtype=torch.float32, out=None):
-    """One-launch decode step (MXFP4, 1 <= M <= 16): Y = fp4_linear(fp4_rotate_quantize(x), wq, ws)."""
+def linear_workspace_bytes(M: int, K: int) -> int:
+    """FP4_LINEAR_WORKSPACE_BYTES(M, K) of include/fp4.h: X's codes, then its scales at the next
+    256-byte boundary."""
+    return ((M * K // 2 + 255) // 256) * 256 + M * K // 32
+
+
+def fp4_rotate_quantize_linear(x: torch.Tensor, wq, ws, block: int, out_dtype=torch.float32, out=None,
+                               workspace="auto"):
+    """Decode step (MXFP4, 1 <= M <= 16): Y = fp4_linear(fp4_rotate_quantize(x), wq, ws).
+
+    workspace: "auto" allocates one of linear_workspace_bytes(M, K) bytes, which lets the library
+    take two launches where that is faster; None forces the one-launch kernel; or a contiguous
+    uint8 CUDA tensor of at least that size."""
     lib = load_library()
     if x.dim() != 2 or x.dtype != torch.bfloat16 or not x.is_cuda or x.stride(1) != 1:
         raise ValueError("fp4_rotate_quantize_linear: expects a 2-D bf16 CUDA tensor with unit column stride")
@@ -238,9 +250,22 @@ def fp4_rotate_quantize_linear(x: torch.Tensor, wq, ws, block: int, out_dtype=to
     else:
         _expect(out, (M, N), out_dtype, "fp4_rotate_quantize_linear", "out")
         y = out
-    _same_device("fp4_rotate_quantize_linear", x.device, wq, ws, y)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('fp4_rotate_quantize_linear: workspace must be "auto", None or a uint8 tensor')
+        workspace = torch.empty(linear_workspace_bytes(M, K), dtype=torch.uint8, device=x.device)
+    if workspace is None:
+        wsp, wsb = None, 0
+        _same_device("fp4_rotate_quantize_linear", x.device, wq, ws, y)
+    else:
+        if not workspace.is_cuda or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("fp4_rotate_quantize_linear: workspace must be a contiguous uint8 CUDA tensor")
+        if workspace.numel() < linear_workspace_bytes(M, K):
+            raise ValueError("fp4_rotate_quantize_linear: workspace too small")
+        wsp, wsb = _ptr(workspace), workspace.numel()
+        _same_device("fp4_rotate_quantize_linear", x.device, wq, ws, y, workspace)
     _check(_launch(x.device, lib.fp4_rotate_quantize_linear, _ptr(x), M, K, x.stride(0), int(block), _ptr(wq),
-                   _ptr(ws), N, _ptr(y), ydt))
+                   _ptr(ws), N, _ptr(y), ydt, wsp, wsb))
     return y
 
 

@@ -74,6 +74,29 @@ int quantize(const char* who, const void* X, int64_t M, int64_t K, int64_t ld, i
                                                   static_cast<hipStream_t>(stream)));
 }
 
+// The validated decode step: one fused launch, or, with a workspace and more rows of X per CU
+// than the fused kernel quantizes profitably, the quantizer into the workspace (codes, then the
+// E8M0 scales at the next 256-byte boundary) followed by the decode GEMM. Both give the same bits.
+int decode_step(const char* who, const void* X, int64_t M, int64_t K, int64_t ldx, int block, const uint8_t* Wq,
+                const uint8_t* Ws, int64_t N, void* Y, int y_dtype, uint8_t* ws, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16 = y_dtype == FP4_OUT_BF16;
+  bool fused = true;
+  if (ws) {
+    const hipError_t e = fp4_decode_fused_preferred(M, N, K, &fused);
+    if (e != hipSuccess) return launched(who, e);
+  }
+  if (fused)
+    return launched(who, fp4_launch_decode_fused(static_cast<const uint16_t*>(X), ldx, block, Wq, Ws, M, N, K, Y, bf16,
+                                                 st));
+  uint8_t* xq = ws;
+  uint8_t* xs = ws + FP4_LINEAR_WORKSPACE_CODES((size_t)M, (size_t)K);
+  hipError_t e = fp4_launch_rotate_quantize(static_cast<const uint16_t*>(X), M, K, ldx, block, FP4_MXFP4,
+                                            FP4_SCALE_STANDARD, false, nullptr, xq, xs, nullptr, st);
+  if (e == hipSuccess) e = fp4_launch_gemm_mxfp4_decode(xq, xs, Wq, Ws, M, N, K, Y, bf16, st);
+  return launched(who, e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -134,7 +157,8 @@ int fp4_linear(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const ui
 }
 
 int fp4_rotate_quantize_linear(const void* X, int64_t M, int64_t K, int64_t ldx, int block, const uint8_t* Wq,
-                               const uint8_t* Ws, int64_t N, void* Y, int y_dtype, void* stream) {
+                               const uint8_t* Ws, int64_t N, void* Y, int y_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   const char* who = "fp4_rotate_quantize_linear";
   if (block != 16 && block != 32 && block != 64 && block != 128)
     return fail(FP4_E_BLOCK, "%s: Hadamard block %d not in {16, 32, 64, 128}", who, block);
@@ -150,12 +174,15 @@ int fp4_rotate_quantize_linear(const void* X, int64_t M, int64_t K, int64_t ldx,
   if (!aligned(X, 16) || ldx % 8) return fail(FP4_E_ALIGN, "%s: X must be 16-byte aligned, ldx %% 8 == 0", who);
   if (!aligned(Wq, 16) || !aligned(Ws, 16) || !aligned(Y, 16))
     return fail(FP4_E_ALIGN, "%s: Wq, Ws and Y must be 16-byte aligned", who);
-  return launched(who, fp4_launch_decode_fused(static_cast<const uint16_t*>(X), ldx, block, Wq, Ws, M, N, K, Y,
-                                               y_dtype == FP4_OUT_BF16, static_cast<hipStream_t>(stream)));
+  const size_t need = FP4_LINEAR_WORKSPACE_BYTES((size_t)M, (size_t)K);
+  if (workspace && !aligned(workspace, 16)) return fail(FP4_E_ALIGN, "%s: workspace must be 16-byte aligned", who);
+  if (workspace && workspace_bytes < need)
+    return fail(FP4_E_SHAPE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes, need);
+  return decode_step(who, X, M, K, ldx, block, Wq, Ws, N, Y, y_dtype, static_cast<uint8_t*>(workspace), stream);
 }
 
 const char* fp4_last_error(void) { return g_err; }
 
-int fp4_abi_version(void) { return 120; }
+int fp4_abi_version(void) { return 130; }
 
 }  // extern "C"

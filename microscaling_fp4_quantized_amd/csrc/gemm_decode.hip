@@ -549,6 +549,29 @@ hipError_t device_cus(int dev, int& cus) {
   return e;
 }
 
+// Launch plan of the fused step: the sliced kernel when every wave's slices fit its LDS area
+// beside X; two tiles per workgroup once there are at least three tiles per CU and two
+// workgroups still fit a CU. Otherwise the register-streaming kernel, one tile per workgroup.
+struct FusedPlan {
+  bool sliced;
+  int T, nper, grid;
+  size_t lds;
+};
+
+FusedPlan fused_plan(int64_t M, int64_t N, int64_t K, int cus) {
+  const size_t xb = (size_t)M * (K / 2 + 16) + (size_t)M * (K / 32);
+  const int nper = (int)((K / kDecSlice + kDecWaves - 1) / kDecWaves);
+  const int tiles = (int)((N + 15) / 16);
+  FusedPlan p{false, 1, nper, tiles, fused_lds_bytes((int)M, (int)K)};
+  if (nper <= kDecMaxSlices && (size_t)kDecWaves * nper * 4096 + xb <= 160 * 1024) {
+    p.sliced = true;
+    p.T = nper == 1 && tiles >= 3 * cus && (size_t)kDecWaves * 2 * 4096 + xb <= 80 * 1024 ? 2 : 1;
+    p.grid = (tiles + p.T - 1) / p.T;
+    p.lds = (size_t)kDecWaves * nper * p.T * 4096 + xb;
+  }
+  return p;
+}
+
 template <int B>
 hipError_t launch_fused(const uint16_t* X, int64_t ldx, const uint8_t* Wq, const uint8_t* Ws, int M, int N, int K,
                         void* Y, int out_bf16, hipStream_t st) {
@@ -569,15 +592,12 @@ hipError_t launch_fused(const uint16_t* X, int64_t ldx, const uint8_t* Wq, const
     }
     if (cached) g_fused_attr[bi][dev].store(1, std::memory_order_release);
   }
-  // the sliced kernel when every wave's slices fit its LDS area beside X; two tiles per workgroup
-  // once there are at least three tiles per CU and two workgroups still fit a CU
-  const size_t xb = (size_t)M * (K / 2 + 16) + (size_t)M * (K / 32);
-  const int nper = (K / kDecSlice + kDecWaves - 1) / kDecWaves;
-  const int tiles = (N + 15) / 16;
-  if (nper <= kDecMaxSlices && (size_t)kDecWaves * nper * 4096 + xb <= 160 * 1024) {
-    const bool two = nper == 1 && tiles >= 3 * cus && (size_t)kDecWaves * 2 * 4096 + xb <= 80 * 1024;
-    const int T = two ? 2 : 1;
-    const size_t lds = (size_t)kDecWaves * nper * T * 4096 + xb;
+  const FusedPlan pl = fused_plan(M, N, K, cus);
+  const int tiles = (N + 15) / 16, nper = pl.nper;
+  if (pl.sliced) {
+    const bool two = pl.T == 2;
+    const int T = pl.T;
+    const size_t lds = pl.lds;
     auto kern = two         ? (out_bf16 ? decode_fused_sliced<B, true, 2, 1> : decode_fused_sliced<B, false, 2, 1>)
                 : nper == 1 ? (out_bf16 ? decode_fused_sliced<B, true, 1, 1> : decode_fused_sliced<B, false, 1, 1>)
                             : (out_bf16 ? decode_fused_sliced<B, true, 1, 2> : decode_fused_sliced<B, false, 1, 2>);
@@ -650,6 +670,22 @@ hipError_t fp4_launch_gemm_mxfp4_decode(const uint8_t* Xq, const uint8_t* Xs, co
 
 bool fp4_decode_fused_fits(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && M <= 16 && N >= 1 && K % 512 == 0 && fp4::fused_lds_bytes((int)M, (int)K) <= 160 * 1024;
+}
+
+// Every workgroup of the fused step quantizes all M rows of X, so its cost grows with the rows
+// quantized per CU, M times the workgroups per CU. Measured on MI355X with W from HBM, K = 4096
+// (one launch against two): N = 4096, one workgroup per CU, 12 tokens 6.9 against 7.3 us, 16
+// tokens 8.0 against 7.6 us; N = 14336, 1.75 workgroups per CU up to 7 tokens, 6 tokens 9.0
+// against 10.8 us, then 3.5 per CU, 8 tokens 12.3 against 11.0 us. The crossover lies near 14
+// rows per CU on both.
+hipError_t fp4_decode_fused_preferred(int64_t M, int64_t N, int64_t K, bool* fused) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = fp4::device_cus(dev, cus);
+  if (e != hipSuccess) return e;
+  const fp4::FusedPlan p = fp4::fused_plan(M, N, K, cus);
+  *fused = M * (int64_t)p.grid <= 14 * (int64_t)cus;
+  return hipSuccess;
 }
 
 hipError_t fp4_launch_decode_fused(const uint16_t* X, int64_t ldx, int block, const uint8_t* Wq, const uint8_t* Ws,

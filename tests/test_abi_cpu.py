@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, s)
     # nothing else with C linkage leaks out
     assert {s for s in exported if s.startswith("fp4_")} == set(declared_symbols())
-    assert lib.fp4_abi_version() == 120
+    assert lib.fp4_abi_version() == 130
 
 
 A16 = 0x10000  # a 16-byte aligned fake address: never dereferenced, validation fails first
@@ -105,8 +105,8 @@ def test_size_limits(lib):
     assert lib.fp4_linear(A16, A16, None, A16, A16, None, 4, 1 << 31, 128, 0, A16, 0, None) == -2
 
 
-def fused(lib, X=A16, M=4, K=512, ldx=512, block=32, Wq=A16, Ws=A16, N=64, Y=A16, ydt=0):
-    return lib.fp4_rotate_quantize_linear(X, M, K, ldx, block, Wq, Ws, N, Y, ydt, None)
+def fused(lib, X=A16, M=4, K=512, ldx=512, block=32, Wq=A16, Ws=A16, N=64, Y=A16, ydt=0, ws=None, wsb=0):
+    return lib.fp4_rotate_quantize_linear(X, M, K, ldx, block, Wq, Ws, N, Y, ydt, ws, wsb, None)
 
 
 def test_fused_decode_validation(lib):
@@ -122,6 +122,12 @@ def test_fused_decode_validation(lib):
     assert fused(lib, Y=A16 + 4) == -5
     assert fused(lib, Ws=A16 + 4) == -5                # 16 scale bytes are read at once
     assert b"fp4_rotate_quantize_linear" in lib.fp4_last_error()
+    # workspace: FP4_LINEAR_WORKSPACE_BYTES(4, 512) = 1024 codes + 64 scale bytes
+    assert binding.linear_workspace_bytes(4, 512) == 1088
+    assert binding.linear_workspace_bytes(3, 512) == 768 + 48
+    assert fused(lib, ws=A16, wsb=1087) == -2
+    assert b"workspace" in lib.fp4_last_error()
+    assert fused(lib, ws=A16 + 8, wsb=4096) == -5
 
 
 def lin(lib, Xq=A16, Xs=A16, xts=None, Wq=A16, Ws=A16, wts=None, M=4, N=4, K=128, fmt=0, Y=A16, ydt=0):

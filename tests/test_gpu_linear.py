@@ -315,9 +315,10 @@ def test_fused_decode_equals_two_calls(M, N, K, block, out_dtype):
     xd = dev_bf16(x)
     xq = B.fp4_rotate_quantize(xd, block, "mxfp4")
     y2 = B.fp4_linear(xq[0], xq[1], wq[0], wq[1], "mxfp4", out_dtype=out_dtype)
-    y1 = B.fp4_rotate_quantize_linear(xd, wq[0], wq[1], block, out_dtype=out_dtype)
+    y1 = B.fp4_rotate_quantize_linear(xd, wq[0], wq[1], block, out_dtype=out_dtype)  # may take two launches
+    y0 = B.fp4_rotate_quantize_linear(xd, wq[0], wq[1], block, out_dtype=out_dtype, workspace=None)  # one launch
     torch.cuda.synchronize()
-    assert torch.equal(y1, y2)
+    assert torch.equal(y1, y2) and torch.equal(y0, y2)
     ref = gemm_reference(x, wt, block, "mxfp4", np.arange(M), np.arange(N))
     if out_dtype == torch.bfloat16:
         ref = O.bf16_rne_f64(ref)
@@ -326,8 +327,9 @@ def test_fused_decode_equals_two_calls(M, N, K, block, out_dtype):
     assert r <= GEMM_REL_FRO_TOL
 
 
-def test_fused_decode_strided_x():
-    M, N, K = 5, 256, 1024
+@pytest.mark.parametrize("M,N", [(5, 256), (16, 4096)])  # one launch; two launches through the workspace
+def test_fused_decode_strided_x(M, N):
+    K = 1024
     x = WL.draw_normal_bf16((M, K), 1.0, seed=3)
     wt = WL.draw_normal_bf16((N, K), 0.02, seed=4)
     wide = torch.zeros((M, K + 64), dtype=torch.bfloat16, device="cuda")
