@@ -232,6 +232,23 @@ FP4_API int fp4_rotate_quantize_linear(const void *X, int64_t M, int64_t K, int6
                                        const uint8_t *Wq, const uint8_t *Ws, int64_t N, void *Y, int y_dtype,
                                        void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * fp4_rotate_quantize_linear_noalloc - fp4_rotate_quantize_linear for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments without the workspace, the same results. Where the
+ * workspace call would take two launches, this one uses an array of
+ * FP4_DECODE_SCRATCH_BYTES (160 KiB + 256) bytes in the library's own device image, one per
+ * GPU, held until the process ends; the call itself allocates nothing. That array is shared:
+ * calls that overlap on one GPU (other streams, other threads) race on it and must be
+ * serialized by the caller. Every size the decode step accepts fits it (FP4_E_SHAPE
+ * otherwise). Errors as fp4_rotate_quantize_linear, and FP4_E_HIP if the array's address
+ * cannot be obtained on the current device.
+ */
+#define FP4_DECODE_SCRATCH_BYTES (160 * 1024 + 256) /* >= every FP4_LINEAR_WORKSPACE_BYTES accepted */
+FP4_API int fp4_rotate_quantize_linear_noalloc(const void *X, int64_t M, int64_t K, int64_t ldx, int block,
+                                               const uint8_t *Wq, const uint8_t *Ws, int64_t N, void *Y,
+                                               int y_dtype, void *stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 FP4_API const char *fp4_last_error(void);
 

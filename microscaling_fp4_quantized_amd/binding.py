@@ -22,6 +22,7 @@ __all__ = [
     "fp4_quantize_weights",
     "fp4_linear",
     "fp4_rotate_quantize_linear",
+    "fp4_rotate_quantize_linear_noalloc",
     "linear_workspace_bytes",
     "fp4_abi_version",
     "group_size",
@@ -69,6 +70,8 @@ def load_library() -> ctypes.CDLL:
         f.restype = i32
     lib.fp4_rotate_quantize_linear.argtypes = [vp, i64, i64, i64, i32, vp, vp, i64, vp, i32, vp, ctypes.c_size_t, vp]
     lib.fp4_rotate_quantize_linear.restype = i32
+    lib.fp4_rotate_quantize_linear_noalloc.argtypes = [vp, i64, i64, i64, i32, vp, vp, i64, vp, i32, vp]
+    lib.fp4_rotate_quantize_linear_noalloc.restype = i32
     lib.fp4_linear.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32, vp]
     lib.fp4_linear.restype = i32
     lib.fp4_last_error.argtypes = []
@@ -266,6 +269,36 @@ def fp4_rotate_quantize_linear(x: torch.Tensor, wq, ws, block: int, out_dtype=to
         _same_device("fp4_rotate_quantize_linear", x.device, wq, ws, y, workspace)
     _check(_launch(x.device, lib.fp4_rotate_quantize_linear, _ptr(x), M, K, x.stride(0), int(block), _ptr(wq),
                    _ptr(ws), N, _ptr(y), ydt, wsp, wsb))
+    return y
+
+
+def fp4_rotate_quantize_linear_noalloc(x: torch.Tensor, wq, ws, block: int, out_dtype=torch.float32, out=None):
+    """The decode step through the allocation-free entry point: where two launches pay off, the
+    library uses its own per-GPU array instead of a workspace. Calls that overlap on one GPU race
+    on that array. With `out` given, nothing is allocated here either."""
+    lib = load_library()
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("fp4_rotate_quantize_linear_noalloc: expects a 2-D bf16 CUDA tensor with unit column stride")
+    for t in (wq, ws):
+        if not t.is_cuda or t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("fp4_rotate_quantize_linear_noalloc: weight codes and scales must be contiguous uint8 "
+                             "CUDA tensors")
+    M, K = x.shape
+    if wq.dim() != 2 or wq.shape[1] * 2 != K:
+        raise ValueError("fp4_rotate_quantize_linear_noalloc: X and W disagree on K")
+    N = wq.shape[0]
+    _expect(ws, (N, K // 32), torch.uint8, "fp4_rotate_quantize_linear_noalloc", "Ws")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("fp4_rotate_quantize_linear_noalloc: out_dtype must be torch.float32 or torch.bfloat16")
+    ydt = {torch.float32: 0, torch.bfloat16: 1}[out_dtype]
+    if out is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    else:
+        _expect(out, (M, N), out_dtype, "fp4_rotate_quantize_linear_noalloc", "out")
+        y = out
+    _same_device("fp4_rotate_quantize_linear_noalloc", x.device, wq, ws, y)
+    _check(_launch(x.device, lib.fp4_rotate_quantize_linear_noalloc, _ptr(x), M, K, x.stride(0), int(block),
+                   _ptr(wq), _ptr(ws), N, _ptr(y), ydt))
     return y
 
 

@@ -74,6 +74,7 @@ bool fp4_gemm_mxfp4_ring_fits(int64_t M, int64_t N, int64_t K);
 bool fp4_gemm_mxfp4_decode_fits(int64_t M, int64_t N, int64_t K);
 bool fp4_decode_fused_fits(int64_t M, int64_t N, int64_t K);
 hipError_t fp4_decode_fused_preferred(int64_t M, int64_t N, int64_t K, bool* fused);
+hipError_t fp4_decode_scratch(uint8_t** ptr);
 hipError_t fp4_launch_decode_fused(const uint16_t* X, int64_t ldx, int block, const uint8_t* Wq, const uint8_t* Ws,
                                    int64_t M, int64_t N, int64_t K, void* Y, int out_bf16, hipStream_t stream);
 hipError_t fp4_launch_gemm_mxfp4_decode(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,

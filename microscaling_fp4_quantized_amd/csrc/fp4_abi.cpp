@@ -74,6 +74,25 @@ int quantize(const char* who, const void* X, int64_t M, int64_t K, int64_t ld, i
                                                   static_cast<hipStream_t>(stream)));
 }
 
+int check_decode_step(const char* who, const void* X, int64_t M, int64_t K, int64_t ldx, int block,
+                      const uint8_t* Wq, const uint8_t* Ws, int64_t N, void* Y, int y_dtype) {
+  if (block != 16 && block != 32 && block != 64 && block != 128)
+    return fail(FP4_E_BLOCK, "%s: Hadamard block %d not in {16, 32, 64, 128}", who, block);
+  if (y_dtype != FP4_OUT_F32 && y_dtype != FP4_OUT_BF16)
+    return fail(FP4_E_FORMAT, "%s: unknown output dtype %d", who, y_dtype);
+  if (!X || !Wq || !Ws || !Y) return fail(FP4_E_NULLPTR, "%s: X, Wq, Ws and Y must be non-NULL", who);
+  if (M < 1 || M > 16 || N < 1 || K < 512 || K % 512 || N > 0x7FFFFFFF || K > 0x7FFFFFFF)
+    return fail(FP4_E_SHAPE, "%s: need 1 <= M <= 16, N >= 1 and K a positive multiple of 512 (M=%lld N=%lld K=%lld)",
+                who, (long long)M, (long long)N, (long long)K);
+  if (!fp4_decode_fused_fits(M, N, K))
+    return fail(FP4_E_SHAPE, "%s: M * K too large for the workgroup's LDS; use fp4_rotate_quantize + fp4_linear", who);
+  if (ldx < K || ldx > (int64_t)1 << 40) return fail(FP4_E_SHAPE, "%s: leading dimension %lld < K", who, (long long)ldx);
+  if (!aligned(X, 16) || ldx % 8) return fail(FP4_E_ALIGN, "%s: X must be 16-byte aligned, ldx %% 8 == 0", who);
+  if (!aligned(Wq, 16) || !aligned(Ws, 16) || !aligned(Y, 16))
+    return fail(FP4_E_ALIGN, "%s: Wq, Ws and Y must be 16-byte aligned", who);
+  return FP4_OK;
+}
+
 // The validated decode step: one fused launch, or, with a workspace and more rows of X per CU
 // than the fused kernel quantizes profitably, the quantizer into the workspace (codes, then the
 // E8M0 scales at the next 256-byte boundary) followed by the decode GEMM. Both give the same bits.
@@ -160,25 +179,29 @@ int fp4_rotate_quantize_linear(const void* X, int64_t M, int64_t K, int64_t ldx,
                                const uint8_t* Ws, int64_t N, void* Y, int y_dtype, void* workspace,
                                size_t workspace_bytes, void* stream) {
   const char* who = "fp4_rotate_quantize_linear";
-  if (block != 16 && block != 32 && block != 64 && block != 128)
-    return fail(FP4_E_BLOCK, "%s: Hadamard block %d not in {16, 32, 64, 128}", who, block);
-  if (y_dtype != FP4_OUT_F32 && y_dtype != FP4_OUT_BF16)
-    return fail(FP4_E_FORMAT, "%s: unknown output dtype %d", who, y_dtype);
-  if (!X || !Wq || !Ws || !Y) return fail(FP4_E_NULLPTR, "%s: X, Wq, Ws and Y must be non-NULL", who);
-  if (M < 1 || M > 16 || N < 1 || K < 512 || K % 512 || N > 0x7FFFFFFF || K > 0x7FFFFFFF)
-    return fail(FP4_E_SHAPE, "%s: need 1 <= M <= 16, N >= 1 and K a positive multiple of 512 (M=%lld N=%lld K=%lld)",
-                who, (long long)M, (long long)N, (long long)K);
-  if (!fp4_decode_fused_fits(M, N, K))
-    return fail(FP4_E_SHAPE, "%s: M * K too large for the workgroup's LDS; use fp4_rotate_quantize + fp4_linear", who);
-  if (ldx < K || ldx > (int64_t)1 << 40) return fail(FP4_E_SHAPE, "%s: leading dimension %lld < K", who, (long long)ldx);
-  if (!aligned(X, 16) || ldx % 8) return fail(FP4_E_ALIGN, "%s: X must be 16-byte aligned, ldx %% 8 == 0", who);
-  if (!aligned(Wq, 16) || !aligned(Ws, 16) || !aligned(Y, 16))
-    return fail(FP4_E_ALIGN, "%s: Wq, Ws and Y must be 16-byte aligned", who);
+  int st = check_decode_step(who, X, M, K, ldx, block, Wq, Ws, N, Y, y_dtype);
+  if (st != FP4_OK) return st;
   const size_t need = FP4_LINEAR_WORKSPACE_BYTES((size_t)M, (size_t)K);
   if (workspace && !aligned(workspace, 16)) return fail(FP4_E_ALIGN, "%s: workspace must be 16-byte aligned", who);
   if (workspace && workspace_bytes < need)
     return fail(FP4_E_SHAPE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes, need);
   return decode_step(who, X, M, K, ldx, block, Wq, Ws, N, Y, y_dtype, static_cast<uint8_t*>(workspace), stream);
+}
+
+int fp4_rotate_quantize_linear_noalloc(const void* X, int64_t M, int64_t K, int64_t ldx, int block,
+                                       const uint8_t* Wq, const uint8_t* Ws, int64_t N, void* Y, int y_dtype,
+                                       void* stream) {
+  const char* who = "fp4_rotate_quantize_linear_noalloc";
+  int st = check_decode_step(who, X, M, K, ldx, block, Wq, Ws, N, Y, y_dtype);
+  if (st != FP4_OK) return st;
+  const size_t need = FP4_LINEAR_WORKSPACE_BYTES((size_t)M, (size_t)K);
+  if (need > (size_t)FP4_DECODE_SCRATCH_BYTES)
+    return fail(FP4_E_SHAPE, "%s: needs %zu bytes of workspace, the library's array holds %zu", who, need,
+                (size_t)FP4_DECODE_SCRATCH_BYTES);
+  uint8_t* ws = nullptr;
+  const hipError_t e = fp4_decode_scratch(&ws);
+  if (e != hipSuccess) return launched(who, e);
+  return decode_step(who, X, M, K, ldx, block, Wq, Ws, N, Y, y_dtype, ws, stream);
 }
 
 const char* fp4_last_error(void) { return g_err; }

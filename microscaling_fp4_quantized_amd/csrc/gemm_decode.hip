@@ -30,6 +30,7 @@
 //  X rows past M repeat row M-1 and W rows past N repeat row N-1; their outputs are discarded.
 #include <atomic>
 
+#include "../../include/fp4.h"
 #include "quant_device.hpp"
 
 namespace fp4 {
@@ -678,6 +679,28 @@ bool fp4_decode_fused_fits(int64_t M, int64_t N, int64_t K) {
 // tokens 8.0 against 7.6 us; N = 14336, 1.75 workgroups per CU up to 7 tokens, 6 tokens 9.0
 // against 10.8 us, then 3.5 per CU, 8 tokens 12.3 against 11.0 us. The crossover lies near 14
 // rows per CU on both.
+// The allocation-free decode step's workspace: one array per GPU, in the library's device
+// image, held until the process ends. Host code uses the address hipGetSymbolAddress returns for
+// the current device (the array's name on the host is only a stand-in), fetched on the first call
+// on each device and kept.
+static __device__ __align__(256) uint8_t scratch[FP4_DECODE_SCRATCH_BYTES];
+static std::atomic<uint8_t*> g_scratch[64];
+
+hipError_t fp4_decode_scratch(uint8_t** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  uint8_t* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(reinterpret_cast<void**>(&p), HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 hipError_t fp4_decode_fused_preferred(int64_t M, int64_t N, int64_t K, bool* fused) {
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
