@@ -103,6 +103,18 @@ def time_batch(fn, iters, torch):
     return start.elapsed_time(end) / iters
 
 
+def ramp(fn, torch, seconds=0.1):
+    """Untimed calls of fn(i) for about `seconds`, so that the batch timed next runs at this
+    kernel's own steady clocks (the GPU sets its clock by the load it carries: right after a
+    different kernel, or after idling, the same kernel runs at another speed)."""
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def time_graph(fn, iters, torch):
     """Average device time (ms) per call of fn(i) with `iters` calls captured in one HIP graph and
     replayed between two events, so the host's launch rate does not bound kernels that run for a
@@ -279,6 +291,7 @@ def extra_rows(B, WL, torch, dev, groups=EXTRA_ROWS):
             B.fp4_rotate_quantize(bufs[i % 3], sw.block, "nvfp4", out=o)
     if "nv_stress" in groups:
         # NVFP4 rotate+quantize, 16384 x 8192, block 32: the max pass and the quantize pass
+        ramp(lambda i: B.fp4_rotate_quantize(bufs[i % 3], sw.block, "nvfp4", out=o), torch)
         ms = time_batch(lambda i: B.fp4_rotate_quantize(bufs[i % 3], sw.block, "nvfp4", out=o), 21, torch)
         nbytes = sw.M * sw.K * (2 + 2 + 0.5 + 1.0 / 16) + 8
         t_max = measured_traffic("rotate_amax@stress_nv32", "rotate_quant.hip")
@@ -307,8 +320,7 @@ def extra_rows(B, WL, torch, dev, groups=EXTRA_ROWS):
                 else:
                     B.fp4_rotate_quantize(bufs[i % 3], sw.block, fmt, out=oo, rule=rule, signs=sg)
 
-            for i in range(2):
-                call(i)
+            ramp(call, torch)
             ms = time_batch(call, 12, torch)
             nb = sw.M * sw.K * ((2 if fmt == "nvfp4" and rule != "given_scale" else 0) + 2 + 0.5 + 1.0 / g)
             name = f"{fmt}_{rule}" + ("_signs" if sg is not None else "")
@@ -328,8 +340,7 @@ def extra_rows(B, WL, torch, dev, groups=EXTRA_ROWS):
             def call128(i, fmt=fmt, oo=oo):
                 B.fp4_rotate_quantize(bufs[i % 3], 128, fmt, out=oo)
 
-            for i in range(3):
-                call128(i)
+            ramp(call128, torch)
             ms = time_batch(call128, 21, torch)
             nb = sw.M * sw.K * ((2 if fmt == "nvfp4" else 0) + 2 + 0.5 + 1.0 / g) + (8 if fmt == "nvfp4" else 0)
             if fmt == "mxfp4":
@@ -373,8 +384,7 @@ def extra_rows(B, WL, torch, dev, groups=EXTRA_ROWS):
         xq, xs, _ = B.fp4_rotate_quantize(bf16_dev(WL.draw_x(wl), dev), wl.block, "mxfp4")
         wq, ws, _ = B.fp4_quantize_weights(bf16_dev(WL.draw_w(wl), dev), wl.block, "mxfp4")
         y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
-        for _ in range(20):  # about 20 ms of this kernel first, so that it is timed at its own steady clocks
-            B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y)
+        ramp(lambda i: B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y), torch, 0.25)
         ms = time_batch(lambda i: B.fp4_linear(xq, xs, wq, ws, "mxfp4", out=y), 10, torch)
         tf = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
         out["gemm_mxfp4_large"] = {"workload": "large: M=8192 K=8192 N=28672, block 128, Y fp32",
@@ -699,8 +709,7 @@ def main():
         def rq(i):
             B.fp4_rotate_quantize(bufs[i % 3], sw.block, sw.fmt, out=outs)
 
-        for i in range(5):
-            rq(i)
+        ramp(rq, torch)
         s_ms = time_batch(rq, 42, torch)
         s_cold = time_cold(rq, 20, torch, dev)
         s_bytes = sw.M * sw.K * (2 + 0.5 + 1.0 / sg)

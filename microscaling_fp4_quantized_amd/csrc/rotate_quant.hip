@@ -206,6 +206,30 @@ __global__ __launch_bounds__(kThreads) void rotate_amax(const uint16_t* __restri
   }
 }
 
+// E4M3 group code of a group maximum a >= 0: the E4M3FN value nearest to a / den (ties to even,
+// saturating at 448), den = 6 s_t. First from q = fl32(a * rD), rD within 1 ulp of
+// 1 / fl32(6 s_t), so that q lies within 4 ulp of a / den: its rounding at the E4M3 mantissa
+// point (or, below 2^-6, at multiples of 2^-9) is the exact decision unless q lies within 8 ulp
+// of a rounding midpoint; those rare groups, and every group when rD is +inf (6 s_t < 2^-125),
+// are decided exactly in float64.
+__device__ __forceinline__ unsigned e4m3_code(float a, float rD, double den) {
+  const float q = a * rD;
+  const unsigned b = __float_as_uint(q);
+  // normal E4M3 range (q >= 2^-6): round the float32 mantissa at bit 20, carry into the exponent
+  const unsigned rn = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;
+  const unsigned cn = min(rn - ((127u - 7u) << 3), 0x7Eu);
+  const bool near_n = (b & 0xFFFFFu) - 0x7FFF8u < 16u;  // within 8 ulp of the midpoint
+  // subnormal E4M3 range: k * 2^-9, k = 0..8
+  const float k = fminf(q, 1.0f) * 512.0f;  // only read below 2^-6
+  const float kr = __builtin_rintf(k);
+  const bool near_s = fabsf(fabsf(k - kr) - 0.5f) < 1.52587890625e-05f;  // 2^-16
+  const bool normal = q >= 0.015625f;
+  unsigned code = normal ? cn : (unsigned)kr;
+  const bool near = (normal ? near_n : near_s) || !(rD < __builtin_inff());
+  if (near) code = e4m3_rne_sat((double)a / den);
+  return code;
+}
+
 // NVFP4 pass 2: group scales and codes given T.
 // One group of 16 under E4M3 code `code`: S = fl32(d * s_t), u = fl32(y * fl32(1/S)), codes
 // rounded by the hardware convert (scale 1); S < 2^-126 stores signed zeros.
@@ -218,7 +242,7 @@ __device__ __forceinline__ void nv_group(const float* y, unsigned code, float s_
     *S_out = 0.f;
     return;
   }
-  const float R = (float)(1.0 / (double)S);  // = fl32(1 / S)
+  const float R = 1.0f / S;  // correctly rounded float32 division: fl32(1 / S)
   float u[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) u[i] = y[i] * R;
@@ -253,13 +277,16 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_nv(const uint16_t* __re
     for (int j = 0; j < 4; ++j) out[j] = sign_codes8(v + 8 * j);
   } else {
     const double den = 6.0 * (double)s_t;  // exact
+    // about 1 / den within 2 ulp; groups are decided exactly in float64 when 6 s_t is tiny
+    const float d32 = 6.0f * s_t;
+    const float rD = d32 >= 0x1p-125f ? __builtin_amdgcn_rcpf(d32) : __builtin_inff();
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const float* y = v + 16 * g;
       float a = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(y[i]));
-      unsigned code = e4m3_rne_sat((double)a / den);
+      unsigned code = e4m3_code(a, rD, den);
       unsigned o[2];
       float S;
       nv_group(y, code, s_t, o, &S);

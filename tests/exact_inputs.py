@@ -107,6 +107,28 @@ def nv_rows(k):
     return [blocks[i:i + width] for i in range(0, len(blocks), width)]
 
 
+# E4M3 rounding midpoints of a / (6 s_t), with the even code each rounds to: between the
+# subnormal steps k * 2^-9, within a binade, across a binade (1.875 / 2) and at the top (416 / 448)
+E4M3_TIES = ((0.5 * 2.0 ** -9, 0x00), (1.5 * 2.0 ** -9, 0x02), (7.5 * 2.0 ** -9, 0x08), (1.0625, 0x38),
+             (1.1875, 0x3A), (1.9375, 0x40), (17.0, 0x58), (432.0, 0x7E))
+
+
+def nv_e4m3_tie_rows(k):
+    """NVFP4 rows (block 16) whose group maxima divided by 6 s_t (s_t = 2^k) lie exactly on
+    every kind of E4M3 rounding midpoint, with either sign, and one bf16 step to either side."""
+    st = 2.0 ** k
+    blocks = [[2688 * st]]
+    for m, _ in E4M3_TIES:
+        a = 6 * m * st
+        for v in [a] + bf16_neighbours(a):
+            ulp = 2.0 ** (np.floor(np.log2(v)) - 7)  # one bf16 step at v
+            blocks += [[v], [-v], [v, -ulp]]
+    width = 16
+    while len(blocks) % width:
+        blocks.append([])
+    return [blocks[i:i + width] for i in range(0, len(blocks), width)]
+
+
 def check_tie_codes(packed, U, scale_of_group, g):
     """Every element of U exactly at t * scale must carry the even neighbour's code, with the
     sign of the element (hand table, independent of the oracle)."""

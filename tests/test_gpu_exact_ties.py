@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from microscaling_fp4_quantized_amd import binding as B
-from exact_inputs import build_input, check_tie_codes, mx_rows, nv_rows
+from exact_inputs import E4M3_TIES, build_input, check_tie_codes, mx_rows, nv_e4m3_tie_rows, nv_rows
 from oracle import fp4_oracle as O
 from parity import assert_quant_parity, compare_quant, dev_bf16, say
 
@@ -64,6 +64,26 @@ def test_nv_exact_ties(k):
     out2 = B.fp4_rotate_quantize(dev_bf16(bits), 16, "nvfp4", tensor_scale=given)
     torch.cuda.synchronize()
     assert torch.equal(out2[0], out[0]) and torch.equal(out2[1], out[1])
+
+
+@pytest.mark.parametrize("k", (-12, 0, 9))
+def test_nv_e4m3_scale_ties(k):
+    # group maxima exactly on E4M3 rounding midpoints (and one bf16 step away): the group scale
+    # code must be the even neighbour, as the oracle decides it exactly
+    rows = nv_e4m3_tie_rows(k)
+    bits, U = build_input(rows, 16)
+    say(f"case E4M3 scale ties, s_t = 2^{k}: X {bits.shape}")
+    for given in (None, torch.tensor([2.0 ** k], dtype=torch.float32, device="cuda")):
+        out = B.fp4_rotate_quantize(dev_bf16(bits), 16, "nvfp4", tensor_scale=given)
+        torch.cuda.synchronize()
+        res = compare_quant(out, bits, 16, "nvfp4")
+        assert_quant_parity(res, f"E4M3 ties s_t=2^{k}", exact=True)
+        assert res["tensor_scale"] == 2.0 ** k
+        sc = out[1].cpu().numpy().reshape(-1)
+        amax = np.abs(U).reshape(-1, 16).max(axis=1)
+        for m, want in E4M3_TIES:
+            at = amax == 6 * m * 2.0 ** k
+            assert at.sum() == 3 and np.all(sc[at] == want), (m, sc[at])
 
 
 def test_negative_zero_block():

@@ -759,3 +759,19 @@ def test_oracle_codes_on_exact_ties(case):
         assert st == np.float32(2.0 ** k)
         n = check_tie_codes(p, U, O.e4m3_value(sc) * 2.0 ** k, 16)
     assert n > 50
+
+
+def test_oracle_e4m3_scale_ties():
+    # group maxima exactly on E4M3 rounding midpoints of a / (6 s_t): the oracle picks the even
+    # neighbour of each (hand table from the E4M3FN definition), for either sign and tensor scale
+    import exact_inputs as E
+
+    for k in (-12, 0, 9):
+        bits, U = E.build_input(E.nv_e4m3_tie_rows(k), 16)
+        _, sc, ts = O.rotate_quantize(bits, 16, "nvfp4")
+        assert ts == np.float32(2.0 ** k)
+        amax = np.abs(U).reshape(-1, 16).max(axis=1)
+        sc = sc.reshape(-1)
+        for m, want in E.E4M3_TIES:
+            at = amax == 6 * m * 2.0 ** k
+            assert at.sum() == 3 and np.all(sc[at] == want), (k, m)
