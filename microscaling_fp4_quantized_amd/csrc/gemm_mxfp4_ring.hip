@@ -11,15 +11,23 @@
 //  * 8 waves (2 per SIMD). The 256x256 tile uses a 2 x 4 wave layout, 128 x 64 outputs per
 //    wave (128 accumulators), so one wave's LDS reads overlap the other wave's MFMAs.
 //  * K advances in stages of 256 elements (128 bytes per row). A 2-deep LDS ring is filled
-//    with buffer_load_dwordx4 ... lds (LDS DMA, no register staging); 16-byte chunks of a row
-//    are XOR-swizzled so the 32 rows of a fragment read hit distinct banks. The buffer form,
-//    not global_load_lds: the compiler counts a pending FLAT-encoded DMA as a possible LDS
-//    access and so waits for every LDS read (lgkmcnt(0)) before each MFMA group while one is
-//    in flight; with the buffer form it waits only for the fragments the MFMAs use.
+//    with buffer_load_dwordx4 ... lds (LDS DMA, no register staging; the stage's offset in the
+//    scalar offset field); 16-byte chunks of a row are XOR-swizzled by the row's low five bits
+//    so the 32 rows of a fragment read hit distinct banks. The buffer form, not
+//    global_load_lds: the compiler counts a pending FLAT-encoded DMA as a possible LDS access
+//    and so waits for every LDS read (lgkmcnt(0)) before each MFMA group while one is in
+//    flight; with the buffer form it waits only for the fragments the MFMAs use.
+//  * LDS holds the A rows of both stages, then the B rows, then the scales: every fragment
+//    read is one of four per-lane offsets (per k-step) plus the stage's base and an immediate,
+//    and the loop carries about a dozen VALU instructions per stage (which compete with the
+//    MFMAs for issue cycles on gfx950).
+//  * K order within a stage: k-step ks takes chunk ks of each row in lane half 0 and chunk
+//    ks + 4 in lane half 1, for both operands, so every product still pairs x_k with w_k and
+//    a lane half's four E8M0 bytes of the stage are one dword, read once per stage; op_sel = ks
+//    picks the byte.
 //  * The workgroup barrier of the ring waits for LDS reads only (each wave has already
 //    waited for its own DMA of the stage), so in-flight prefetches are not drained.
-//  * E8M0 scales are DMA'd 16 bytes per row (two stages) into their own double buffer,
-//    read once per two stages, and shifted per lane half so the MFMA op_sel picks the byte.
+//  * E8M0 scales are DMA'd 16 bytes per row (two stages) into their own double buffer.
 //  * Output tiles go through LDS so Y is written as whole row segments.
 //  * Tile order: workgroup i runs on XCD i % 8; each XCD takes a contiguous range of tiles,
 //    walked M-fastest within groups of 8 tile rows, so tiles running together share
@@ -97,7 +105,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const uint8_t* bas
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// 16-byte chunk q of row r sits at slot q ^ swz(r) of the row. swz depends only on r % 32, so
+// every 32-row fragment reads at the same lane offsets; over any 16 consecutive rows it takes each
+// value twice, once on even and once on odd rows, so a fragment read hits distinct banks.
+__device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
 
 // One output tile [m0, m0 + 256) x [n0, n0 + C::BN) over all of K.
 template <bool OUT_BF16, class C>
@@ -107,6 +118,9 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
                                           int K, int m0, int n0) {
   constexpr int WGN = C::WGN, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
   constexpr int STAGE = C::STAGE, A_WL = C::A_WL, B_WL = C::B_WL, SC_BYTES = C::SC_BYTES, SC_WL = C::SC_WL;
+  // LDS: the A rows of both stages, then the B rows of both stages, then the scale buffers,
+  // so that a fragment read is a per-lane offset of the stage plus an immediate.
+  constexpr int A_ST = BM * BKB, B_ST = C::BN * BKB, B_BASE = NS * A_ST;
   uint8_t* scl = smem + NS * STAGE;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
@@ -153,19 +167,20 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
         if (wave * SC_WL + i < C::SC_LOADS)
           __builtin_amdgcn_raw_ptr_buffer_load_lds((wave * SC_WL + i) * 64 < BM ? rsXs : rsWs,
                                                    (lds_void*)(dst + (wave * SC_WL + i) * 1024), 16,
-                                                   offS[i] + (unsigned)(s >> 1) * 16, 0, 0, 0);
+                                                   offS[i], (unsigned)(s >> 1) * 16, 0, 0);
     }
-    uint8_t* buf = smem + (s & 1) * STAGE;
+    uint8_t* bufa = smem + (s & 1) * A_ST;
+    uint8_t* bufb = smem + B_BASE + (s & 1) * B_ST;
 #pragma unroll
     for (int i = 0; i < A_WL; ++i)
       if (i % KSTEPS == p)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(buf + (wave * A_WL + i) * 1024), 16,
-                                                 offA[i] + (unsigned)s * BKB, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(bufa + (wave * A_WL + i) * 1024), 16,
+                                                 offA[i], (unsigned)s * BKB, 0, 0);
 #pragma unroll
     for (int i = 0; i < B_WL; ++i)
       if (i % KSTEPS == p)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void*)(buf + BM * BKB + (wave * B_WL + i) * 1024), 16,
-                                                 offB[i] + (unsigned)s * BKB, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void*)(bufb + (wave * B_WL + i) * 1024), 16,
+                                                 offB[i], (unsigned)s * BKB, 0, 0);
   };
 
   v16f acc[FM][FN];
@@ -177,8 +192,12 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int fr = lane & 31, fh = lane >> 5;
-  const unsigned sh = 8u * (unsigned)fh;  // lane half h uses scale byte 2*ks + h
-  v4u sg_a[FM], sg_b[FN];                 // scale dwords of the current two stages, lane-shifted
+  // per-lane offsets of the lane's row in stage 0 (A: row wm0 + fr, B: row wn0 + fr) and of its
+  // chunk ks + 4 h; the stage adds A_ST / B_ST, fragment i / j an immediate i * 4 KB
+  const int ra = (wm0 + fr) * BKB, rb = B_BASE + (wn0 + fr) * BKB;
+  int cx[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) cx[ks] = ((ks + 4 * fh) ^ swz(fr)) << 4;
 
   // Stage s: wait for its DMA (this wave's, then everyone's at the barrier), then multiply it
   // while the parts of stage s+1 refill the buffer of stage s-1, which every wave has finished
@@ -188,44 +207,39 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
   auto run_stage = [&](int s, auto with_dma) {
     wait_vmcnt<0>();
     ring_barrier();
-    const uint8_t* buf = smem + (s & 1) * STAGE;
     const int sl = s & 1;
-    if (sl == 0) {
-      const uint8_t* sbuf = scl + ((s >> 1) & 1) * SC_BYTES;
+    const int la = ra + sl * A_ST, lb = rb + sl * B_ST;
+    // the lane half's 4 scale bytes of the stage (pair buffer (s >> 1) & 1, bytes 8 sl + 4 h ..
+    // + 3 of the row's 16): byte ks goes with k-step ks
+    unsigned sg_a[FM], sg_b[FN];
+    {
+      const uint8_t* sbuf = scl + ((s >> 1) & 1) * SC_BYTES + 8 * sl + 4 * fh;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) sg_a[i] = *reinterpret_cast<const v4u*>(sbuf + (wm0 + i * 32 + fr) * 16) >> sh;
+      for (int i = 0; i < FM; ++i) sg_a[i] = *reinterpret_cast<const unsigned*>(sbuf + (wm0 + i * 32 + fr) * 16);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) sg_b[j] = *reinterpret_cast<const v4u*>(sbuf + (BM + wn0 + j * 32 + fr) * 16) >> sh;
+      for (int j = 0; j < FN; ++j) sg_b[j] = *reinterpret_cast<const unsigned*>(sbuf + (BM + wn0 + j * 32 + fr) * 16);
     }
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       if constexpr (decltype(with_dma)::value) issue_part(s + 1, ks);
-      const int c = 2 * ks + fh;  // 16-byte chunk of the row = 32-element group
-      // scale byte 2ks + h of the stage's 8 -> dword 2*sl + ks/2, byte 2*(ks&1) after the shift
-      unsigned xa[FM], xb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) xa[i] = sl == 0 ? sg_a[i][ks >> 1] : sg_a[i][2 + (ks >> 1)];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) xb[j] = sl == 0 ? sg_b[j][ks >> 1] : sg_b[j][2 + (ks >> 1)];
       v4u a[FM], b[FN];
+      const int oa = la + cx[ks], ob = lb + cx[ks];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm0 + i * 32 + fr;
-        a[i] = *reinterpret_cast<const v4u*>(buf + r * BKB + ((c ^ swz(r)) << 4));
-      }
+      for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const v4u*>(smem + oa + i * 32 * BKB);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = wn0 + j * 32 + fr;
-        b[j] = *reinterpret_cast<const v4u*>(buf + BM * BKB + r * BKB + ((c ^ swz(r)) << 4));
-      }
+      for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const v4u*>(smem + ob + j * 32 * BKB);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const v8i av = v8i{(int)a[i][0], (int)a[i][1], (int)a[i][2], (int)a[i][3], 0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const v8i bv = v8i{(int)b[j][0], (int)b[j][1], (int)b[j][2], (int)b[j][3], 0, 0, 0, 0};
-          if ((ks & 1) == 0) acc[i][j] = mfma32<0>(av, bv, acc[i][j], (int)xa[i], (int)xb[j]);
-          else acc[i][j] = mfma32<2>(av, bv, acc[i][j], (int)xa[i], (int)xb[j]);
+          switch (ks) {  // byte ks of the lane half's scale dword
+            case 0: acc[i][j] = mfma32<0>(av, bv, acc[i][j], (int)sg_a[i], (int)sg_b[j]); break;
+            case 1: acc[i][j] = mfma32<1>(av, bv, acc[i][j], (int)sg_a[i], (int)sg_b[j]); break;
+            case 2: acc[i][j] = mfma32<2>(av, bv, acc[i][j], (int)sg_a[i], (int)sg_b[j]); break;
+            default: acc[i][j] = mfma32<3>(av, bv, acc[i][j], (int)sg_a[i], (int)sg_b[j]); break;
+          }
         }
       }
     }
