@@ -13,9 +13,11 @@
 // Design for CDNA4:
 //  * Codes and scales stay 4- and 8-bit in LDS. K advances 256 per stage; a 2-deep ring
 //    (144 KB) is filled by LDS DMA (buffer_load_dwordx4 ... lds) as in the MXFP4 kernel:
-//    16-byte chunks of a row XOR-swizzled so the 32 rows of a fragment read hit distinct
-//    banks, the 16 E4M3 bytes of each row and stage in their own buffer, one barrier per
-//    stage, the DMA of stage s+1 issued in four parts across the k-blocks of stage s.
+//    16-byte chunks of a row XOR-swizzled by the row's low five bits so the 32 rows of a
+//    fragment read hit distinct banks, the A rows of both stages before the B rows so every
+//    fragment read is a per-lane offset plus an immediate, the 16 E4M3 bytes of each row and
+//    stage in their own buffer, one barrier per stage, the DMA of stage s+1 issued in four
+//    parts across the k-blocks of stage s.
 //  * Each wave reads its fragments as 16 bytes (32 codes of one row) per lane and
 //    dequantizes them in registers right before the MFMAs: one packed convert per code
 //    byte (v_cvt_scalef32_pk_f16_fp4) and one packed multiply by the group scale d, itself
@@ -98,7 +100,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const uint8_t* bas
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// 16-byte chunk q of row r sits at slot q ^ swz(r) of the row. swz depends only on r % 32, so
+// every 32-row fragment reads at the same lane offsets; over any 16 consecutive rows it takes each
+// value twice, once on even and once on odd rows, so a fragment read hits distinct banks.
+__device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
 
 // Two E4M3 scale bytes (word W of w) -> the exact fp16 pair (d0, d1): every E4M3FN value,
 // subnormals included, is an fp16 number, and the gfx950 FP8 convert with a unit scale gives it.
@@ -127,6 +132,9 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
                                         void* __restrict__ Yv, int M, int N, int K, int m0, int n0) {
   constexpr int WGN = C::WGN, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
   constexpr int STAGE = C::STAGE, SC = C::SC, A_WL = C::A_WL, B_WL = C::B_WL, SC_WL = C::SC_WL;
+  // LDS: the A rows of both stages, then the B rows of both stages, then the scale buffers,
+  // so that a fragment read is a per-lane offset of the stage plus an immediate.
+  constexpr int A_ST = BM * BKB, B_ST = C::BN * BKB, B_BASE = NS * A_ST;
   uint8_t* scl = smem + NS * STAGE;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
@@ -169,19 +177,20 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
         if (wave * SC_WL + i < C::SC_LOADS)
           __builtin_amdgcn_raw_ptr_buffer_load_lds((wave * SC_WL + i) * 64 < BM ? rsXs : rsWs,
                                                    (lds_void*)(dst + (wave * SC_WL + i) * 1024), 16,
-                                                   offS[i] + (unsigned)s * SCB, 0, 0, 0);
+                                                   offS[i], (unsigned)s * SCB, 0, 0);
     }
-    uint8_t* buf = smem + (s & 1) * STAGE;
+    uint8_t* bufa = smem + (s & 1) * A_ST;
+    uint8_t* bufb = smem + B_BASE + (s & 1) * B_ST;
 #pragma unroll
     for (int i = 0; i < A_WL; ++i)
       if (i % KBLK == p)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(buf + (wave * A_WL + i) * 1024), 16,
-                                                 offA[i] + (unsigned)s * BKB, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(bufa + (wave * A_WL + i) * 1024), 16,
+                                                 offA[i], (unsigned)s * BKB, 0, 0);
 #pragma unroll
     for (int i = 0; i < B_WL; ++i)
       if (i % KBLK == p)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void*)(buf + BM * BKB + (wave * B_WL + i) * 1024), 16,
-                                                 offB[i] + (unsigned)s * BKB, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void*)(bufb + (wave * B_WL + i) * 1024), 16,
+                                                 offB[i], (unsigned)s * BKB, 0, 0);
   };
 
   v16f acc[FM][FN];
@@ -193,6 +202,12 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int fr = lane & 31, fh = lane >> 5;
+  // per-lane offsets of the lane's row in stage 0 (A: row wm0 + fr, B: row wn0 + fr) and of its
+  // chunk 2 kb + h of block kb; the stage adds A_ST / B_ST, fragment i / j an immediate i * 4 KB
+  const int ra = (wm0 + fr) * BKB, rb = B_BASE + (wn0 + fr) * BKB;
+  int cx[KBLK];
+#pragma unroll
+  for (int kb = 0; kb < KBLK; ++kb) cx[kb] = ((2 * kb + fh) ^ swz(fr)) << 4;
   const unsigned psel = fh ? 0x07060302u : 0x05040100u;  // bytes 2h, 2h + 1 of two dwords
 
   // Stage s: wait for its DMA (this wave's, then everyone's at the barrier), then multiply it
@@ -202,7 +217,7 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
   auto run_stage = [&](int s, auto with_dma) {
     wait_vmcnt<0>();
     ring_barrier();
-    const uint8_t* buf = smem + (s & 1) * STAGE;
+    const int la = ra + (s & 1) * A_ST, lb = rb + (s & 1) * B_ST;
     const uint8_t* sbuf = scl + (s & 1) * SC;
     // the lane's scale bytes of the stage: of each block's four (one dword), the two of its lane
     // half, gathered as word kb % 2 of dword kb / 2
@@ -222,18 +237,13 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
 #pragma unroll
     for (int kb = 0; kb < KBLK; ++kb) {
       if constexpr (decltype(with_dma)::value) issue_part(s + 1, kb);
-      const int c = 2 * kb + fh;  // 16-byte chunk of the row: elements 32h .. 32h + 31 of block kb
+      // 16-byte chunk 2 kb + h of the row: elements 32h .. 32h + 31 of block kb
       v4u ca[FM], cb[FN];
+      const int oa = la + cx[kb], ob = lb + cx[kb];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm0 + i * 32 + fr;
-        ca[i] = *reinterpret_cast<const v4u*>(buf + r * BKB + ((c ^ swz(r)) << 4));
-      }
+      for (int i = 0; i < FM; ++i) ca[i] = *reinterpret_cast<const v4u*>(smem + oa + i * 32 * BKB);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = wn0 + j * 32 + fr;
-        cb[j] = *reinterpret_cast<const v4u*>(buf + BM * BKB + r * BKB + ((c ^ swz(r)) << 4));
-      }
+      for (int j = 0; j < FN; ++j) cb[j] = *reinterpret_cast<const v4u*>(smem + ob + j * 32 * BKB);
       // group scales of the lane's two 16-element groups of block kb (groups 4 kb + 2h and + 1)
       h2 da[FM], db[FN];
 #pragma unroll
