@@ -130,6 +130,28 @@ def test_fused_decode_validation(lib):
     assert fused(lib, ws=A16 + 8, wsb=4096) == -5
 
 
+def fused_na(lib, X=A16, M=4, K=512, ldx=512, block=32, Wq=A16, Ws=A16, N=64, Y=A16, ydt=0):
+    return lib.fp4_rotate_quantize_linear_noalloc(X, M, K, ldx, block, Wq, Ws, N, Y, ydt, None)
+
+
+def test_noalloc_decode_validation(lib):
+    # the same argument checks as the workspace call, before anything is launched
+    assert fused_na(lib, block=8) == -3
+    assert fused_na(lib, ydt=2) == -4
+    assert fused_na(lib, X=None) == -1
+    assert fused_na(lib, M=17) == -2
+    assert fused_na(lib, K=640, ldx=640) == -2
+    assert fused_na(lib, M=16, K=1 << 15, ldx=1 << 15) == -2
+    assert fused_na(lib, Y=A16 + 4) == -5
+    assert b"fp4_rotate_quantize_linear_noalloc" in lib.fp4_last_error()
+    # every workspace the decode step can need fits the library's array
+    for M in (1, 16):
+        K = 512
+        while M * (K // 2 + 16 + K // 32) <= 160 * 1024:
+            assert binding.linear_workspace_bytes(M, K) <= 160 * 1024 + 256
+            K += 512
+
+
 def lin(lib, Xq=A16, Xs=A16, xts=None, Wq=A16, Ws=A16, wts=None, M=4, N=4, K=128, fmt=0, Y=A16, ydt=0):
     return lib.fp4_linear(Xq, Xs, xts, Wq, Ws, wts, M, N, K, fmt, Y, ydt, None)
 
