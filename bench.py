@@ -72,12 +72,12 @@ def gemm_kernel_for(fmt: str, M: int, N: int, K: int):
     buffers are 16-byte aligned (torch's allocations are): the library's dispatch predicates, in
     its order."""
     if fmt == "mxfp4":
-        if M <= 16 and K % 512 == 0:
+        if M <= 16 and K % 512 == 0 and K < (1 << 28):
             return "gemm_decode.hip", "gemm_mxfp4_decode"
         if K % 512 == 0 and K < (1 << 25) and M >= 256 and N >= 256:
             return "gemm_mxfp4_ring.hip", "gemm_mxfp4_ring"
         return "gemm_mxfp4.hip", "gemm_mxfp4_kernel"
-    if K % 64 == 0 and M >= 256 and N >= 256:
+    if K % 256 == 0 and K < (1 << 25) and M >= 256 and N >= 256:
         return "gemm_nvfp4_ring.hip", "gemm_nvfp4_ring"
     return "gemm_nvfp4.hip", "gemm_nvfp4_kernel"
 

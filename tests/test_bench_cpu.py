@@ -79,7 +79,9 @@ def test_roofline_kernel_follows_the_library_dispatch():
     assert bench.gemm_kernel_for("mxfp4", 16, 4096, 4224)[1] == "gemm_mxfp4_kernel"   # K % 512 != 0
     assert bench.gemm_kernel_for("mxfp4", 17, 4096, 4096)[1] == "gemm_mxfp4_kernel"   # neither
     assert bench.gemm_kernel_for("nvfp4", 16, 4096, 4096)[1] == "gemm_nvfp4_kernel"
-    assert bench.gemm_kernel_for("nvfp4", 256, 256, 64)[1] == "gemm_nvfp4_ring"
+    assert bench.gemm_kernel_for("nvfp4", 256, 256, 256)[1] == "gemm_nvfp4_ring"
+    assert bench.gemm_kernel_for("nvfp4", 256, 256, 384)[1] == "gemm_nvfp4_kernel"    # K % 256 != 0
+    assert bench.gemm_kernel_for("mxfp4", 16, 4096, 1 << 28)[1] == "gemm_mxfp4_kernel"  # K past the decode bound
 
 
 def test_committed_bench_line_contract():
