@@ -96,3 +96,81 @@ def test_linear_sweep(case):
         r = rel_fro(got, ref)
         say(f"sweep l{j} {out_dtype}: rel fro {r:.3e}")
         assert r <= GEMM_REL_FRO_TOL
+
+
+def _quant_cases_extreme(n, seed):
+    """Like _quant_cases, with input scales from 1e-35 to 1e35: tensor scales near the ends of
+    the float32 range, E8M0 codes near 0 and 254, and the E4M3 decision's float64 fallback."""
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        fmt = ["mxfp4", "nvfp4"][i % 2]
+        block = int(r.choice([16, 32, 64, 128]))
+        K = max(32, int(block * r.integers(1, 6)) if block >= 32 else int(32 * r.integers(1, 12)))
+        M = int(r.integers(1, 60))
+        rules = ["standard", "fit"] + (["ocp_floor", "oas"] if fmt == "mxfp4" else [])
+        rule = rules[int(r.integers(0, len(rules)))]
+        scale = float(10.0 ** r.uniform(-35, 35))
+        out.append((i, fmt, block, M, K, rule, scale))
+    return out
+
+
+@pytest.mark.parametrize("case", _quant_cases_extreme(100, 2026), ids=lambda c: f"qx{c[0]}")
+def test_quantizer_sweep_extreme_scales(case):
+    i, fmt, block, M, K, rule, scale = case
+    say(f"case sweep qx{i}: {fmt} b{block} M {M} K {K} rule {rule} scale {scale:.3g}")
+    x = WL.draw_normal_bf16((M, K), scale, seed=12000 + i)
+    q = B.fp4_rotate_quantize(dev_bf16(x), block, fmt, rule=rule)
+    torch.cuda.synchronize()
+    res = compare_quant(q, x, block, fmt, rule=rule)
+    assert_quant_parity(res, f"sweep qx{i}", exact=True)
+
+
+def _code_cases(n, seed):
+    """Random codes and scales for fp4_linear over every kernel route: unit scales (every
+    product and sum exact, so Y must equal the float64 product bit for bit) or random ones."""
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        fmt = "mxfp4" if i % 5 < 3 else "nvfp4"
+        route = i % 3
+        if route == 0:
+            M, N, K = int(r.integers(1, 17)), int(r.integers(1, 900)), 512 * int(r.integers(1, 9))
+        elif route == 1:
+            M, N, K = int(r.integers(17, 400)), int(r.integers(1, 400)), 128 * int(r.integers(1, 20))
+        else:
+            M, N, K = int(r.integers(256, 800)), int(r.integers(256, 800)), 512 * int(r.integers(1, 5))
+        out.append((i, fmt, M, N, K, bool(i % 2), int(r.integers(0, 2**31))))
+    return out
+
+
+@pytest.mark.parametrize("case", _code_cases(60, 77077), ids=lambda c: f"lc{c[0]}")
+def test_linear_random_codes(case):
+    i, fmt, M, N, K, unit, seed = case
+    say(f"case sweep lc{i}: {fmt} M {M} N {N} K {K} unit scales {unit}")
+    r = np.random.default_rng(seed)
+    g = 32 if fmt == "mxfp4" else 16
+    xq = O.pack_nibbles(r.integers(0, 16, (M, K), dtype=np.uint8))
+    wq = O.pack_nibbles(r.integers(0, 16, (N, K), dtype=np.uint8))
+    one, lo, hi = (127, 118, 136) if fmt == "mxfp4" else (0x38, 0x20, 0x60)  # E8M0 / E4M3 codes of 1.0
+    xs = np.full((M, K // g), one, np.uint8) if unit else r.integers(lo, hi, (M, K // g), dtype=np.uint8)
+    ws = np.full((N, K // g), one, np.uint8) if unit else r.integers(lo, hi, (N, K // g), dtype=np.uint8)
+    xt = wt = None
+    kw = {}
+    if fmt == "nvfp4":
+        xt = np.float32(1.0) if unit else np.float32(r.uniform(0.01, 3.0))
+        wt = np.float32(1.0) if unit else np.float32(r.uniform(0.01, 3.0))
+        kw = dict(x_ts=torch.tensor([float(xt)], device="cuda"), w_ts=torch.tensor([float(wt)], device="cuda"))
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    ref = O.linear_f64(xq, xs, wq, ws, fmt, xt, wt)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        y = B.fp4_linear(t(xq), t(xs), t(wq), t(ws), fmt, out_dtype=out_dtype, **kw)
+        torch.cuda.synchronize()
+        got = host(y.float() if out_dtype == torch.bfloat16 else y).astype(np.float64)
+        want = O.bf16_rne_f64(ref) if out_dtype == torch.bfloat16 else ref.astype(np.float32).astype(np.float64)
+        if unit:
+            assert np.array_equal(got, want), f"lc{i} {out_dtype}: max |diff| {np.abs(got - want).max()}"
+        else:
+            r_err = rel_fro(got, want)
+            say(f"sweep lc{i} {out_dtype}: rel fro {r_err:.3e}")
+            assert r_err <= GEMM_REL_FRO_TOL
