@@ -3,7 +3,8 @@
 
     python bench_profiles.py commands OUT    print the profiling commands (run them on the GPU
                                              machine from /tmp with TMPDIR=/tmp); raw output goes
-                                             under OUT/{trace,fetch,write,copy_fetch,copy_write,sq1,sq2}
+                                             under OUT/{trace,fetch,write,copy_fetch,copy_write,sq1,sq2,
+                                             nvsq1,nvsq2}
     python bench_profiles.py summarize OUT   read that raw output and write profiles/*.txt and
                                              profiles/traffic.json
 
@@ -63,7 +64,13 @@ TRAFFIC_MAP = [
     ("rotate_quant_nv<128, 0>", 4194304, "rotate_quant_nv@stress_nv128", "rotate_quant.hip",
      "stress_nv128 16384x8192 block 128, quantize pass"),
 ]
-SQ_KERNEL = ("gemm_mxfp4_ring<true>", 262144)
+# SQ counter passes: (raw-output prefix, bench workload, (kernel, grid), summary file, description)
+SQ_TARGETS = [
+    ("sq", "prefill_mx", ("gemm_mxfp4_ring<true>", 262144), "gemm_mxfp4_ring_prefill_sq_counters.txt",
+     "prefill_mx: M=2048 K=4096 N=14336, MXFP4 block 32, bf16 Y"),
+    ("nvsq", "prefill_nv", ("gemm_nvfp4_ring<true>", 262144), "gemm_nvfp4_ring_prefill_nv_sq_counters.txt",
+     "prefill_nv: M=2048 K=4096 N=14336, NVFP4 block 16, bf16 Y"),
+]
 
 
 def commands(out):
@@ -76,9 +83,11 @@ def commands(out):
                      f"-- {py} {BENCH_ARGS}")
         lines.append(f"timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d $REPO/{out}/copy_{d} -o run "
                      f"-- {py} --copy-probe 256 --no-cpu")
-    for d, cs in SQ_PASSES.items():
-        lines.append(f"timeout -s KILL 300 rocprofv3 --pmc {cs} --output-format csv -d $REPO/{out}/{d} -o run "
-                     f"-- {py} {BENCH_ARGS} --no-extra --stress ''")
+    for prefix, wl, _, _, _ in SQ_TARGETS:
+        wl_arg = "" if wl == "prefill_mx" else f" --workload {wl}"
+        for d, cs in SQ_PASSES.items():
+            lines.append(f"timeout -s KILL 300 rocprofv3 --pmc {cs} --output-format csv "
+                         f"-d $REPO/{out}/{prefix}{d[2:]} -o run -- {py} {BENCH_ARGS} --no-extra --stress ''{wl_arg}")
     return lines
 
 
@@ -119,10 +128,18 @@ def counter_means(d, counter):
 
 
 def summarize(out):
-    import bench
-
     out = os.path.join(ROOT, out) if not os.path.isabs(out) else out
     cmds = commands(os.path.relpath(out, ROOT))
+    # each summary is written only when its raw output is present, so a partial run (say, the SQ
+    # passes alone) leaves the other summaries as they are
+    if os.path.isdir(os.path.join(out, "trace")):
+        _summarize_trace_and_traffic(out, cmds)
+    _summarize_sq(out, cmds)
+
+
+def _summarize_trace_and_traffic(out, cmds):
+    import bench
+
     # kernel trace: per (kernel, grid) medians and means
     trace = _rows(os.path.join(out, "trace", "**", "*kernel_trace.csv"))
     durs = {}
@@ -181,23 +198,28 @@ def summarize(out):
         json.dump(table, f, indent=1)
         f.write("\n")
 
-    # SQ counters of the headline GEMM
-    if all(os.path.isdir(os.path.join(out, d)) for d in SQ_PASSES):
+
+def _summarize_sq(out, cmds):
+    # SQ counters of the GEMMs
+    for prefix, wl, kern, fname, desc in SQ_TARGETS:
+        dirs = [prefix + d[2:] for d in SQ_PASSES]
+        if not all(os.path.isdir(os.path.join(out, d)) for d in dirs):
+            continue
         vals = {}
-        for d, cs in SQ_PASSES.items():
+        for d, (pd, cs) in zip(dirs, SQ_PASSES.items()):
             for c in cs.split():
                 m = counter_means(os.path.join(out, d), c)
-                if SQ_KERNEL in m:
-                    vals[c] = m[SQ_KERNEL]
-        lines = [f"# SQ counters of {SQ_KERNEL[0]} grid {SQ_KERNEL[1]} (prefill_mx: M=2048 K=4096 N=14336, MXFP4",
-                 "# block 32, bf16 Y), averages per dispatch summed over the chip. SQ_WAVE_CYCLES and SQ_WAIT_* are",
-                 "# sampled every 4 cycles. commands:"] + ["#   " + c for c in cmds[0:1] + cmds[6:]]
+                if kern in m:
+                    vals[c] = m[kern]
+        lines = [f"# SQ counters of {kern[0]} grid {kern[1]} ({desc}), averages per dispatch summed",
+                 "# over the chip. SQ_WAVE_CYCLES and SQ_WAIT_* are sampled every 4 cycles. commands:"]
+        lines += ["#   " + cmds[0]] + ["#   " + c for c in cmds if any(f"/{d} " in c for d in dirs)]
         for c, (v, n) in vals.items():
             extra = ""
             if c.startswith("SQ_WAIT") and "SQ_WAVE_CYCLES" in vals:
                 extra = f"   ({v / vals['SQ_WAVE_CYCLES'][0]:.1%} of wave cycles)"
             lines.append(f"{c:<32}{v:>16.0f}  over {n} dispatches{extra}")
-        with open(os.path.join(PROFILES, "gemm_mxfp4_ring_prefill_sq_counters.txt"), "w") as f:
+        with open(os.path.join(PROFILES, fname), "w") as f:
             f.write("\n".join(lines) + "\n")
 
 
