@@ -21,7 +21,9 @@
  * Conventions shared by every call:
  *  - Pointers named as device pointers must point to device memory of the
  *    current HIP device. The caller owns and allocates every buffer; the library
- *    allocates nothing and keeps no state besides a thread-local error string.
+ *    allocates nothing. Its only state is a thread-local error string, per-device
+ *    launch settings set up on first use, and the device array of the
+ *    allocation-free decode call below.
  *  - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
  *    asynchronously; no call synchronises the host.
  *  - All arguments are validated before anything is launched. On a non-OK
@@ -207,11 +209,11 @@ FP4_API int fp4_linear(const uint8_t *Xq, const uint8_t *Xs, const float *x_ts,
  * feeding the 4-bit matmul.
  * Normally one launch: every workgroup quantizes the whole of X into on-chip memory with
  * the quantizer's own device code, while its W streams in. That pays off for a few tokens
- * (MI355X, W from HBM: 1 token on N = 14336, K = 4096 in 8.8 us against 10.7 us for the two
- * calls). With many rows of X per CU (M times the workgroups per CU, above about 14) the
+ * (MI355X, W from HBM: 1 token on N = 14336, K = 4096 in about 8 us against 10 us for the
+ * two calls). With many rows of X per CU (M times the workgroups per CU, above about 14) the
  * repeated quantization costs more than a second launch; given a workspace, the call then
  * quantizes X once into it and runs the decode GEMM (two launches on `stream`; 16 tokens on
- * N = 14336: 12.1 us instead of 20.9 us for one launch).
+ * N = 14336: about 12 us instead of 21 us for one launch).
  *
  *  X       device bf16 [M, ldx], 16-byte aligned, ldx >= K, ldx % 8 == 0.
  *  M       1..16 tokens.   K: a multiple of 512 with M * (K/2 + 16 + K/32) <= 160 KiB.
