@@ -72,7 +72,7 @@ def gemm_kernel_for(fmt: str, M: int, N: int, K: int):
     buffers are 16-byte aligned (torch's allocations are): the library's dispatch predicates, in
     its order."""
     if fmt == "mxfp4":
-        if M <= 16 and K % 512 == 0 and K < (1 << 28):
+        if K % 512 == 0 and (K < (1 << 28) if M <= 16 else (M <= 64 and K <= 8192)):
             return "gemm_decode.hip", "gemm_mxfp4_decode"
         if K % 512 == 0 and K < (1 << 25) and M >= 256 and N >= 256:
             return "gemm_mxfp4_ring.hip", "gemm_mxfp4_ring"
@@ -418,14 +418,20 @@ def extra_rows(B, WL, torch, dev, groups=EXTRA_ROWS):
     return out
 
 
+# traffic-table key of each decode row's kernel (the launch configuration differs with N and M)
+DECODE_TRAFFIC_KEY = {"decode_wide1": "gemm_mxfp4_decode@decode_wide", "decode_wide4": "gemm_mxfp4_decode@decode_wide",
+                      "decode_wide16": "gemm_mxfp4_decode@decode_wide", "decode_wide32": "gemm_mxfp4_decode@decode_wide32",
+                      "decode_wide64": "gemm_mxfp4_decode@decode_wide64"}
+
+
 def decode_rows(B, WL, torch, dev, names=("decode1", "decode4", "decode16", "decode_wide1", "decode_wide4",
-                                            "decode_wide16")):
-    """Decode-shaped MXFP4 layers (M in {1, 4, 16} tokens, K=4096; W 4096x4096 or 14336x4096),
-    bound by reading W from HBM. Each row is timed as a HIP graph of calls that cycle over copies of
+                                            "decode_wide16", "decode_wide32", "decode_wide64")):
+    """Decode-shaped MXFP4 layers (M in {1, 4, 16} tokens, K=4096; W 4096x4096 or 14336x4096; and
+    batches of 32 and 64 tokens against the wide W), bound by reading W from HBM. Each row is timed as a HIP graph of calls that cycle over copies of
     W totalling more than 512 MB, so that no call finds its W in the 256 MB Infinity Cache (as in a
     model whose weights do not fit in it); the graph's result is checked against an eager call. The
     same call with one W, resident in the cache, is reported as warm_us. The whole decode step from
-    bf16 X (two calls, or the one-launch fused call) is timed the same way."""
+    bf16 X (two calls, or for M <= 16 the one-launch fused call) is timed the same way."""
     import math
 
     out = {}
@@ -458,7 +464,7 @@ def decode_rows(B, WL, torch, dev, names=("decode1", "decode4", "decode16", "dec
                "w_copies": n_sets, "graph_replay_matches_eager": graph_ok,
                "warm_us": ms_warm * 1e3, "warm_GB/s": nbytes / (ms_warm * 1e-3) / 1e9,
                "us_per_python_call": ms_call * 1e3,
-               "traffic": measured_traffic("gemm_mxfp4_decode@" + ("decode_wide" if wl.N > 4096 else "decode"),
+               "traffic": measured_traffic(DECODE_TRAFFIC_KEY.get(name, "gemm_mxfp4_decode@decode"),
                                           "gemm_decode.hip"),
                "note": f"{calls} calls in one HIP graph over {n_sets} copies of W ({n_sets * wbytes / 1e6:.0f} MB), "
                        "so W comes from HBM; warm_us: one W, resident in the Infinity Cache"}
@@ -481,12 +487,16 @@ def decode_rows(B, WL, torch, dev, names=("decode1", "decode4", "decode16", "dec
             B.fp4_rotate_quantize_linear(xb, w_i[0], w_i[1], wl.block, out=y, workspace=ws_buf)
 
         ms_two = time_graph(two_calls, calls, torch)
-        ms_fused = time_graph(fused, calls, torch)
-        same = bool(torch.equal(y, y2))
-        row["step_from_bf16_x"] = {"two_calls_us": ms_two * 1e3, "fused_us": ms_fused * 1e3,
-                                   "fused_equals_two_calls": same}
-        log(f"[bench] {name} step from bf16 X, W from HBM: two calls {ms_two * 1e3:.2f} us, "
-            f"fused {ms_fused * 1e3:.2f} us (same result: {same})")
+        if wl.M <= 16:
+            ms_fused = time_graph(fused, calls, torch)
+            same = bool(torch.equal(y, y2))
+            row["step_from_bf16_x"] = {"two_calls_us": ms_two * 1e3, "fused_us": ms_fused * 1e3,
+                                       "fused_equals_two_calls": same}
+            log(f"[bench] {name} step from bf16 X, W from HBM: two calls {ms_two * 1e3:.2f} us, "
+                f"fused {ms_fused * 1e3:.2f} us (same result: {same})")
+        else:  # the fused call takes at most 16 tokens
+            row["step_from_bf16_x"] = {"two_calls_us": ms_two * 1e3}
+            log(f"[bench] {name} step from bf16 X, W from HBM: two calls {ms_two * 1e3:.2f} us")
         out[f"gemm_{name}"] = row
         del sets, wq, ws
     return out

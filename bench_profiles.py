@@ -47,10 +47,14 @@ TRAFFIC_MAP = [
      "large M=8192 K=8192 N=28672 fp32 Y"),
     ("gemm_nvfp4_ring<true>", 262144, "gemm_nvfp4_ring@prefill_nv", "gemm_nvfp4_ring.hip",
      "prefill_nv M=2048 K=4096 N=14336 bf16 Y"),
-    ("gemm_mxfp4_decode<false, 1>", 131072, "gemm_mxfp4_decode@decode", "gemm_decode.hip",
+    ("gemm_mxfp4_decode<false, 1, 1>", 131072, "gemm_mxfp4_decode@decode", "gemm_decode.hip",
      "decode M in {1,4,16} K=4096 N=4096 fp32 Y, one 16-row tile per workgroup, W from HBM"),
-    ("gemm_mxfp4_decode<false, 2>", 229376, "gemm_mxfp4_decode@decode_wide", "gemm_decode.hip",
+    ("gemm_mxfp4_decode<false, 2, 1>", 229376, "gemm_mxfp4_decode@decode_wide", "gemm_decode.hip",
      "decode_wide M in {1,4,16} K=4096 N=14336 fp32 Y, two 16-row tiles per workgroup, W from HBM"),
+    ("gemm_mxfp4_decode<false, 2, 2>", 229376, "gemm_mxfp4_decode@decode_wide32", "gemm_decode.hip",
+     "decode_wide32 M=32 K=4096 N=14336 fp32 Y, two 16-row tiles and two X fragments per workgroup, W from HBM"),
+    ("gemm_mxfp4_decode<false, 2, 4>", 229376, "gemm_mxfp4_decode@decode_wide64", "gemm_decode.hip",
+     "decode_wide64 M=64 K=4096 N=14336 fp32 Y, two 16-row tiles and four X fragments per workgroup, W from HBM"),
     ("rotate_quant_mx<32, 0>", 4194304, "rotate_quant_mx@stress_mx32", "rotate_quant.hip",
      "stress_mx32 16384x8192 block 32"),
     ("rotate_quant_mx<128, 0>", 4194304, "rotate_quant_mx@stress_mx128", "rotate_quant.hip",

@@ -189,8 +189,9 @@ FP4_API int fp4_quantize_weights_ex(const void *W, int64_t N, int64_t K, int64_t
  *  M, N >= 1; K >= 128 and K % 128 == 0. M, N, K <= 2^31 - 1 and M * K / 2,
  *  N * K / 2 <= 2^40 bytes; larger shapes return FP4_E_SHAPE.
  *  Xq, Wq 16-byte aligned; Xs, Ws 4-byte aligned. (MXFP4 with 16-byte-aligned Xs and Ws
- *  and K % 512 == 0 runs the decode kernel for M <= 16 and the 256-row-tile kernel for
- *  M, N >= 256; other pointers or shapes run the general kernel.)
+ *  and K % 512 == 0 runs the weight-streaming decode kernel for M <= 16, and for M <= 64
+ *  when K <= 8192, and the 256-row-tile kernel for M, N >= 256; other pointers or shapes
+ *  run the general kernel.)
  *  Y   device [M, N] row-major, float32 (FP4_OUT_F32) or bf16 (FP4_OUT_BF16,
  *      round-to-nearest-even); 16-byte aligned.
  * No bias, no activation. One kernel launch on `stream`.

@@ -1,4 +1,5 @@
-// Decode-shaped W4A4 MXFP4 GEMM for gfx950 (M <= 16 rows of activations).
+// Decode-shaped W4A4 MXFP4 GEMM for gfx950 (M <= 16 rows of activations, and up to 64 rows
+// for layers whose K fits the per-wave slices).
 //
 // "Bridging the Gap Between Promise and Performance for Microscaling FP4
 // Quantization" (gist.science, German edition), Technische Zusammenfassung §2
@@ -27,8 +28,13 @@
 //  * Layers whose slices do not fit the LDS area (K above 8192 / T) take a chunked variant: the
 //    workgroup stages W through LDS in chunks of at most 4096 elements as whole 1 KB row pieces,
 //    the next chunk's loads in flight while the current one is multiplied.
+//  * Up to 64 tokens (MF = ceil(M / 16) column fragments of X): every W fragment a wave reads
+//    is multiplied with each of the MF X fragments, so W is still read once and only the MFMA
+//    count and the L2 reads of X grow with M; the partial sums of all MF x T output fragments
+//    meet in the same fixed order.
 //  X rows past M repeat row M-1 and W rows past N repeat row N-1; their outputs are discarded.
 #include <atomic>
+#include <type_traits>
 
 #include "../../include/fp4.h"
 #include "quant_device.hpp"
@@ -183,8 +189,9 @@ constexpr int kDecSlice = 512;  // K elements of a wave's slice: 256 code bytes 
 constexpr int kDecMaxSlices = 2;  // tile-slices (4 KB each) a wave holds in LDS at once
 
 // At most 128 VGPRs (4 waves per SIMD), so that two workgroups share a CU. NPER (1 or 2): slices
-// per wave; wave w takes slices w and w + 8. LDS: 8 waves x NPER x T x 4 KB.
-template <bool OUT_BF16, int T>
+// per wave; wave w takes slices w and w + 8. LDS: 8 waves x NPER x T x 4 KB. MF (1..4): 16-token
+// column fragments of X; the MF x T partial sums of a wave fit its area (MF x T KB <= NPER x T x 4 KB).
+template <bool OUT_BF16, int T, int MF>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemm_mxfp4_decode(
     const uint8_t* __restrict__ Xq, const uint8_t* __restrict__ Xs, const uint8_t* __restrict__ Wq,
     const uint8_t* __restrict__ Ws, void* __restrict__ Yv, int M, int N, int K, int NPER) {
@@ -196,13 +203,14 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
   const int nb = blockIdx.x * 16 * T;
   const int area_bytes = NPER * T * 4096;
   uint8_t* area = lds + wave * area_bytes;  // tile-slice (j, tt) at (j * T + tt) * 4 KB: 16 rows x 256 bytes
-  const size_t xrow = (size_t)min(r, M - 1);
+  static_assert(MF >= 1 && MF <= 4 && MF * T <= kDecWaves, "column fragments");
+  constexpr int NJ = kDecMaxSlices / T;  // the launch takes this kernel only when NPER <= NJ
 
   // W of the wave's slices into its area: instruction i of a tile-slice carries rows 4i .. 4i+3;
   // lane l lands at byte 16 * (l % 16) of row 4i + l / 16 and fetches the row's 16-byte chunk
   // (l % 16) ^ row there. Buffer loads over each tile's rows (32-bit offsets; rows past N read as
   // zero, and their outputs are discarded). The rows' E8M0 bytes of a slice go to registers.
-  v4u wsv[kDecMaxSlices][T];
+  v4u wsv[NJ][T];
 #pragma unroll
   for (int tt = 0; tt < T; ++tt) {
     const int n0 = __builtin_amdgcn_readfirstlane(min(nb + 16 * tt, N - 1));
@@ -210,7 +218,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(Wq + (size_t)n0 * KB, rows * KB);
     const size_t wrow = (size_t)min(n0 + r, N - 1);
 #pragma unroll
-    for (int j = 0; j < kDecMaxSlices; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int sl = wave + 8 * j;
       if (j < NPER && sl < nsl) {  // wave-uniform
         uint8_t* dst = area + (j * T + tt) * 4096;
@@ -225,19 +233,30 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
       }
     }
   }
-  v4f acc[T];
+  v4f acc[MF][T];
 #pragma unroll
-  for (int tt = 0; tt < T; ++tt) acc[tt] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int f = 0; f < MF; ++f)
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) acc[f][tt] = v4f{0.f, 0.f, 0.f, 0.f};
   const unsigned sh = 8u * (unsigned)g;
 #pragma unroll
-  for (int j = 0; j < kDecMaxSlices; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const int sl = wave + 8 * j;
     if (j < NPER && sl < nsl) {
-      v4u xb[kDecBatch];
+      // X fragment f of the slice into buffer f % 2: token 16 f + r (clamped to M - 1), the lane's
+      // 16 code bytes of each of the 4 steps and the 4 E8M0 bytes of its row. Two fragments are
+      // requested before the wait for W; fragment f + 2 right after the products of fragment f
+      // are issued, so its L2 latency overlaps those of fragment f + 1.
+      v4u xb[2][kDecBatch], xsv[2];
+      auto load_x = [&](int f) {
+        const size_t xrow = (size_t)min(16 * f + r, M - 1);
 #pragma unroll
-      for (int u = 0; u < kDecBatch; ++u)
-        xb[u] = *reinterpret_cast<const v4u*>(Xq + xrow * KB + (size_t)sl * 256 + 64 * u + 16 * g);
-      const v4u xsv = *reinterpret_cast<const v4u*>(Xs + xrow * KS + (size_t)sl * 16);
+        for (int u = 0; u < kDecBatch; ++u)
+          xb[f & 1][u] = *reinterpret_cast<const v4u*>(Xq + xrow * KB + (size_t)sl * 256 + 64 * u + 16 * g);
+        xsv[f & 1] = *reinterpret_cast<const v4u*>(Xs + xrow * KS + (size_t)sl * 16);
+      };
+      load_x(0);
+      if (MF > 1) load_x(1);
       // this wave's DMA has landed (its area is read by no other wave until the reduction)
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       asm volatile("" ::: "memory");
@@ -248,28 +267,37 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
         for (int u = 0; u < kDecBatch; ++u)
           wf[tt][u] = *reinterpret_cast<const v4u*>(area + (j * T + tt) * 4096 + r * 256 + 16 * (((4 * u + g) ^ r) & 15));
 #pragma unroll
-      for (int tt = 0; tt < T; ++tt)
+      for (int f = 0; f < MF; ++f) {
 #pragma unroll
-        for (int u = 0; u < kDecBatch; ++u) {
-          const v8i a = v8i{(int)wf[tt][u][0], (int)wf[tt][u][1], (int)wf[tt][u][2], (int)wf[tt][u][3], 0, 0, 0, 0};
-          const v8i b = v8i{(int)xb[u][0], (int)xb[u][1], (int)xb[u][2], (int)xb[u][3], 0, 0, 0, 0};
-          acc[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[tt], 4, 4, 0, (int)(wsv[j][tt][u] >> sh), 0,
-                                                                      (int)(xsv[u] >> sh));
-        }
+        for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+          for (int u = 0; u < kDecBatch; ++u) {
+            const v4u& x = xb[f & 1][u];
+            const v8i a = v8i{(int)wf[tt][u][0], (int)wf[tt][u][1], (int)wf[tt][u][2], (int)wf[tt][u][3], 0, 0, 0, 0};
+            const v8i b = v8i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+            acc[f][tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[f][tt], 4, 4, 0,
+                                                                         (int)(wsv[j][tt][u] >> sh), 0,
+                                                                         (int)(xsv[f & 1][u] >> sh));
+          }
+        if (f + 2 < MF) load_x(f + 2);
+      }
     }
   }
   // partial sums into the wave's own area (its fragment reads are done), then the fixed-order sum
+  // of output fragment (f, tt) by wave f * T + tt
   v4f* red = reinterpret_cast<v4f*>(area);
 #pragma unroll
-  for (int tt = 0; tt < T; ++tt) red[tt * 64 + lane] = acc[tt];
-  __syncthreads();
-  if (wave >= T) return;
-  const int tt = wave;
-  v4f sum = reinterpret_cast<const v4f*>(lds)[tt * 64 + lane];
+  for (int f = 0; f < MF; ++f)
 #pragma unroll
-  for (int w = 1; w < kDecWaves; ++w) sum += reinterpret_cast<const v4f*>(lds + w * area_bytes)[tt * 64 + lane];
-  // lane holds D[n + 4g + i][m = r], i = 0..3: four consecutive features of token r
-  store_out<OUT_BF16>(Yv, M, N, lane & 15, nb + 16 * tt + 4 * (lane >> 4), sum);
+    for (int tt = 0; tt < T; ++tt) red[(f * T + tt) * 64 + lane] = acc[f][tt];
+  __syncthreads();
+  if (wave >= MF * T) return;
+  const int q = wave, f = q / T, tt = q % T;
+  v4f sum = reinterpret_cast<const v4f*>(lds)[q * 64 + lane];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) sum += reinterpret_cast<const v4f*>(lds + w * area_bytes)[q * 64 + lane];
+  // lane holds D[n + 4g + i][m = 16 f + r], i = 0..3: four consecutive features of one token
+  store_out<OUT_BF16>(Yv, M, N, 16 * f + (lane & 15), nb + 16 * tt + 4 * (lane >> 4), sum);
 }
 
 // The chunked variant for long K. At most 128 VGPRs (4 waves per SIMD).
@@ -615,32 +643,35 @@ hipError_t launch_fused(const uint16_t* X, int64_t ldx, const uint8_t* Wq, const
 }  // namespace fp4
 
 // 16 rows of W and their 32-bit buffer offsets: 16 * K / 2 < 2^32
+// M <= 16: any K (the chunked kernel takes long K). 16 < M <= 64: the sliced kernel only, whose
+// per-wave slices hold K <= 8192 with one tile per workgroup.
 bool fp4_gemm_mxfp4_decode_fits(int64_t M, int64_t N, int64_t K) {
-  return M <= 16 && K % 512 == 0 && N >= 1 && K < ((int64_t)1 << 28);
+  return M >= 1 && N >= 1 && K % 512 == 0 && (M <= 16 ? K < ((int64_t)1 << 28) : (M <= 64 && K <= 8192));
 }
 
 namespace fp4 {
 namespace {
-std::atomic<int> g_dec_attr[2][2][64];  // per output dtype, T and device: dynamic-LDS limit raised
+std::atomic<int> g_dec_attr[2][2][4][64];  // per output dtype, T, MF and device: dynamic-LDS limit raised
 
-template <bool OUT_BF16, int T>
+template <bool OUT_BF16, int T, int MF>
 hipError_t launch_decode(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws, int M, int N, int K,
                          void* Y, int dev, hipStream_t st) {
   const int nper = (K / kDecSlice + kDecWaves - 1) / kDecWaves;  // slices per wave
   const bool sliced = nper <= kDecMaxSlices / T;
+  if (MF > 1 && !sliced) return hipErrorInvalidValue;  // excluded by fp4_gemm_mxfp4_decode_fits and the T choice
   const int KC = dec_chunk(K);
-  auto kern = sliced ? gemm_mxfp4_decode<OUT_BF16, T> : gemm_mxfp4_decode_chunked<OUT_BF16, T>;
+  auto kern = sliced ? gemm_mxfp4_decode<OUT_BF16, T, MF> : gemm_mxfp4_decode_chunked<OUT_BF16, T>;
   const int lds = sliced ? kDecWaves * nper * T * 4096
                          : T * (dec_tile_bytes(KC) > kDecWaves * 64 * 16 ? dec_tile_bytes(KC) : kDecWaves * 64 * 16);
   const bool cached = dev >= 0 && dev < 64;
-  if (!cached || !g_dec_attr[OUT_BF16][T - 1][dev].load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_mxfp4_decode<OUT_BF16, T>,
+  if (!cached || !g_dec_attr[OUT_BF16][T - 1][MF - 1][dev].load(std::memory_order_acquire)) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_mxfp4_decode<OUT_BF16, T, MF>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)gemm_mxfp4_decode_chunked<OUT_BF16, T>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
-    if (cached) g_dec_attr[OUT_BF16][T - 1][dev].store(1, std::memory_order_release);
+    if (cached) g_dec_attr[OUT_BF16][T - 1][MF - 1][dev].store(1, std::memory_order_release);
   }
   const int tiles = (N + 15) / 16;
   hipLaunchKernelGGL(kern, dim3((unsigned)((tiles + T - 1) / T)), dim3(kDecThreads), lds, st, Xq, Xs, Wq, Ws, Y, M, N, K,
@@ -659,14 +690,27 @@ hipError_t fp4_launch_gemm_mxfp4_decode(const uint8_t* Xq, const uint8_t* Xs, co
   e = fp4::device_cus(dev, cus);
   if (e != hipSuccess) return e;
   // two tiles per workgroup once there are at least three tiles per CU: the tiles share the X
-  // fragments, and every workgroup is resident at once (two per CU at up to 128 VGPRs)
-  const bool two = (N + 15) / 16 >= 3 * (int64_t)cus;
+  // fragments, and every workgroup is resident at once (two per CU at up to 128 VGPRs). Above
+  // 16 tokens only the sliced kernel runs, which holds two tiles' slices up to K = 4096.
+  const int mf = (int)((M + 15) / 16);
+  const bool two = (N + 15) / 16 >= 3 * (int64_t)cus && (mf == 1 || K <= 4096);
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (out_bf16)
-    return two ? fp4::launch_decode<true, 2>(Xq, Xs, Wq, Ws, m, n, k, Y, dev, st)
-               : fp4::launch_decode<true, 1>(Xq, Xs, Wq, Ws, m, n, k, Y, dev, st);
-  return two ? fp4::launch_decode<false, 2>(Xq, Xs, Wq, Ws, m, n, k, Y, dev, st)
-             : fp4::launch_decode<false, 1>(Xq, Xs, Wq, Ws, m, n, k, Y, dev, st);
+  auto go = [&](auto bf16, auto t, auto f) {
+    return fp4::launch_decode<decltype(bf16)::value, decltype(t)::value, decltype(f)::value>(Xq, Xs, Wq, Ws, m, n, k,
+                                                                                             Y, dev, st);
+  };
+  auto with_mf = [&](auto bf16, auto t) {
+    switch (mf) {
+      case 1: return go(bf16, t, std::integral_constant<int, 1>{});
+      case 2: return go(bf16, t, std::integral_constant<int, 2>{});
+      case 3: return go(bf16, t, std::integral_constant<int, 3>{});
+      default: return go(bf16, t, std::integral_constant<int, 4>{});
+    }
+  };
+  auto with_t = [&](auto bf16) {
+    return two ? with_mf(bf16, std::integral_constant<int, 2>{}) : with_mf(bf16, std::integral_constant<int, 1>{});
+  };
+  return out_bf16 ? with_t(std::true_type{}) : with_t(std::false_type{});
 }
 
 bool fp4_decode_fused_fits(int64_t M, int64_t N, int64_t K) {

@@ -62,12 +62,14 @@ def test_bench_traffic_lookups_are_in_the_map():
 
 def test_roofline_kernel_follows_the_library_dispatch():
     # the kernel fp4_linear runs for each workload (16-byte-aligned scales): decode kernel for M <= 16
-    # with K % 512 == 0, the 256-row-tile kernels for M, N >= 256, the general kernels otherwise
+    # with K % 512 == 0 (up to 64 rows when K <= 8192), the 256-row-tile kernels for M, N >= 256, the
+    # general kernels otherwise
     from microscaling_fp4_quantized_amd import workloads as WL
 
     want = {"tiny": "gemm_mxfp4_kernel", "decode1": "gemm_mxfp4_decode", "decode4": "gemm_mxfp4_decode",
             "decode16": "gemm_mxfp4_decode", "decode_wide1": "gemm_mxfp4_decode",
             "decode_wide4": "gemm_mxfp4_decode", "decode_wide16": "gemm_mxfp4_decode",
+            "decode_wide32": "gemm_mxfp4_decode", "decode_wide64": "gemm_mxfp4_decode",
             "prefill_nv": "gemm_nvfp4_ring", "prefill_mx": "gemm_mxfp4_ring", "prefill_mx_m4096": "gemm_mxfp4_ring",
             "large": "gemm_mxfp4_ring"}
     for name, w in WL.WORKLOADS.items():
@@ -77,7 +79,10 @@ def test_roofline_kernel_follows_the_library_dispatch():
         assert kern == want[name], name
         assert os.path.exists(os.path.join(ROOT, "microscaling_fp4_quantized_amd", "csrc", src))
     assert bench.gemm_kernel_for("mxfp4", 16, 4096, 4224)[1] == "gemm_mxfp4_kernel"   # K % 512 != 0
-    assert bench.gemm_kernel_for("mxfp4", 17, 4096, 4096)[1] == "gemm_mxfp4_kernel"   # neither
+    assert bench.gemm_kernel_for("mxfp4", 17, 4096, 4096)[1] == "gemm_mxfp4_decode"   # up to 64 tokens
+    assert bench.gemm_kernel_for("mxfp4", 64, 4096, 8192)[1] == "gemm_mxfp4_decode"
+    assert bench.gemm_kernel_for("mxfp4", 64, 4096, 8704)[1] == "gemm_mxfp4_kernel"   # K past the slices
+    assert bench.gemm_kernel_for("mxfp4", 65, 4096, 4096)[1] == "gemm_mxfp4_kernel"   # neither
     assert bench.gemm_kernel_for("nvfp4", 16, 4096, 4096)[1] == "gemm_nvfp4_kernel"
     assert bench.gemm_kernel_for("nvfp4", 256, 256, 256)[1] == "gemm_nvfp4_ring"
     assert bench.gemm_kernel_for("nvfp4", 256, 256, 384)[1] == "gemm_nvfp4_kernel"    # K % 256 != 0

@@ -71,6 +71,44 @@ def test_decode_kernel_unit_scales_exact(M, N, K):
     assert np.array_equal(host(yb.float()).astype(np.float64), O.bf16_rne_f64(ref))
 
 
+@pytest.mark.parametrize("M,N,K", [(17, 300, 512), (32, 4096, 4096), (33, 12300, 1024), (48, 777, 8192),
+                                   (64, 12289, 4096), (63, 4100, 8192), (64, 16, 2560), (40, 20, 1536),
+                                   (65, 300, 1024)])
+def test_decode_kernel_up_to_64_tokens_unit_scales_exact(M, N, K):
+    # 16 < M <= 64 with K % 512 == 0 and K <= 8192 runs the decode kernel with ceil(M / 16) column
+    # fragments of X per W fragment (17, 33: one and two rows into the last fragment; 48, 63, 64:
+    # three and four fragments); N >= 3 * 16 * 256 with K <= 4096 puts two tiles in a workgroup
+    # (12300, 12289: ragged last workgroup), K = 8192 gives each wave two slices with one tile,
+    # K = 512 and 2560 leave waves idle. M = 65 takes the general kernel.
+    rng = np.random.default_rng(5 * M + N + K)
+    c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    xs = np.full((M, K // 32), 127, np.uint8)
+    ws = np.full((N, K // 32), 127, np.uint8)
+    ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "mxfp4")
+    say(f"case decode-kernel (<= 64 tokens) unit-scale exact M {M} N {N} K {K}")
+    args = (dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), "mxfp4")
+    y = B.fp4_linear(*args)
+    assert np.array_equal(host(y).astype(np.float64), ref)
+    yb = B.fp4_linear(*args, out_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.float()).astype(np.float64), O.bf16_rne_f64(ref))
+
+
+@pytest.mark.parametrize("M,N,K", [(50, 1000, 2048), (64, 12300, 4096)])
+def test_decode_kernel_up_to_64_tokens_random_scales(M, N, K):
+    rng = np.random.default_rng(M + N)
+    c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    xs = rng.integers(110, 140, size=(M, K // 32)).astype(np.uint8)
+    ws = rng.integers(110, 140, size=(N, K // 32)).astype(np.uint8)
+    ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "mxfp4")
+    say(f"case decode-kernel (<= 64 tokens) random scales M {M} N {N} K {K}")
+    y = B.fp4_linear(dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), "mxfp4")
+    r = rel_fro(host(y), ref)
+    say(f"rel fro {r:.3e}")
+    assert r <= 1e-6
+
+
 def test_decode_kernel_random_scales():
     rng = np.random.default_rng(99)
     M, N, K = 7, 520, 3072
@@ -262,7 +300,8 @@ def test_ragged_shapes(fmt, block, M, N, K):
     assert r <= GEMM_REL_FRO_TOL
 
 
-@pytest.mark.parametrize("name", ["decode1", "decode4", "decode16", "decode_wide1", "decode_wide16"])
+@pytest.mark.parametrize("name", ["decode1", "decode4", "decode16", "decode_wide1", "decode_wide16", "decode_wide32",
+                                  "decode_wide64"])
 def test_decode_full(name):
     w = WL.WORKLOADS[name]
     x, wt = WL.draw_x(w), WL.draw_w(w)
