@@ -77,6 +77,8 @@ def gemm_kernel_for(fmt: str, M: int, N: int, K: int):
         if K % 512 == 0 and K < (1 << 25) and M >= 256 and N >= 256:
             return "gemm_mxfp4_ring.hip", "gemm_mxfp4_ring"
         return "gemm_mxfp4.hip", "gemm_mxfp4_kernel"
+    if M <= 16 and K % 512 == 0 and K <= 8192:
+        return "gemm_decode.hip", "gemm_nvfp4_decode"
     if K % 256 == 0 and K < (1 << 25) and M >= 256 and N >= 256:
         return "gemm_nvfp4_ring.hip", "gemm_nvfp4_ring"
     return "gemm_nvfp4.hip", "gemm_nvfp4_kernel"
@@ -415,6 +417,7 @@ def extra_rows(B, WL, torch, dev, groups=EXTRA_ROWS):
         del xq, xs, wq, ws, y
     if "decode" in groups:
         out.update(decode_rows(B, WL, torch, dev))
+        out.update(nv_decode_rows(B, WL, torch, dev))
     return out
 
 
@@ -498,6 +501,48 @@ def decode_rows(B, WL, torch, dev, names=("decode1", "decode4", "decode16", "dec
             row["step_from_bf16_x"] = {"two_calls_us": ms_two * 1e3}
             log(f"[bench] {name} step from bf16 X, W from HBM: two calls {ms_two * 1e3:.2f} us")
         out[f"gemm_{name}"] = row
+        del sets, wq, ws
+    return out
+
+
+def nv_decode_rows(B, WL, torch, dev, names=("decode_nv_wide1", "decode_nv_wide16")):
+    """NVFP4 decode-shaped layers (1 and 16 tokens, K=4096, W 14336x4096, block 16), timed as
+    decode_rows times the MXFP4 ones: a HIP graph of calls over copies of W totalling more than
+    512 MB (W from HBM), and warm_us with one W resident in the Infinity Cache."""
+    import math
+
+    out = {}
+    for name in names:
+        wl = WL.WORKLOADS[name]
+        xq, xs, xt = B.fp4_rotate_quantize(bf16_dev(WL.draw_x(wl), dev), wl.block, "nvfp4")
+        wq, ws, wt = B.fp4_quantize_weights(bf16_dev(WL.draw_w(wl), dev), wl.block, "nvfp4")
+        wbytes = wl.N * wl.K * (0.5 + 1.0 / 16)
+        n_sets = int(math.ceil(512e6 / wbytes))
+        sets = [(wq.clone(), ws.clone()) for _ in range(n_sets)]
+        y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
+        B.fp4_linear(xq, xs, wq, ws, "nvfp4", x_ts=xt, w_ts=wt, out=y)
+        ref = y.clone()
+        calls = 2 * n_sets
+
+        def gemm(i):
+            w_i = sets[i % n_sets]
+            B.fp4_linear(xq, xs, w_i[0], w_i[1], "nvfp4", x_ts=xt, w_ts=wt, out=y)
+
+        y.zero_()
+        ms = time_graph(gemm, calls, torch)
+        graph_ok = bool(torch.equal(y, ref))
+        ms_warm = time_graph(lambda i: B.fp4_linear(xq, xs, wq, ws, "nvfp4", x_ts=xt, w_ts=wt, out=y), 50, torch)
+        nbytes = wbytes + wl.M * wl.K * (0.5 + 1.0 / 16) + wl.M * wl.N * 4 + 8
+        out[f"gemm_{name}"] = {
+            "workload": f"{name}: M={wl.M} K={wl.K} N={wl.N} NVFP4 block {wl.block}, Y fp32",
+            "us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": nbytes, "w_copies": n_sets, "graph_replay_matches_eager": graph_ok,
+            "warm_us": ms_warm * 1e3,
+            "traffic": measured_traffic("gemm_nvfp4_decode@decode_nv_wide", "gemm_decode.hip"),
+            "note": f"{calls} calls in one HIP graph over {n_sets} copies of W ({n_sets * wbytes / 1e6:.0f} MB), "
+                    "so W comes from HBM; warm_us: one W, resident in the Infinity Cache"}
+        log(f"[bench] {name} NVFP4 GEMM {ms * 1e3:.2f} us with W from HBM = {nbytes / (ms * 1e-3) / 1e9:.0f} GB/s; "
+            f"W in cache {ms_warm * 1e3:.2f} us; graph matches eager: {graph_ok}")
         del sets, wq, ws
     return out
 

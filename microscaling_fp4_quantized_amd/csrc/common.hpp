@@ -67,6 +67,8 @@ __device__ __forceinline__ float e4m3_value(unsigned c) {
 hipError_t fp4_launch_rotate_quantize(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int block,
                                       int fmt, int rule, bool given_tensor_scale, const int8_t* signs,
                                       uint8_t* codes, uint8_t* scales, float* tensor_scale, hipStream_t stream);
+// Compute units of device `dev`, queried once per device.
+hipError_t fp4_device_cus(int dev, int* cus);
 hipError_t fp4_launch_gemm_mxfp4(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
                                  const uint8_t* Ws, int64_t M, int64_t N, int64_t K, void* Y,
                                  int out_bf16, hipStream_t stream);
@@ -82,6 +84,10 @@ hipError_t fp4_launch_gemm_mxfp4_decode(const uint8_t* Xq, const uint8_t* Xs, co
 hipError_t fp4_launch_gemm_mxfp4_ring(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
                                       int64_t M, int64_t N, int64_t K, void* Y, int out_bf16, hipStream_t stream);
 bool fp4_gemm_nvfp4_ring_fits(int64_t M, int64_t N, int64_t K);
+bool fp4_gemm_nvfp4_decode_fits(int64_t M, int64_t N, int64_t K);
+hipError_t fp4_launch_gemm_nvfp4_decode(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const uint8_t* Wq,
+                                        const uint8_t* Ws, const float* w_ts, int64_t M, int64_t N, int64_t K, void* Y,
+                                        int out_bf16, hipStream_t stream);
 hipError_t fp4_launch_gemm_nvfp4_ring(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const uint8_t* Wq,
                                       const uint8_t* Ws, const float* w_ts, int64_t M, int64_t N, int64_t K, void* Y,
                                       int out_bf16, hipStream_t stream);

@@ -713,6 +713,8 @@ hipError_t fp4_launch_gemm_mxfp4_decode(const uint8_t* Xq, const uint8_t* Xs, co
   return out_bf16 ? with_t(std::true_type{}) : with_t(std::false_type{});
 }
 
+hipError_t fp4_device_cus(int dev, int* cus) { return fp4::device_cus(dev, *cus); }
+
 bool fp4_decode_fused_fits(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && M <= 16 && N >= 1 && K % 512 == 0 && fp4::fused_lds_bytes((int)M, (int)K) <= 160 * 1024;
 }
@@ -763,4 +765,197 @@ hipError_t fp4_launch_decode_fused(const uint16_t* X, int64_t ldx, int block, co
     case 64: return fp4::launch_fused<64>(X, ldx, Wq, Ws, (int)M, (int)N, (int)K, Y, out_bf16, st);
     default: return fp4::launch_fused<128>(X, ldx, Wq, Ws, (int)M, (int)N, (int)K, Y, out_bf16, st);
   }
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 decode (M <= 16): the weight streaming of gemm_mxfp4_decode, with the E4M3 group scales
+// applied by dequantizing both operands exactly to fp16 in registers (e2m1 * d has at most 6
+// significant bits within [2^-10, 2688]) and multiplying with v_mfma_f32_16x16x32_f16: W (from
+// the wave's LDS area) as the row operand, X (M rows, read from L2) as the column operand, so each
+// lane again ends with 4 consecutive features of one token. Within each 128-element block q of a
+// slice, k-step t of lane group g takes elements 32 (4 q + g) + 8 t .. + 7 of both operands: a
+// lane reads one 16-byte chunk of codes per block, and every product still pairs x_k with w_k.
+// The reduced sums are multiplied by x_ts * w_ts.
+// "Bridging the Gap Between Promise and Performance for Microscaling FP4 Quantization"
+// (gist.science, Spanish edition), Resumen técnico §2.B item 2 (NVFP4 group and tensor scales).
+// ---------------------------------------------------------------------------
+namespace fp4 {
+namespace {
+
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+
+// E4M3 codes in the low two bytes of w -> the exact fp16 pair (every E4M3FN value is an fp16 number)
+__device__ __forceinline__ h2v nv_scale_pair(unsigned w) { return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false); }
+
+// Eight E2M1 codes (one dword, element 2i in the low nibble of byte i) times the fp16 scale d
+__device__ __forceinline__ h8v nv_dequant8(unsigned codes, _Float16 d) {
+  const h2v dd = {d, d};
+  v4u o;
+  o[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * dd);
+  o[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * dd);
+  o[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * dd);
+  o[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * dd);
+  return __builtin_bit_cast(h8v, o);
+}
+
+// The two scale bytes of chunk c = 4 q + g (bytes 2c, 2c + 1 of a row's 32 per slice): dword
+// 2 q + g / 2 of the 8, half g % 2.
+template <int Q>
+__device__ __forceinline__ h2v nv_chunk_scales(const v4u (&s)[2], int g) {
+  constexpr int d0 = 2 * Q, d1 = 2 * Q + 1;
+  const unsigned w = (g >> 1) ? s[d1 >> 2][d1 & 3] : s[d0 >> 2][d0 & 3];
+  return nv_scale_pair(w >> (16 * (g & 1)));
+}
+
+// At most 128 VGPRs (4 waves per SIMD). NPER slices per wave, as gemm_mxfp4_decode.
+template <bool OUT_BF16, int T>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemm_nvfp4_decode(
+    const uint8_t* __restrict__ Xq, const uint8_t* __restrict__ Xs, const float* __restrict__ x_ts,
+    const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Ws, const float* __restrict__ w_ts,
+    void* __restrict__ Yv, int M, int N, int K, int NPER) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int NJ = kDecMaxSlices / T;  // the launch takes this kernel only when NPER <= NJ
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const unsigned KB = (unsigned)K / 2, KS = (unsigned)K / 16;
+  const int nsl = K / kDecSlice;
+  const int nb = blockIdx.x * 16 * T;
+  const int area_bytes = NPER * T * 4096;
+  uint8_t* area = lds + wave * area_bytes;  // tile-slice (j, tt) at (j * T + tt) * 4 KB: 16 rows x 256 bytes
+  const size_t xrow = (size_t)min(r, M - 1);
+
+  // W codes of the wave's slices into its area by the LDS DMA, as in gemm_mxfp4_decode (the code
+  // layout is the same); the 32 E4M3 bytes of the lane's row and slice into registers.
+  v4u wsv[NJ][T][2];
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) {
+    const int n0 = __builtin_amdgcn_readfirstlane(min(nb + 16 * tt, N - 1));
+    const unsigned rows = (unsigned)__builtin_amdgcn_readfirstlane(min(16, N - n0));
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(Wq + (size_t)n0 * KB, rows * KB);
+    const size_t wrow = (size_t)min(n0 + r, N - 1);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int sl = wave + 8 * j;
+      if (j < NPER && sl < nsl) {  // wave-uniform
+        uint8_t* dst = area + (j * T + tt) * 4096;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 4 * i + (lane >> 4), q = lane & 15;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(dst + i * 1024), 16,
+                                                   (unsigned)row * KB + (unsigned)sl * 256u + 16u * (unsigned)(q ^ row),
+                                                   0, 0, 0);
+        }
+        const uint8_t* ps = Ws + wrow * KS + (size_t)sl * 32;
+        wsv[j][tt][0] = *reinterpret_cast<const v4u*>(ps);
+        wsv[j][tt][1] = *reinterpret_cast<const v4u*>(ps + 16);
+      }
+    }
+  }
+  v4f acc[T];
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) acc[tt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int sl = wave + 8 * j;
+    if (j < NPER && sl < nsl) {
+      // X of token r (clamped to M - 1): chunk 4 q + g of the slice for each block q, and the
+      // token's 32 E4M3 bytes of the slice
+      v4u xc[4], xsv[2];
+      const uint8_t* px = Xq + xrow * KB + (size_t)sl * 256 + 16 * g;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xc[q] = *reinterpret_cast<const v4u*>(px + 64 * q);
+      const uint8_t* pxs = Xs + xrow * KS + (size_t)sl * 32;
+      xsv[0] = *reinterpret_cast<const v4u*>(pxs);
+      xsv[1] = *reinterpret_cast<const v4u*>(pxs + 16);
+      // this wave's DMA has landed (its area is read by no other wave until the reduction)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      asm volatile("" ::: "memory");
+      auto block = [&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        const h2v dx = nv_chunk_scales<q>(xsv, g);
+        v4u wc[T];
+        h2v dw[T];
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+          wc[tt] = *reinterpret_cast<const v4u*>(area + (j * T + tt) * 4096 + r * 256 + 16 * (((4 * q + g) ^ r) & 15));
+          dw[tt] = nv_chunk_scales<q>(wsv[j][tt], g);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {  // elements 32 (4 q + g) + 8 t .. + 7: group 2 (4 q + g) + t / 2
+          const h8v b = nv_dequant8(xc[q][t], t < 2 ? dx[0] : dx[1]);
+#pragma unroll
+          for (int tt = 0; tt < T; ++tt) {
+            const h8v a = nv_dequant8(wc[tt][t], t < 2 ? dw[tt][0] : dw[tt][1]);
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[tt], 0, 0, 0);
+          }
+        }
+      };
+      block(std::integral_constant<int, 0>{});
+      block(std::integral_constant<int, 1>{});
+      block(std::integral_constant<int, 2>{});
+      block(std::integral_constant<int, 3>{});
+    }
+  }
+  // partial sums into the wave's own area, then the fixed-order sum and the tensor scales
+  v4f* red = reinterpret_cast<v4f*>(area);
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) red[tt * 64 + lane] = acc[tt];
+  __syncthreads();
+  if (wave >= T) return;
+  const int tt = wave;
+  v4f sum = reinterpret_cast<const v4f*>(lds)[tt * 64 + lane];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) sum += reinterpret_cast<const v4f*>(lds + w * area_bytes)[tt * 64 + lane];
+  const float ts = x_ts[0] * w_ts[0];
+  // lane holds D[n + 4g + i][m = r], i = 0..3: four consecutive features of token r
+  store_out<OUT_BF16>(Yv, M, N, lane & 15, nb + 16 * tt + 4 * (lane >> 4), sum * ts);
+}
+
+std::atomic<int> g_nvdec_attr[2][2][64];  // per output dtype, T and device: dynamic-LDS limit raised
+
+template <bool OUT_BF16, int T>
+hipError_t launch_nv_decode(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const uint8_t* Wq,
+                            const uint8_t* Ws, const float* w_ts, int M, int N, int K, void* Y, int dev, hipStream_t st) {
+  const int nper = (K / kDecSlice + kDecWaves - 1) / kDecWaves;  // slices per wave
+  if (nper > kDecMaxSlices / T) return hipErrorInvalidValue;    // excluded by the fits test and the T choice
+  auto kern = gemm_nvfp4_decode<OUT_BF16, T>;
+  const bool cached = dev >= 0 && dev < 64;
+  if (!cached || !g_nvdec_attr[OUT_BF16][T - 1][dev].load(std::memory_order_acquire)) {
+    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    if (cached) g_nvdec_attr[OUT_BF16][T - 1][dev].store(1, std::memory_order_release);
+  }
+  const int tiles = (N + 15) / 16;
+  hipLaunchKernelGGL(kern, dim3((unsigned)((tiles + T - 1) / T)), dim3(kDecThreads), kDecWaves * nper * T * 4096, st, Xq,
+                     Xs, x_ts, Wq, Ws, w_ts, Y, M, N, K, nper);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace fp4
+
+// 1..16 tokens, K a multiple of 512 whose slices fit the waves' LDS areas with one tile (K <= 8192)
+bool fp4_gemm_nvfp4_decode_fits(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= 16 && N >= 1 && K % 512 == 0 && K <= 8192;
+}
+
+hipError_t fp4_launch_gemm_nvfp4_decode(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const uint8_t* Wq,
+                                        const uint8_t* Ws, const float* w_ts, int64_t M, int64_t N, int64_t K, void* Y,
+                                        int out_bf16, hipStream_t st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int cus = 0;
+  e = fp4::device_cus(dev, cus);
+  if (e != hipSuccess) return e;
+  // two tiles per workgroup (sharing the X fragments) once there are at least three tiles per CU
+  // and two tiles' slices fit the waves' areas (K <= 4096)
+  const bool two = (N + 15) / 16 >= 3 * (int64_t)cus && K <= 4096;
+  const int m = (int)M, n = (int)N, k = (int)K;
+  if (out_bf16)
+    return two ? fp4::launch_nv_decode<true, 2>(Xq, Xs, x_ts, Wq, Ws, w_ts, m, n, k, Y, dev, st)
+               : fp4::launch_nv_decode<true, 1>(Xq, Xs, x_ts, Wq, Ws, w_ts, m, n, k, Y, dev, st);
+  return two ? fp4::launch_nv_decode<false, 2>(Xq, Xs, x_ts, Wq, Ws, w_ts, m, n, k, Y, dev, st)
+             : fp4::launch_nv_decode<false, 1>(Xq, Xs, x_ts, Wq, Ws, w_ts, m, n, k, Y, dev, st);
 }

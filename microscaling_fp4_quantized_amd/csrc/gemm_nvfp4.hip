@@ -175,6 +175,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_nvfp4_kernel(
     }
 }
 
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_general(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const uint8_t* Wq,
+                          const uint8_t* Ws, const float* w_ts, int64_t M, int64_t N, int64_t K, void* Y,
+                          int out_bf16, hipStream_t st) {
+  using C = NvCfg<BM, BN, WM, WN>;
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+  const dim3 grid(tiles_m * tiles_n), block(C::NT);
+  if (out_bf16)
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<BM, BN, WM, WN, true>), grid, block, 0, st, Xq, Xs, x_ts, Wq, Ws, w_ts, Y,
+                       (int)M, (int)N, (int)K, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<BM, BN, WM, WN, false>), grid, block, 0, st, Xq, Xs, x_ts, Wq, Ws, w_ts, Y,
+                       (int)M, (int)N, (int)K, tiles_n);
+  return hipGetLastError();
+}
+
 }  // namespace
 }  // namespace fp4
 
@@ -185,17 +201,18 @@ hipError_t fp4_launch_gemm_nvfp4(const uint8_t* Xq, const uint8_t* Xs, const flo
   // aligned to 16 bytes (K % 256 == 0 keeps every row aligned then); the general kernel below
   // reads 2-byte pieces.
   const bool scales16 = ((reinterpret_cast<uintptr_t>(Xs) | reinterpret_cast<uintptr_t>(Ws)) & 15) == 0;
+  if (scales16 && fp4_gemm_nvfp4_decode_fits(M, N, K))
+    return fp4_launch_gemm_nvfp4_decode(Xq, Xs, x_ts, Wq, Ws, w_ts, M, N, K, Y, out_bf16, st);
   if (scales16 && fp4_gemm_nvfp4_ring_fits(M, N, K))
     return fp4_launch_gemm_nvfp4_ring(Xq, Xs, x_ts, Wq, Ws, w_ts, M, N, K, Y, out_bf16, st);
-  constexpr int BM = 128, BN = 128, WM = 64, WN = 64;
-  using C = fp4::NvCfg<BM, BN, WM, WN>;
-  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-  const dim3 grid(tiles_m * tiles_n), block(C::NT);
-  if (out_bf16)
-    hipLaunchKernelGGL((fp4::gemm_nvfp4_kernel<BM, BN, WM, WN, true>), grid, block, 0, st, Xq, Xs, x_ts,
-                       Wq, Ws, w_ts, Y, (int)M, (int)N, (int)K, tiles_n);
-  else
-    hipLaunchKernelGGL((fp4::gemm_nvfp4_kernel<BM, BN, WM, WN, false>), grid, block, 0, st, Xq, Xs, x_ts,
-                       Wq, Ws, w_ts, Y, (int)M, (int)N, (int)K, tiles_n);
-  return hipGetLastError();
+  // 128x128 tiles on 4 waves; 64x64 tiles when those would give fewer than two workgroups per CU
+  // and M <= 192 (at N = 14336: 1.4x faster for 1 to 16 rows, 1.1-1.2x for 65 to 192; slower at
+  // 255 rows, where the 16-bit products outweigh the wider grid)
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = fp4_device_cus(dev, &cus);
+  if (e != hipSuccess) return e;
+  const bool small = ((M + 127) / 128) * ((N + 127) / 128) < 2 * (int64_t)cus && M <= 192;
+  return small ? fp4::launch_general<64, 64, 32, 32>(Xq, Xs, x_ts, Wq, Ws, w_ts, M, N, K, Y, out_bf16, st)
+               : fp4::launch_general<128, 128, 64, 64>(Xq, Xs, x_ts, Wq, Ws, w_ts, M, N, K, Y, out_bf16, st);
 }

@@ -239,6 +239,46 @@ def test_nv_large_tile_kernel_unit_scales_exact(M, N, K):
     assert np.array_equal(host(yb.float()).astype(np.float64), O.bf16_rne_f64(ref))
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 77, 512), (5, 300, 1536), (16, 4096, 4096), (3, 130, 8192), (16, 18, 2560),
+                                   (9, 12300, 1024), (16, 12289, 4096), (8, 14336, 4096), (2, 33, 8192),
+                                   (4, 200, 9216), (16, 64, 640)])
+def test_nv_decode_kernel_unit_scales_exact(M, N, K):
+    # NVFP4 with M <= 16, K % 512 == 0 and K <= 8192 runs the weight-streaming decode kernel: 8 waves
+    # each dequantize their own 512-wide K slices of W (from LDS) and X (from L2) to fp16 (K = 8192:
+    # two slices per wave; 512, 1536, 2560 leave waves idle); N >= 3 * 16 * 256 with K <= 4096 puts
+    # two 16-row tiles in a workgroup (12300, 12289: ragged last workgroup). K = 9216 and 640 take the
+    # general kernel. Unit group and tensor scales make every sum exact.
+    rng = np.random.default_rng(7 * M + N + K)
+    c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    xs = np.full((M, K // 16), 0x38, np.uint8)
+    ws = np.full((N, K // 16), 0x38, np.uint8)
+    ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "nvfp4", 1.0, 1.0)
+    say(f"case NV decode-kernel unit-scale exact M {M} N {N} K {K}")
+    args = (dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), "nvfp4")
+    y = B.fp4_linear(*args, x_ts=dev_f32(1.0), w_ts=dev_f32(1.0))
+    assert np.array_equal(host(y).astype(np.float64), ref)
+    yb = B.fp4_linear(*args, x_ts=dev_f32(1.0), w_ts=dev_f32(1.0), out_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.float()).astype(np.float64), O.bf16_rne_f64(ref))
+
+
+@pytest.mark.parametrize("M,N,K", [(7, 520, 3072), (16, 12300, 4096), (1, 300, 8192)])
+def test_nv_decode_kernel_random_scales(M, N, K):
+    rng = np.random.default_rng(13 * M + N)
+    c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    xs = rng.integers(0, 0x7F, size=(M, K // 16)).astype(np.uint8)  # every finite E4M3 code, subnormals included
+    ws = rng.integers(0, 0x7F, size=(N, K // 16)).astype(np.uint8)
+    xt, wt = 0.0123, 3.5e-3
+    ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "nvfp4", np.float32(xt), np.float32(wt))
+    say(f"case NV decode-kernel random scales M {M} N {N} K {K}")
+    y = B.fp4_linear(dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), "nvfp4",
+                     x_ts=dev_f32(xt), w_ts=dev_f32(wt))
+    r = rel_fro(host(y), ref)
+    say(f"rel fro {r:.3e}")
+    assert r <= 1e-6
+
+
 @pytest.mark.parametrize("M,N,K", [(512, 768, 2048), (259, 300, 512), (2048, 12544, 768)])
 def test_nv_large_tile_kernel_random_scales(M, N, K):
     rng = np.random.default_rng(11 * M + N)
@@ -301,7 +341,7 @@ def test_ragged_shapes(fmt, block, M, N, K):
 
 
 @pytest.mark.parametrize("name", ["decode1", "decode4", "decode16", "decode_wide1", "decode_wide16", "decode_wide32",
-                                  "decode_wide64"])
+                                  "decode_wide64", "decode_nv_wide1", "decode_nv_wide16"])
 def test_decode_full(name):
     w = WL.WORKLOADS[name]
     x, wt = WL.draw_x(w), WL.draw_w(w)
