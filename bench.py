@@ -77,7 +77,7 @@ def gemm_kernel_for(fmt: str, M: int, N: int, K: int):
         if K % 512 == 0 and K < (1 << 25) and M >= 256 and N >= 256:
             return "gemm_mxfp4_ring.hip", "gemm_mxfp4_ring"
         return "gemm_mxfp4.hip", "gemm_mxfp4_kernel"
-    if M <= 16 and K % 512 == 0 and K <= 8192:
+    if M <= 64 and K % 512 == 0 and K <= 8192:
         return "gemm_decode.hip", "gemm_nvfp4_decode"
     if K % 256 == 0 and K < (1 << 25) and M >= 256 and N >= 256:
         return "gemm_nvfp4_ring.hip", "gemm_nvfp4_ring"
@@ -505,8 +505,8 @@ def decode_rows(B, WL, torch, dev, names=("decode1", "decode4", "decode16", "dec
     return out
 
 
-def nv_decode_rows(B, WL, torch, dev, names=("decode_nv_wide1", "decode_nv_wide16")):
-    """NVFP4 decode-shaped layers (1 and 16 tokens, K=4096, W 14336x4096, block 16), timed as
+def nv_decode_rows(B, WL, torch, dev, names=("decode_nv_wide1", "decode_nv_wide16", "decode_nv_wide64")):
+    """NVFP4 decode-shaped layers (1, 16 and 64 tokens, K=4096, W 14336x4096, block 16), timed as
     decode_rows times the MXFP4 ones: a HIP graph of calls over copies of W totalling more than
     512 MB (W from HBM), and warm_us with one W resident in the Infinity Cache."""
     import math
@@ -538,7 +538,8 @@ def nv_decode_rows(B, WL, torch, dev, names=("decode_nv_wide1", "decode_nv_wide1
             "us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes": nbytes, "w_copies": n_sets, "graph_replay_matches_eager": graph_ok,
             "warm_us": ms_warm * 1e3,
-            "traffic": measured_traffic("gemm_nvfp4_decode@decode_nv_wide", "gemm_decode.hip"),
+            "traffic": measured_traffic("gemm_nvfp4_decode@decode_nv_wide" + ("64" if wl.M > 16 else ""),
+                                        "gemm_decode.hip"),
             "note": f"{calls} calls in one HIP graph over {n_sets} copies of W ({n_sets * wbytes / 1e6:.0f} MB), "
                     "so W comes from HBM; warm_us: one W, resident in the Infinity Cache"}
         log(f"[bench] {name} NVFP4 GEMM {ms * 1e3:.2f} us with W from HBM = {nbytes / (ms * 1e-3) / 1e9:.0f} GB/s; "

@@ -55,8 +55,11 @@ TRAFFIC_MAP = [
      "decode_wide32 M=32 K=4096 N=14336 fp32 Y, two 16-row tiles and two X fragments per workgroup, W from HBM"),
     ("gemm_mxfp4_decode<false, 2, 4>", 229376, "gemm_mxfp4_decode@decode_wide64", "gemm_decode.hip",
      "decode_wide64 M=64 K=4096 N=14336 fp32 Y, two 16-row tiles and four X fragments per workgroup, W from HBM"),
-    ("gemm_nvfp4_decode<false, 2>", 229376, "gemm_nvfp4_decode@decode_nv_wide", "gemm_decode.hip",
+    ("gemm_nvfp4_decode<false, 2, 1>", 229376, "gemm_nvfp4_decode@decode_nv_wide", "gemm_decode.hip",
      "decode_nv_wide M in {1,16} K=4096 N=14336 NVFP4 block 16 fp32 Y, two 16-row tiles per workgroup, W from HBM"),
+    ("gemm_nvfp4_decode<false, 2, 4>", 229376, "gemm_nvfp4_decode@decode_nv_wide64", "gemm_decode.hip",
+     "decode_nv_wide64 M=64 K=4096 N=14336 NVFP4 block 16 fp32 Y, two 16-row tiles and four X fragments per "
+     "workgroup, W from HBM"),
     ("rotate_quant_mx<32, 0>", 4194304, "rotate_quant_mx@stress_mx32", "rotate_quant.hip",
      "stress_mx32 16384x8192 block 32"),
     ("rotate_quant_mx<128, 0>", 4194304, "rotate_quant_mx@stress_mx128", "rotate_quant.hip",

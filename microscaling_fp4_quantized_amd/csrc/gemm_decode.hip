@@ -768,7 +768,8 @@ hipError_t fp4_launch_decode_fused(const uint16_t* X, int64_t ldx, int block, co
 }
 
 // ---------------------------------------------------------------------------
-// NVFP4 decode (M <= 16): the weight streaming of gemm_mxfp4_decode, with the E4M3 group scales
+// NVFP4 decode (M <= 16, or up to 64 rows as MF = ceil(M / 16) column fragments of X that share
+// every dequantized W fragment): the weight streaming of gemm_mxfp4_decode, with the E4M3 group scales
 // applied by dequantizing both operands exactly to fp16 in registers (e2m1 * d has at most 6
 // significant bits within [2^-10, 2688]) and multiplying with v_mfma_f32_16x16x32_f16: W (from
 // the wave's LDS area) as the row operand, X (M rows, read from L2) as the column operand, so each
@@ -809,13 +810,14 @@ __device__ __forceinline__ h2v nv_chunk_scales(const v4u (&s)[2], int g) {
 }
 
 // At most 128 VGPRs (4 waves per SIMD). NPER slices per wave, as gemm_mxfp4_decode.
-template <bool OUT_BF16, int T>
+template <bool OUT_BF16, int T, int MF>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemm_nvfp4_decode(
     const uint8_t* __restrict__ Xq, const uint8_t* __restrict__ Xs, const float* __restrict__ x_ts,
     const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Ws, const float* __restrict__ w_ts,
     void* __restrict__ Yv, int M, int N, int K, int NPER) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int NJ = kDecMaxSlices / T;  // the launch takes this kernel only when NPER <= NJ
+  static_assert(MF >= 1 && MF <= 4 && MF * T <= kDecWaves, "column fragments");
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const unsigned KB = (unsigned)K / 2, KS = (unsigned)K / 16;
@@ -823,7 +825,6 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
   const int nb = blockIdx.x * 16 * T;
   const int area_bytes = NPER * T * 4096;
   uint8_t* area = lds + wave * area_bytes;  // tile-slice (j, tt) at (j * T + tt) * 4 KB: 16 rows x 256 bytes
-  const size_t xrow = (size_t)min(r, M - 1);
 
   // W codes of the wave's slices into its area by the LDS DMA, as in gemm_mxfp4_decode (the code
   // layout is the same); the 32 E4M3 bytes of the lane's row and slice into registers.
@@ -852,42 +853,97 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
       }
     }
   }
-  v4f acc[T];
+  v4f acc[MF][T];
 #pragma unroll
-  for (int tt = 0; tt < T; ++tt) acc[tt] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int f = 0; f < MF; ++f)
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) acc[f][tt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int sl = wave + 8 * j;
     if (j < NPER && sl < nsl) {
-      // X of token r (clamped to M - 1): chunk 4 q + g of the slice for each block q, and the
-      // token's 32 E4M3 bytes of the slice
-      v4u xc[4], xsv[2];
-      const uint8_t* px = Xq + xrow * KB + (size_t)sl * 256 + 16 * g;
+      // X fragment f: token 16 f + r (clamped to M - 1); per block q, chunk 4 q + g of the slice
+      // and the two E4M3 bytes of that chunk
+      auto x_codes = [&](int f, int q) {
+        const size_t xrow = (size_t)min(16 * f + r, M - 1);
+        return *reinterpret_cast<const v4u*>(Xq + xrow * KB + (size_t)sl * 256 + 16 * (4 * q + g));
+      };
+      auto x_scales = [&](int f, int q) {  // the dword of the token's slice scales holding them
+        const size_t xrow = (size_t)min(16 * f + r, M - 1);
+        const unsigned w = *reinterpret_cast<const unsigned*>(Xs + xrow * KS + (size_t)sl * 32 + 4 * (2 * q + (g >> 1)));
+        return nv_scale_pair(w >> (16 * (g & 1)));
+      };
+      auto w_chunk = [&](int tt, int q) {
+        return *reinterpret_cast<const v4u*>(area + (j * T + tt) * 4096 + r * 256 + 16 * (((4 * q + g) ^ r) & 15));
+      };
+      if constexpr (MF == 1) {
+        // one X fragment: all of its codes and scales of the slice requested before the wait for W,
+        // and each W fragment dequantized right before its product
+        v4u xc[4], xsv[2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) xc[q] = *reinterpret_cast<const v4u*>(px + 64 * q);
-      const uint8_t* pxs = Xs + xrow * KS + (size_t)sl * 32;
-      xsv[0] = *reinterpret_cast<const v4u*>(pxs);
-      xsv[1] = *reinterpret_cast<const v4u*>(pxs + 16);
-      // this wave's DMA has landed (its area is read by no other wave until the reduction)
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        for (int q = 0; q < 4; ++q) xc[q] = x_codes(0, q);
+        const uint8_t* pxs = Xs + (size_t)min(r, M - 1) * KS + (size_t)sl * 32;
+        xsv[0] = *reinterpret_cast<const v4u*>(pxs);
+        xsv[1] = *reinterpret_cast<const v4u*>(pxs + 16);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
+        asm volatile("" ::: "memory");
+        auto block1 = [&](auto qc) {
+          constexpr int q = decltype(qc)::value;
+          const h2v dx = nv_chunk_scales<q>(xsv, g);
+          v4u wc[T];
+          h2v dw[T];
+#pragma unroll
+          for (int tt = 0; tt < T; ++tt) {
+            wc[tt] = w_chunk(tt, q);
+            dw[tt] = nv_chunk_scales<q>(wsv[j][tt], g);
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {  // elements 32 (4 q + g) + 8 t .. + 7: group 2 (4 q + g) + t / 2
+            const h8v b = nv_dequant8(xc[q][t], t < 2 ? dx[0] : dx[1]);
+#pragma unroll
+            for (int tt = 0; tt < T; ++tt) {
+              const h8v a = nv_dequant8(wc[tt][t], t < 2 ? dw[tt][0] : dw[tt][1]);
+              acc[0][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[0][tt], 0, 0, 0);
+            }
+          }
+        };
+        block1(std::integral_constant<int, 0>{});
+        block1(std::integral_constant<int, 1>{});
+        block1(std::integral_constant<int, 2>{});
+        block1(std::integral_constant<int, 3>{});
+        continue;
+      }
+      // several X fragments: the first block of each requested before the wait for W; per block, W
+      // dequantized once and shared by the MF fragments
+      v4u xc0[MF];
+      h2v dx0[MF];
+#pragma unroll
+      for (int f = 0; f < MF; ++f) {
+        xc0[f] = x_codes(f, 0);
+        dx0[f] = x_scales(f, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
       asm volatile("" ::: "memory");
       auto block = [&](auto qc) {
         constexpr int q = decltype(qc)::value;
-        const h2v dx = nv_chunk_scales<q>(xsv, g);
-        v4u wc[T];
-        h2v dw[T];
+        h8v wf[T][4];
 #pragma unroll
         for (int tt = 0; tt < T; ++tt) {
-          wc[tt] = *reinterpret_cast<const v4u*>(area + (j * T + tt) * 4096 + r * 256 + 16 * (((4 * q + g) ^ r) & 15));
-          dw[tt] = nv_chunk_scales<q>(wsv[j][tt], g);
+          const v4u wc = w_chunk(tt, q);
+          const h2v dw = nv_chunk_scales<q>(wsv[j][tt], g);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) wf[tt][t] = nv_dequant8(wc[t], t < 2 ? dw[0] : dw[1]);
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {  // elements 32 (4 q + g) + 8 t .. + 7: group 2 (4 q + g) + t / 2
-          const h8v b = nv_dequant8(xc[q][t], t < 2 ? dx[0] : dx[1]);
+        for (int f = 0; f < MF; ++f) {
+          const v4u xc = q == 0 ? xc0[f] : x_codes(f, q);
+          const h2v dx = q == 0 ? dx0[f] : x_scales(f, q);
 #pragma unroll
-          for (int tt = 0; tt < T; ++tt) {
-            const h8v a = nv_dequant8(wc[tt][t], t < 2 ? dw[tt][0] : dw[tt][1]);
-            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[tt], 0, 0, 0);
+          for (int t = 0; t < 4; ++t) {
+            const h8v b = nv_dequant8(xc[t], t < 2 ? dx[0] : dx[1]);
+#pragma unroll
+            for (int tt = 0; tt < T; ++tt)
+              acc[f][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[tt][t], b, acc[f][tt], 0, 0, 0);
           }
         }
       };
@@ -897,34 +953,37 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
       block(std::integral_constant<int, 3>{});
     }
   }
-  // partial sums into the wave's own area, then the fixed-order sum and the tensor scales
+  // partial sums into the wave's own area, then the fixed-order sum of output fragment (f, tt)
+  // by wave f * T + tt, and the tensor scales
   v4f* red = reinterpret_cast<v4f*>(area);
 #pragma unroll
-  for (int tt = 0; tt < T; ++tt) red[tt * 64 + lane] = acc[tt];
-  __syncthreads();
-  if (wave >= T) return;
-  const int tt = wave;
-  v4f sum = reinterpret_cast<const v4f*>(lds)[tt * 64 + lane];
+  for (int f = 0; f < MF; ++f)
 #pragma unroll
-  for (int w = 1; w < kDecWaves; ++w) sum += reinterpret_cast<const v4f*>(lds + w * area_bytes)[tt * 64 + lane];
+    for (int tt = 0; tt < T; ++tt) red[(f * T + tt) * 64 + lane] = acc[f][tt];
+  __syncthreads();
+  if (wave >= MF * T) return;
+  const int qo = wave, f = qo / T, tt = qo % T;
+  v4f sum = reinterpret_cast<const v4f*>(lds)[qo * 64 + lane];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) sum += reinterpret_cast<const v4f*>(lds + w * area_bytes)[qo * 64 + lane];
   const float ts = x_ts[0] * w_ts[0];
-  // lane holds D[n + 4g + i][m = r], i = 0..3: four consecutive features of token r
-  store_out<OUT_BF16>(Yv, M, N, lane & 15, nb + 16 * tt + 4 * (lane >> 4), sum * ts);
+  // lane holds D[n + 4g + i][m = 16 f + r], i = 0..3: four consecutive features of one token
+  store_out<OUT_BF16>(Yv, M, N, 16 * f + (lane & 15), nb + 16 * tt + 4 * (lane >> 4), sum * ts);
 }
 
-std::atomic<int> g_nvdec_attr[2][2][64];  // per output dtype, T and device: dynamic-LDS limit raised
+std::atomic<int> g_nvdec_attr[2][2][4][64];  // per output dtype, T, MF and device: dynamic-LDS limit raised
 
-template <bool OUT_BF16, int T>
+template <bool OUT_BF16, int T, int MF>
 hipError_t launch_nv_decode(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const uint8_t* Wq,
                             const uint8_t* Ws, const float* w_ts, int M, int N, int K, void* Y, int dev, hipStream_t st) {
   const int nper = (K / kDecSlice + kDecWaves - 1) / kDecWaves;  // slices per wave
   if (nper > kDecMaxSlices / T) return hipErrorInvalidValue;    // excluded by the fits test and the T choice
-  auto kern = gemm_nvfp4_decode<OUT_BF16, T>;
+  auto kern = gemm_nvfp4_decode<OUT_BF16, T, MF>;
   const bool cached = dev >= 0 && dev < 64;
-  if (!cached || !g_nvdec_attr[OUT_BF16][T - 1][dev].load(std::memory_order_acquire)) {
+  if (!cached || !g_nvdec_attr[OUT_BF16][T - 1][MF - 1][dev].load(std::memory_order_acquire)) {
     const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
-    if (cached) g_nvdec_attr[OUT_BF16][T - 1][dev].store(1, std::memory_order_release);
+    if (cached) g_nvdec_attr[OUT_BF16][T - 1][MF - 1][dev].store(1, std::memory_order_release);
   }
   const int tiles = (N + 15) / 16;
   hipLaunchKernelGGL(kern, dim3((unsigned)((tiles + T - 1) / T)), dim3(kDecThreads), kDecWaves * nper * T * 4096, st, Xq,
@@ -935,9 +994,9 @@ hipError_t launch_nv_decode(const uint8_t* Xq, const uint8_t* Xs, const float* x
 }  // namespace
 }  // namespace fp4
 
-// 1..16 tokens, K a multiple of 512 whose slices fit the waves' LDS areas with one tile (K <= 8192)
+// 1..64 tokens, K a multiple of 512 whose slices fit the waves' LDS areas with one tile (K <= 8192)
 bool fp4_gemm_nvfp4_decode_fits(int64_t M, int64_t N, int64_t K) {
-  return M >= 1 && M <= 16 && N >= 1 && K % 512 == 0 && K <= 8192;
+  return M >= 1 && M <= 64 && N >= 1 && K % 512 == 0 && K <= 8192;
 }
 
 hipError_t fp4_launch_gemm_nvfp4_decode(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const uint8_t* Wq,
@@ -952,10 +1011,21 @@ hipError_t fp4_launch_gemm_nvfp4_decode(const uint8_t* Xq, const uint8_t* Xs, co
   // two tiles per workgroup (sharing the X fragments) once there are at least three tiles per CU
   // and two tiles' slices fit the waves' areas (K <= 4096)
   const bool two = (N + 15) / 16 >= 3 * (int64_t)cus && K <= 4096;
-  const int m = (int)M, n = (int)N, k = (int)K;
-  if (out_bf16)
-    return two ? fp4::launch_nv_decode<true, 2>(Xq, Xs, x_ts, Wq, Ws, w_ts, m, n, k, Y, dev, st)
-               : fp4::launch_nv_decode<true, 1>(Xq, Xs, x_ts, Wq, Ws, w_ts, m, n, k, Y, dev, st);
-  return two ? fp4::launch_nv_decode<false, 2>(Xq, Xs, x_ts, Wq, Ws, w_ts, m, n, k, Y, dev, st)
-             : fp4::launch_nv_decode<false, 1>(Xq, Xs, x_ts, Wq, Ws, w_ts, m, n, k, Y, dev, st);
+  const int m = (int)M, n = (int)N, k = (int)K, mf = (m + 15) / 16;
+  auto go = [&](auto bf16, auto t, auto f) {
+    return fp4::launch_nv_decode<decltype(bf16)::value, decltype(t)::value, decltype(f)::value>(
+        Xq, Xs, x_ts, Wq, Ws, w_ts, m, n, k, Y, dev, st);
+  };
+  auto with_mf = [&](auto bf16, auto t) {
+    switch (mf) {
+      case 1: return go(bf16, t, std::integral_constant<int, 1>{});
+      case 2: return go(bf16, t, std::integral_constant<int, 2>{});
+      case 3: return go(bf16, t, std::integral_constant<int, 3>{});
+      default: return go(bf16, t, std::integral_constant<int, 4>{});
+    }
+  };
+  auto with_t = [&](auto bf16) {
+    return two ? with_mf(bf16, std::integral_constant<int, 2>{}) : with_mf(bf16, std::integral_constant<int, 1>{});
+  };
+  return out_bf16 ? with_t(std::true_type{}) : with_t(std::false_type{});
 }

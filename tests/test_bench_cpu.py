@@ -71,6 +71,7 @@ def test_roofline_kernel_follows_the_library_dispatch():
             "decode_wide4": "gemm_mxfp4_decode", "decode_wide16": "gemm_mxfp4_decode",
             "decode_wide32": "gemm_mxfp4_decode", "decode_wide64": "gemm_mxfp4_decode",
             "decode_nv_wide1": "gemm_nvfp4_decode", "decode_nv_wide16": "gemm_nvfp4_decode",
+            "decode_nv_wide64": "gemm_nvfp4_decode",
             "prefill_nv": "gemm_nvfp4_ring", "prefill_mx": "gemm_mxfp4_ring", "prefill_mx_m4096": "gemm_mxfp4_ring",
             "large": "gemm_mxfp4_ring"}
     for name, w in WL.WORKLOADS.items():
@@ -86,7 +87,8 @@ def test_roofline_kernel_follows_the_library_dispatch():
     assert bench.gemm_kernel_for("mxfp4", 65, 4096, 4096)[1] == "gemm_mxfp4_kernel"   # neither
     assert bench.gemm_kernel_for("nvfp4", 16, 4096, 4096)[1] == "gemm_nvfp4_decode"
     assert bench.gemm_kernel_for("nvfp4", 16, 4096, 8704)[1] == "gemm_nvfp4_kernel"    # K past the slices
-    assert bench.gemm_kernel_for("nvfp4", 17, 4096, 4096)[1] == "gemm_nvfp4_kernel"
+    assert bench.gemm_kernel_for("nvfp4", 64, 4096, 4096)[1] == "gemm_nvfp4_decode"
+    assert bench.gemm_kernel_for("nvfp4", 65, 4096, 4096)[1] == "gemm_nvfp4_kernel"
     assert bench.gemm_kernel_for("nvfp4", 256, 256, 256)[1] == "gemm_nvfp4_ring"
     assert bench.gemm_kernel_for("nvfp4", 256, 256, 384)[1] == "gemm_nvfp4_kernel"    # K % 256 != 0
     assert bench.gemm_kernel_for("mxfp4", 16, 4096, 1 << 28)[1] == "gemm_mxfp4_kernel"  # K past the decode bound

@@ -241,13 +241,15 @@ def test_nv_large_tile_kernel_unit_scales_exact(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(1, 77, 512), (5, 300, 1536), (16, 4096, 4096), (3, 130, 8192), (16, 18, 2560),
                                    (9, 12300, 1024), (16, 12289, 4096), (8, 14336, 4096), (2, 33, 8192),
-                                   (4, 200, 9216), (16, 64, 640)])
+                                   (4, 200, 9216), (16, 64, 640), (17, 300, 512), (33, 12300, 1024),
+                                   (48, 777, 8192), (64, 12289, 4096), (64, 16, 2560), (65, 300, 1024)])
 def test_nv_decode_kernel_unit_scales_exact(M, N, K):
-    # NVFP4 with M <= 16, K % 512 == 0 and K <= 8192 runs the weight-streaming decode kernel: 8 waves
+    # NVFP4 with M <= 64, K % 512 == 0 and K <= 8192 runs the weight-streaming decode kernel: 8 waves
     # each dequantize their own 512-wide K slices of W (from LDS) and X (from L2) to fp16 (K = 8192:
     # two slices per wave; 512, 1536, 2560 leave waves idle); N >= 3 * 16 * 256 with K <= 4096 puts
-    # two 16-row tiles in a workgroup (12300, 12289: ragged last workgroup). K = 9216 and 640 take the
-    # general kernel. Unit group and tensor scales make every sum exact.
+    # two 16-row tiles in a workgroup (12300, 12289: ragged last workgroup); above 16 rows every W
+    # fragment meets ceil(M / 16) X fragments. K = 9216 and 640, and M = 65, take the general
+    # kernel. Unit group and tensor scales make every sum exact.
     rng = np.random.default_rng(7 * M + N + K)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
@@ -262,7 +264,8 @@ def test_nv_decode_kernel_unit_scales_exact(M, N, K):
     assert np.array_equal(host(yb.float()).astype(np.float64), O.bf16_rne_f64(ref))
 
 
-@pytest.mark.parametrize("M,N,K", [(7, 520, 3072), (16, 12300, 4096), (1, 300, 8192)])
+@pytest.mark.parametrize("M,N,K", [(7, 520, 3072), (16, 12300, 4096), (1, 300, 8192), (50, 1000, 2048),
+                                   (64, 12300, 4096)])
 def test_nv_decode_kernel_random_scales(M, N, K):
     rng = np.random.default_rng(13 * M + N)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
@@ -341,7 +344,7 @@ def test_ragged_shapes(fmt, block, M, N, K):
 
 
 @pytest.mark.parametrize("name", ["decode1", "decode4", "decode16", "decode_wide1", "decode_wide16", "decode_wide32",
-                                  "decode_wide64", "decode_nv_wide1", "decode_nv_wide16"])
+                                  "decode_wide64", "decode_nv_wide1", "decode_nv_wide16", "decode_nv_wide64"])
 def test_decode_full(name):
     w = WL.WORKLOADS[name]
     x, wt = WL.draw_x(w), WL.draw_w(w)
