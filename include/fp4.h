@@ -177,10 +177,9 @@ FP4_API int fp4_quantize_weights_ex(const void *W, int64_t N, int64_t K, int64_t
  *  MXFP4: dq = e2m1(code) * 2^(scale - 127); runs on gfx950 scaled MFMA with
  *         the E8M0 scales consumed by the instruction.
  *  NVFP4: dq = e2m1(code) * e4m3(scale) * s_t; the E4M3 group scale is folded
- *         into an exact 16-bit operand in the kernel prologue (fp16 in the
- *         256-row-tile kernel used when M, N >= 256, bf16 in the general one; E4M3
- *         scales have no native MFMA form on gfx950), x_ts * w_ts is applied in the
- *         epilogue. Scale codes are the finite non-negative E4M3FN codes
+ *         into an exact 16-bit operand before the products (fp16 in the 256-row-tile
+ *         and decode kernels, bf16 in the general one; E4M3 scales have no native
+ *         MFMA form on gfx950), x_ts * w_ts is applied to the sums. Scale codes are the finite non-negative E4M3FN codes
  *         0x00..0x7E that the quantizers write; other codes are outside the contract.
  *
  *  Xq  device uint8 [M, K/2], Xs device uint8 [M, K/g]  (fp4_rotate_quantize output)
@@ -188,10 +187,12 @@ FP4_API int fp4_quantize_weights_ex(const void *W, int64_t N, int64_t K, int64_t
  *  x_ts, w_ts  NVFP4: device float[1] tensor scales (4-byte aligned); MXFP4: must be NULL.
  *  M, N >= 1; K >= 128 and K % 128 == 0. M, N, K <= 2^31 - 1 and M * K / 2,
  *  N * K / 2 <= 2^40 bytes; larger shapes return FP4_E_SHAPE.
- *  Xq, Wq 16-byte aligned; Xs, Ws 4-byte aligned. (MXFP4 with 16-byte-aligned Xs and Ws
- *  and K % 512 == 0 runs the weight-streaming decode kernel for M <= 16, and for M <= 64
- *  when K <= 8192, and the 256-row-tile kernel for M, N >= 256; other pointers or shapes
- *  run the general kernel.)
+ *  Xq, Wq 16-byte aligned; Xs, Ws 4-byte aligned. (With 16-byte-aligned Xs and Ws: MXFP4
+ *  with K % 512 == 0 runs the weight-streaming decode kernel for M <= 16, and for M <= 64
+ *  when K <= 8192, and the 256-row-tile kernel for M, N >= 256; NVFP4 runs the decode
+ *  kernel for M <= 64 when K % 512 == 0 and K <= 8192, and the 256-row-tile kernel for
+ *  M, N >= 256 when K % 256 == 0. Other pointers or shapes run the general kernel, on
+ *  64 x 64 tiles when its 128 x 128 grid would be small.)
  *  Y   device [M, N] row-major, float32 (FP4_OUT_F32) or bf16 (FP4_OUT_BF16,
  *      round-to-nearest-even); 16-byte aligned.
  * No bias, no activation. One kernel launch on `stream`.
