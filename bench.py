@@ -76,11 +76,15 @@ def gemm_kernel_for(fmt: str, M: int, N: int, K: int):
             return "gemm_decode.hip", "gemm_mxfp4_decode"
         if K % 512 == 0 and K < (1 << 25) and M >= 256 and N >= 256:
             return "gemm_mxfp4_ring.hip", "gemm_mxfp4_ring"
+        if K % 512 == 0 and K < (1 << 25) and M > 64 and N >= 1024:
+            return "gemm_mxfp4_ring.hip", "gemm_mxfp4_ring_skinny"
         return "gemm_mxfp4.hip", "gemm_mxfp4_kernel"
     if M <= 64 and K % 512 == 0 and K <= 8192:
         return "gemm_decode.hip", "gemm_nvfp4_decode"
     if K % 256 == 0 and K < (1 << 25) and M >= 256 and N >= 256:
         return "gemm_nvfp4_ring.hip", "gemm_nvfp4_ring"
+    if K % 256 == 0 and K < (1 << 25) and M > 64 and N >= 1024:
+        return "gemm_nvfp4_ring.hip", "gemm_nvfp4_ring_skinny"
     return "gemm_nvfp4.hip", "gemm_nvfp4_kernel"
 
 
@@ -421,16 +425,28 @@ def extra_rows(B, WL, torch, dev, groups=EXTRA_ROWS):
     return out
 
 
-# traffic-table key of each decode row's kernel (the launch configuration differs with N and M)
-DECODE_TRAFFIC_KEY = {"decode_wide1": "gemm_mxfp4_decode@decode_wide", "decode_wide4": "gemm_mxfp4_decode@decode_wide",
-                      "decode_wide16": "gemm_mxfp4_decode@decode_wide", "decode_wide32": "gemm_mxfp4_decode@decode_wide32",
-                      "decode_wide64": "gemm_mxfp4_decode@decode_wide64"}
+# traffic-table key and kernel source of each decode row (the kernel and its launch differ with N and M)
+DECODE_TRAFFIC_KEY = {
+    "decode1": ("gemm_mxfp4_decode@decode", "gemm_decode.hip"),
+    "decode4": ("gemm_mxfp4_decode@decode", "gemm_decode.hip"),
+    "decode16": ("gemm_mxfp4_decode@decode", "gemm_decode.hip"),
+    "decode_wide1": ("gemm_mxfp4_decode@decode_wide", "gemm_decode.hip"),
+    "decode_wide4": ("gemm_mxfp4_decode@decode_wide", "gemm_decode.hip"),
+    "decode_wide16": ("gemm_mxfp4_decode@decode_wide", "gemm_decode.hip"),
+    "decode_wide32": ("gemm_mxfp4_decode@decode_wide32", "gemm_decode.hip"),
+    "decode_wide64": ("gemm_mxfp4_decode@decode_wide64", "gemm_decode.hip"),
+    "decode_wide128": ("gemm_mxfp4_ring_skinny@decode_wide128", "gemm_mxfp4_ring.hip"),
+    "decode_nv_wide1": ("gemm_nvfp4_decode@decode_nv_wide", "gemm_decode.hip"),
+    "decode_nv_wide16": ("gemm_nvfp4_decode@decode_nv_wide", "gemm_decode.hip"),
+    "decode_nv_wide64": ("gemm_nvfp4_decode@decode_nv_wide64", "gemm_decode.hip"),
+    "decode_nv_wide128": ("gemm_nvfp4_ring_skinny@decode_nv_wide128", "gemm_nvfp4_ring.hip"),
+}
 
 
 def decode_rows(B, WL, torch, dev, names=("decode1", "decode4", "decode16", "decode_wide1", "decode_wide4",
-                                            "decode_wide16", "decode_wide32", "decode_wide64")):
+                                            "decode_wide16", "decode_wide32", "decode_wide64", "decode_wide128")):
     """Decode-shaped MXFP4 layers (M in {1, 4, 16} tokens, K=4096; W 4096x4096 or 14336x4096; and
-    batches of 32 and 64 tokens against the wide W), bound by reading W from HBM. Each row is timed as a HIP graph of calls that cycle over copies of
+    batches of 32, 64 and 128 tokens against the wide W), bound by reading W from HBM. Each row is timed as a HIP graph of calls that cycle over copies of
     W totalling more than 512 MB, so that no call finds its W in the 256 MB Infinity Cache (as in a
     model whose weights do not fit in it); the graph's result is checked against an eager call. The
     same call with one W, resident in the cache, is reported as warm_us. The whole decode step from
@@ -467,8 +483,7 @@ def decode_rows(B, WL, torch, dev, names=("decode1", "decode4", "decode16", "dec
                "w_copies": n_sets, "graph_replay_matches_eager": graph_ok,
                "warm_us": ms_warm * 1e3, "warm_GB/s": nbytes / (ms_warm * 1e-3) / 1e9,
                "us_per_python_call": ms_call * 1e3,
-               "traffic": measured_traffic(DECODE_TRAFFIC_KEY.get(name, "gemm_mxfp4_decode@decode"),
-                                          "gemm_decode.hip"),
+               "traffic": measured_traffic(*DECODE_TRAFFIC_KEY[name]),
                "note": f"{calls} calls in one HIP graph over {n_sets} copies of W ({n_sets * wbytes / 1e6:.0f} MB), "
                        "so W comes from HBM; warm_us: one W, resident in the Infinity Cache"}
         log(f"[bench] {name} GEMM {ms * 1e3:.2f} us with W from HBM = {row['GB/s']:.0f} GB/s "
@@ -505,8 +520,9 @@ def decode_rows(B, WL, torch, dev, names=("decode1", "decode4", "decode16", "dec
     return out
 
 
-def nv_decode_rows(B, WL, torch, dev, names=("decode_nv_wide1", "decode_nv_wide16", "decode_nv_wide64")):
-    """NVFP4 decode-shaped layers (1, 16 and 64 tokens, K=4096, W 14336x4096, block 16), timed as
+def nv_decode_rows(B, WL, torch, dev, names=("decode_nv_wide1", "decode_nv_wide16", "decode_nv_wide64",
+                                               "decode_nv_wide128")):
+    """NVFP4 decode-shaped layers (1, 16, 64 and 128 tokens, K=4096, W 14336x4096, block 16), timed as
     decode_rows times the MXFP4 ones: a HIP graph of calls over copies of W totalling more than
     512 MB (W from HBM), and warm_us with one W resident in the Infinity Cache."""
     import math
@@ -538,8 +554,7 @@ def nv_decode_rows(B, WL, torch, dev, names=("decode_nv_wide1", "decode_nv_wide1
             "us": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes": nbytes, "w_copies": n_sets, "graph_replay_matches_eager": graph_ok,
             "warm_us": ms_warm * 1e3,
-            "traffic": measured_traffic("gemm_nvfp4_decode@decode_nv_wide" + ("64" if wl.M > 16 else ""),
-                                        "gemm_decode.hip"),
+            "traffic": measured_traffic(*DECODE_TRAFFIC_KEY[name]),
             "note": f"{calls} calls in one HIP graph over {n_sets} copies of W ({n_sets * wbytes / 1e6:.0f} MB), "
                     "so W comes from HBM; warm_us: one W, resident in the Infinity Cache"}
         log(f"[bench] {name} NVFP4 GEMM {ms * 1e3:.2f} us with W from HBM = {nbytes / (ms * 1e-3) / 1e9:.0f} GB/s; "

@@ -76,6 +76,7 @@ struct Tile {
 };
 using Wide = Tile<256, 2, 4>;
 using Narrow = Tile<192, 4, 2>;
+using Skinny = Tile<64, 8, 1>;  // 65-255 rows: 256 x 64 tiles, 8 waves of 32 x 64
 constexpr float kNvNarrowCost = 0.84f;  // measured time of a 256x192 tile over a 256x256 one
 
 template <int N>
@@ -374,6 +375,23 @@ __global__ __launch_bounds__(NT) void gemm_nvfp4_ring(const uint8_t* __restrict_
   }
 }
 
+// One 256 x 64 tile per workgroup, tile index b -> (tm, tn) M-fastest; for fewer than 256 rows of X.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(NT) void gemm_nvfp4_ring_skinny(const uint8_t* __restrict__ Xq,
+                                                             const uint8_t* __restrict__ Xs,
+                                                             const float* __restrict__ x_ts,
+                                                             const uint8_t* __restrict__ Wq,
+                                                             const uint8_t* __restrict__ Ws,
+                                                             const float* __restrict__ w_ts, void* __restrict__ Yv,
+                                                             int M, int N, int K, int tiles_m) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int b = blockIdx.x, tm = b % tiles_m, tn = b / tiles_m;
+  nv_tile<OUT_BF16, Skinny>(smem, Xq, Xs, x_ts, Wq, Ws, w_ts, Yv, M, N, K, tm * BM, tn * Skinny::BN);
+}
+
+template <bool B>
+std::atomic<int> g_skinny_attr[64];
+
 // per kernel instantiation and device: the dynamic-LDS limit has been raised
 template <bool B>
 std::atomic<int> g_attr_done[64];
@@ -399,6 +417,18 @@ hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const
     if (cached) g_cus[dev].store(cus, std::memory_order_release);
   }
   const int tiles_m = (M + BM - 1) / BM;
+  if (M < BM) {
+    auto sk = gemm_nvfp4_ring_skinny<B>;
+    if (!cached || !g_skinny_attr<B>[dev].load(std::memory_order_acquire)) {
+      e = hipFuncSetAttribute((const void*)sk, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+      if (e != hipSuccess) return e;
+      if (cached) g_skinny_attr<B>[dev].store(1, std::memory_order_release);
+    }
+    const int tiles_n = (N + Skinny::BN - 1) / Skinny::BN;
+    hipLaunchKernelGGL(sk, dim3(tiles_m * tiles_n), dim3(NT), LDS_BYTES, st, Xq, Xs, x_ts, Wq, Ws, w_ts, Y, M, N, K,
+                       tiles_m);
+    return hipGetLastError();
+  }
   int tn1, tn2;
   fp4_plan_tile_columns(tiles_m, N, cus, kNvNarrowCost, tn1, tn2);
   hipLaunchKernelGGL(kern, dim3(tiles_m * (tn1 + tn2)), dim3(NT), LDS_BYTES, st, Xq, Xs, x_ts, Wq, Ws, w_ts, Y, M, N,
@@ -410,7 +440,7 @@ hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const
 }  // namespace fp4
 
 bool fp4_gemm_nvfp4_ring_fits(int64_t M, int64_t N, int64_t K) {
-  return K % 256 == 0 && K < ((int64_t)1 << 25) && M >= 256 && N >= 256;
+  return K % 256 == 0 && K < ((int64_t)1 << 25) && ((M >= 256 && N >= 256) || (M > 64 && N >= 1024));
 }
 
 hipError_t fp4_launch_gemm_nvfp4_ring(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const uint8_t* Wq,

@@ -19,9 +19,9 @@ name       X (bf16)                                                     W
 =========  ==========================================================  =====
 tiny       16x256 N(0,1), 4 outlier channels x50                        256x256 N(0,0.02)
 decode     M in {1,4,16} x 4096, Student-t(5), 1% channels x30           4096x4096 N(0,0.02)
-           (decode_wide: the same X against W 14336x4096; decode_wide32/64: 32 and
-           64 rows, a batch of sequences decoding together; decode_nv_wide1/16/64: NVFP4
-           block 16 against W 14336x4096)
+           (decode_wide: the same X against W 14336x4096; decode_wide32/64/128: 32, 64
+           and 128 rows, a batch of sequences decoding together; decode_nv_wide1/16/64/128:
+           NVFP4 block 16 against W 14336x4096)
 prefill    2048x4096, Student-t(5), 1% channels x30                      14336x4096 N(0,0.02)
            (NVFP4 block 16 as stated; also run in MXFP4 block 32, Y bf16)
 large      8192x8192 N(0,1), 0.5% channels x100                          28672x8192 N(0,0.02)
@@ -101,9 +101,11 @@ WORKLOADS = {
     "decode_wide16": Workload("decode_wide16", 8, 16, 4096, 14336, 32, "mxfp4", "t5", 0.01, 30.0),
     "decode_wide32": Workload("decode_wide32", 8, 32, 4096, 14336, 32, "mxfp4", "t5", 0.01, 30.0),
     "decode_wide64": Workload("decode_wide64", 8, 64, 4096, 14336, 32, "mxfp4", "t5", 0.01, 30.0),
+    "decode_wide128": Workload("decode_wide128", 8, 128, 4096, 14336, 32, "mxfp4", "t5", 0.01, 30.0),
     "decode_nv_wide1": Workload("decode_nv_wide1", 8, 1, 4096, 14336, 16, "nvfp4", "t5", 0.01, 30.0),
     "decode_nv_wide16": Workload("decode_nv_wide16", 8, 16, 4096, 14336, 16, "nvfp4", "t5", 0.01, 30.0),
     "decode_nv_wide64": Workload("decode_nv_wide64", 8, 64, 4096, 14336, 16, "nvfp4", "t5", 0.01, 30.0),
+    "decode_nv_wide128": Workload("decode_nv_wide128", 8, 128, 4096, 14336, 16, "nvfp4", "t5", 0.01, 30.0),
     "large": Workload("large", 4, 8192, 8192, 28672, 128, "mxfp4", "normal", 0.005, 100.0),
     "stress_mx32": Workload("stress_mx32", 5, 16384, 8192, 0, 32, "mxfp4", "t3_lognormal", 0, 1.0),
     "stress_mx128": Workload("stress_mx128", 5, 16384, 8192, 0, 128, "mxfp4", "t3_lognormal", 0, 1.0),

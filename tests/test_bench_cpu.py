@@ -58,6 +58,10 @@ def test_bench_traffic_lookups_are_in_the_map():
     assert set(lits) <= keys, set(lits) - keys
     assert {"gemm_mxfp4_ring@prefill_mx", "rotate_quant_mx@stress_mx32", "gemm_mxfp4_decode@decode",
             "gemm_mxfp4_decode@decode_wide"} <= keys
+    # the decode rows' table: every key measured, on the source it names
+    srcs = {k: src for _, _, k, src, _ in bench_profiles.TRAFFIC_MAP}
+    for name, (key, src) in bench.DECODE_TRAFFIC_KEY.items():
+        assert srcs.get(key) == src, (name, key, src)
 
 
 def test_roofline_kernel_follows_the_library_dispatch():
@@ -71,7 +75,8 @@ def test_roofline_kernel_follows_the_library_dispatch():
             "decode_wide4": "gemm_mxfp4_decode", "decode_wide16": "gemm_mxfp4_decode",
             "decode_wide32": "gemm_mxfp4_decode", "decode_wide64": "gemm_mxfp4_decode",
             "decode_nv_wide1": "gemm_nvfp4_decode", "decode_nv_wide16": "gemm_nvfp4_decode",
-            "decode_nv_wide64": "gemm_nvfp4_decode",
+            "decode_nv_wide64": "gemm_nvfp4_decode", "decode_wide128": "gemm_mxfp4_ring_skinny",
+            "decode_nv_wide128": "gemm_nvfp4_ring_skinny",
             "prefill_nv": "gemm_nvfp4_ring", "prefill_mx": "gemm_mxfp4_ring", "prefill_mx_m4096": "gemm_mxfp4_ring",
             "large": "gemm_mxfp4_ring"}
     for name, w in WL.WORKLOADS.items():
@@ -84,11 +89,13 @@ def test_roofline_kernel_follows_the_library_dispatch():
     assert bench.gemm_kernel_for("mxfp4", 17, 4096, 4096)[1] == "gemm_mxfp4_decode"   # up to 64 tokens
     assert bench.gemm_kernel_for("mxfp4", 64, 4096, 8192)[1] == "gemm_mxfp4_decode"
     assert bench.gemm_kernel_for("mxfp4", 64, 4096, 8704)[1] == "gemm_mxfp4_kernel"   # K past the slices
-    assert bench.gemm_kernel_for("mxfp4", 65, 4096, 4096)[1] == "gemm_mxfp4_kernel"   # neither
+    assert bench.gemm_kernel_for("mxfp4", 65, 4096, 4096)[1] == "gemm_mxfp4_ring_skinny"  # 256 x 64 tiles
+    assert bench.gemm_kernel_for("mxfp4", 65, 1000, 4096)[1] == "gemm_mxfp4_kernel"   # too few columns
+    assert bench.gemm_kernel_for("nvfp4", 100, 2048, 768)[1] == "gemm_nvfp4_ring_skinny"
     assert bench.gemm_kernel_for("nvfp4", 16, 4096, 4096)[1] == "gemm_nvfp4_decode"
     assert bench.gemm_kernel_for("nvfp4", 16, 4096, 8704)[1] == "gemm_nvfp4_kernel"    # K past the slices
     assert bench.gemm_kernel_for("nvfp4", 64, 4096, 4096)[1] == "gemm_nvfp4_decode"
-    assert bench.gemm_kernel_for("nvfp4", 65, 4096, 4096)[1] == "gemm_nvfp4_kernel"
+    assert bench.gemm_kernel_for("nvfp4", 65, 1000, 4096)[1] == "gemm_nvfp4_kernel"
     assert bench.gemm_kernel_for("nvfp4", 256, 256, 256)[1] == "gemm_nvfp4_ring"
     assert bench.gemm_kernel_for("nvfp4", 256, 256, 384)[1] == "gemm_nvfp4_kernel"    # K % 256 != 0
     assert bench.gemm_kernel_for("mxfp4", 16, 4096, 1 << 28)[1] == "gemm_mxfp4_kernel"  # K past the decode bound

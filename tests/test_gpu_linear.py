@@ -109,6 +109,52 @@ def test_decode_kernel_up_to_64_tokens_random_scales(M, N, K):
     assert r <= 1e-6
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("M,N,K", [(65, 1024, 512), (100, 1100, 1536), (200, 3000, 4096), (255, 14336, 1024),
+                                   (129, 1030, 8192)])
+def test_skinny_tiles_unit_scales_exact(fmt, M, N, K):
+    # 64 < M < 256 with N >= 1024 (and K % 512 == 0 for MXFP4, K % 256 == 0 for NVFP4) runs the
+    # large-tile kernels on 256 x 64 tiles, one row tile whose rows past M repeat row M - 1 (N = 1100,
+    # 3000, 1030: a ragged last column tile). Unit scales make every sum exact.
+    rng = np.random.default_rng(3 * M + N + K)
+    c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    g, one = (32, 127) if fmt == "mxfp4" else (16, 0x38)
+    xs = np.full((M, K // g), one, np.uint8)
+    ws = np.full((N, K // g), one, np.uint8)
+    ts = {} if fmt == "mxfp4" else {"x_ts": dev_f32(1.0), "w_ts": dev_f32(1.0)}
+    ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, fmt, *(() if fmt == "mxfp4" else (1.0, 1.0)))
+    say(f"case skinny-tile unit-scale exact {fmt} M {M} N {N} K {K}")
+    args = (dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), fmt)
+    y = B.fp4_linear(*args, **ts)
+    assert np.array_equal(host(y).astype(np.float64), ref)
+    yb = B.fp4_linear(*args, **ts, out_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.float()).astype(np.float64), O.bf16_rne_f64(ref))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_skinny_tiles_random_scales(fmt):
+    M, N, K = 150, 2100, 2048
+    rng = np.random.default_rng(21 if fmt == "mxfp4" else 22)
+    c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    if fmt == "mxfp4":
+        xs = rng.integers(110, 140, size=(M, K // 32)).astype(np.uint8)
+        ws = rng.integers(110, 140, size=(N, K // 32)).astype(np.uint8)
+        ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "mxfp4")
+        ts = {}
+    else:
+        xs = rng.integers(0, 0x7F, size=(M, K // 16)).astype(np.uint8)
+        ws = rng.integers(0, 0x7F, size=(N, K // 16)).astype(np.uint8)
+        ref = O.linear_f64(O.pack_nibbles(c), xs, O.pack_nibbles(d), ws, "nvfp4", np.float32(0.0123), np.float32(3.5e-3))
+        ts = {"x_ts": dev_f32(0.0123), "w_ts": dev_f32(3.5e-3)}
+    say(f"case skinny-tile random scales {fmt} M {M} N {N} K {K}")
+    y = B.fp4_linear(dev_u8(O.pack_nibbles(c)), dev_u8(xs), dev_u8(O.pack_nibbles(d)), dev_u8(ws), fmt, **ts)
+    r = rel_fro(host(y), ref)
+    say(f"rel fro {r:.3e}")
+    assert r <= 1e-6
+
+
 def test_decode_kernel_random_scales():
     rng = np.random.default_rng(99)
     M, N, K = 7, 520, 3072
@@ -344,7 +390,8 @@ def test_ragged_shapes(fmt, block, M, N, K):
 
 
 @pytest.mark.parametrize("name", ["decode1", "decode4", "decode16", "decode_wide1", "decode_wide16", "decode_wide32",
-                                  "decode_wide64", "decode_nv_wide1", "decode_nv_wide16", "decode_nv_wide64"])
+                                  "decode_wide64", "decode_wide128", "decode_nv_wide1", "decode_nv_wide16",
+                                  "decode_nv_wide64", "decode_nv_wide128"])
 def test_decode_full(name):
     w = WL.WORKLOADS[name]
     x, wt = WL.draw_x(w), WL.draw_w(w)
