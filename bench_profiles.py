@@ -55,10 +55,10 @@ TRAFFIC_MAP = [
      "decode_wide32 M=32 K=4096 N=14336 fp32 Y, two 16-row tiles and two X fragments per workgroup, W from HBM"),
     ("gemm_mxfp4_decode<false, 2, 4>", 229376, "gemm_mxfp4_decode@decode_wide64", "gemm_decode.hip",
      "decode_wide64 M=64 K=4096 N=14336 fp32 Y, two 16-row tiles and four X fragments per workgroup, W from HBM"),
-    ("gemm_mxfp4_ring_skinny<false>", 114688, "gemm_mxfp4_ring_skinny@decode_wide128", "gemm_mxfp4_ring.hip",
-     "decode_wide128 M=128 K=4096 N=14336 fp32 Y, 256x64 tiles, W from HBM"),
-    ("gemm_nvfp4_ring_skinny<false>", 114688, "gemm_nvfp4_ring_skinny@decode_nv_wide128", "gemm_nvfp4_ring.hip",
-     "decode_nv_wide128 M=128 K=4096 N=14336 NVFP4 block 16 fp32 Y, 256x64 tiles, W from HBM"),
+    ("gemm_mxfp4_ring_skinny<false, Tile<64, 4, 2, 128>>", 114688, "gemm_mxfp4_ring_skinny@decode_wide128",
+     "gemm_mxfp4_ring.hip", "decode_wide128 M=128 K=4096 N=14336 fp32 Y, 128x64 tiles, W from HBM"),
+    ("gemm_nvfp4_ring_skinny<false, Tile<64, 4, 2, 128>>", 114688, "gemm_nvfp4_ring_skinny@decode_nv_wide128",
+     "gemm_nvfp4_ring.hip", "decode_nv_wide128 M=128 K=4096 N=14336 NVFP4 block 16 fp32 Y, 128x64 tiles, W from HBM"),
     ("gemm_nvfp4_decode<false, 2, 1>", 229376, "gemm_nvfp4_decode@decode_nv_wide", "gemm_decode.hip",
      "decode_nv_wide M in {1,16} K=4096 N=14336 NVFP4 block 16 fp32 Y, two 16-row tiles per workgroup, W from HBM"),
     ("gemm_nvfp4_decode<false, 2, 4>", 229376, "gemm_nvfp4_decode@decode_nv_wide64", "gemm_decode.hip",
@@ -123,7 +123,7 @@ def _grid(r):
 
 def _name(r):
     n = r["Kernel_Name"].replace("void ", "").replace("fp4::(anonymous namespace)::", "")
-    return n.split("(")[0].strip()
+    return n.split("(")[0].strip().replace("> >", ">>")
 
 
 def counter_means(d, counter):

@@ -36,6 +36,8 @@
 //    workgroups part-filled, the columns left after whole rounds of 256-wide tiles are
 //    covered by 256x192 tiles (4 x 2 waves of 64 x 96), each about 0.78 of a wide tile's
 //    time, so the last round is full of cheaper tiles.
+//  * Fewer than 256 rows of X (and N >= 1024): one row tile of 64-column tiles (128 x 64 up to
+//    128 rows, 256 x 64 above), so that enough workgroups stream W; rows past M repeat row M-1.
 // Requires K % 512 == 0 (whole scale groups) and K < 2^25 (32-bit buffer offsets); other
 // shapes use the general kernel.
 #include <atomic>
@@ -56,10 +58,10 @@ constexpr int KSTEPS = 4;                // 32x32x64 steps per stage
 constexpr int NS = 2;                    // ring depth
 constexpr int LDS_BYTES = NS * (BM + 256) * BKB + 2 * (BM + 256) * 16;  // sized for the wide tile: 144 KB
 
-// One tile shape: BN columns, WGM x WGN waves.
-template <int BN_, int WGM_, int WGN_>
+// One tile shape: BM_ rows, BN columns, WGM x WGN waves.
+template <int BN_, int WGM_, int WGN_, int BM_ = BM>
 struct Tile {
-  static constexpr int BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
   static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
   static constexpr int STAGE = (BM + BN) * BKB;
   static constexpr int A_WL = BM / 8 / WAVES, B_WL = BN / 8 / WAVES;  // 1 KB DMA wave-loads per wave
@@ -76,7 +78,12 @@ struct Tile {
 };
 using Wide = Tile<256, 2, 4>;
 using Narrow = Tile<192, 4, 2>;
-using Skinny = Tile<64, 8, 1>;  // 65-255 rows: 256 x 64 tiles, 8 waves of 32 x 64
+using Skinny = Tile<64, 8, 1>;  // 129-255 rows: 256 x 64 tiles, 8 waves of 32 x 64
+using Skinny128 = Tile<64, 4, 2, 128>;  // 65-128 rows: 128 x 64 tiles, 8 waves of 32 x 32
+template <class C>
+constexpr int lds_need() {  // the ring and scale buffers, or the epilogue staging if larger
+  return NS * C::STAGE + 2 * C::SC_BYTES > WAVES * 32 * C::EP ? NS * C::STAGE + 2 * C::SC_BYTES : WAVES * 32 * C::EP;
+}
 constexpr float kNarrowCost = 0.78f;  // measured time of a 256x192 tile over a 256x256 one (MXFP4)
 
 template <int N>
@@ -117,6 +124,7 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
                                           const uint8_t* __restrict__ Xs, const uint8_t* __restrict__ Wq,
                                           const uint8_t* __restrict__ Ws, void* __restrict__ Yv, int M, int N,
                                           int K, int m0, int n0) {
+  constexpr int BM = C::BM;
   constexpr int WGN = C::WGN, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
   constexpr int STAGE = C::STAGE, A_WL = C::A_WL, B_WL = C::B_WL, SC_BYTES = C::SC_BYTES, SC_WL = C::SC_WL;
   // LDS: the A rows of both stages, then the B rows of both stages, then the scale buffers,
@@ -347,8 +355,8 @@ __global__ __launch_bounds__(NT) void gemm_mxfp4_ring(const uint8_t* __restrict_
   }
 }
 
-// One 256 x 64 tile per workgroup, tile index b -> (tm, tn) M-fastest; for fewer than 256 rows of X.
-template <bool OUT_BF16>
+// One C::BM x 64 tile per workgroup, tile index b -> (tm, tn) M-fastest; for fewer than 256 rows of X.
+template <bool OUT_BF16, class C>
 __global__ __launch_bounds__(NT) void gemm_mxfp4_ring_skinny(const uint8_t* __restrict__ Xq,
                                                              const uint8_t* __restrict__ Xs,
                                                              const uint8_t* __restrict__ Wq,
@@ -356,11 +364,26 @@ __global__ __launch_bounds__(NT) void gemm_mxfp4_ring_skinny(const uint8_t* __re
                                                              int M, int N, int K, int tiles_m) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int b = blockIdx.x, tm = b % tiles_m, tn = b / tiles_m;
-  ring_tile<OUT_BF16, Skinny>(smem, Xq, Xs, Wq, Ws, Yv, M, N, K, tm * BM, tn * Skinny::BN);
+  ring_tile<OUT_BF16, C>(smem, Xq, Xs, Wq, Ws, Yv, M, N, K, tm * C::BM, tn * C::BN);
 }
 
 template <bool B>
-std::atomic<int> g_skinny_attr[64];
+std::atomic<int> g_skinny_attr[2][64];
+
+template <bool B, class C>
+hipError_t launch_skinny(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws, int M, int N,
+                         int K, void* Y, int dev, int slot, hipStream_t st) {
+  auto sk = gemm_mxfp4_ring_skinny<B, C>;
+  const bool cached = dev >= 0 && dev < 64;
+  if (!cached || !g_skinny_attr<B>[slot][dev].load(std::memory_order_acquire)) {
+    const hipError_t e = hipFuncSetAttribute((const void*)sk, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    if (cached) g_skinny_attr<B>[slot][dev].store(1, std::memory_order_release);
+  }
+  const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
+  hipLaunchKernelGGL(sk, dim3(tiles_m * tiles_n), dim3(NT), lds_need<C>(), st, Xq, Xs, Wq, Ws, Y, M, N, K, tiles_m);
+  return hipGetLastError();
+}
 
 // per kernel instantiation and device: the dynamic-LDS limit has been raised
 template <bool B>
@@ -387,17 +410,8 @@ hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const
     if (cached) g_cus[dev].store(cus, std::memory_order_release);
   }
   const int tiles_m = (M + BM - 1) / BM;
-  if (M < BM) {
-    auto sk = gemm_mxfp4_ring_skinny<B>;
-    if (!cached || !g_skinny_attr<B>[dev].load(std::memory_order_acquire)) {
-      e = hipFuncSetAttribute((const void*)sk, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-      if (e != hipSuccess) return e;
-      if (cached) g_skinny_attr<B>[dev].store(1, std::memory_order_release);
-    }
-    const int tiles_n = (N + Skinny::BN - 1) / Skinny::BN;
-    hipLaunchKernelGGL(sk, dim3(tiles_m * tiles_n), dim3(NT), LDS_BYTES, st, Xq, Xs, Wq, Ws, Y, M, N, K, tiles_m);
-    return hipGetLastError();
-  }
+  if (M <= 128) return launch_skinny<B, Skinny128>(Xq, Xs, Wq, Ws, M, N, K, Y, dev, 1, st);
+  if (M < BM) return launch_skinny<B, Skinny>(Xq, Xs, Wq, Ws, M, N, K, Y, dev, 0, st);
   int tn1, tn2;
   fp4_plan_tile_columns(tiles_m, N, cus, kNarrowCost, tn1, tn2);
   hipLaunchKernelGGL(kern, dim3(tiles_m * (tn1 + tn2)), dim3(NT), LDS_BYTES, st, Xq, Xs, Wq, Ws, Y, M, N, K, tiles_m,

@@ -110,12 +110,13 @@ def test_decode_kernel_up_to_64_tokens_random_scales(M, N, K):
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
-@pytest.mark.parametrize("M,N,K", [(65, 1024, 512), (100, 1100, 1536), (200, 3000, 4096), (255, 14336, 1024),
-                                   (129, 1030, 8192)])
+@pytest.mark.parametrize("M,N,K", [(65, 1024, 512), (100, 1100, 1536), (128, 2048, 512), (200, 3000, 4096),
+                                   (255, 14336, 1024), (129, 1030, 8192)])
 def test_skinny_tiles_unit_scales_exact(fmt, M, N, K):
     # 64 < M < 256 with N >= 1024 (and K % 512 == 0 for MXFP4, K % 256 == 0 for NVFP4) runs the
-    # large-tile kernels on 256 x 64 tiles, one row tile whose rows past M repeat row M - 1 (N = 1100,
-    # 3000, 1030: a ragged last column tile). Unit scales make every sum exact.
+    # large-tile kernels on one row tile of 64-column tiles, 128 rows up to M = 128 and 256 above,
+    # whose rows past M repeat row M - 1 (N = 1100, 3000, 1030: a ragged last column tile). Unit
+    # scales make every sum exact.
     rng = np.random.default_rng(3 * M + N + K)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
