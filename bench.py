@@ -72,12 +72,12 @@ def gemm_kernel_for(fmt: str, M: int, N: int, K: int):
     buffers are 16-byte aligned (torch's allocations are): the library's dispatch predicates, in
     its order."""
     if fmt == "mxfp4":
-        if K % 512 == 0 and (K < (1 << 28) if M <= 16 else (M <= 64 and K <= 8192)):
+        ring = K % 512 == 0 and K < (1 << 25) and ((M >= 256 and N >= 256) or (M > 64 and N >= 1024) or
+                                                   (M > 32 and N >= 8192))
+        if not (ring and M > 32) and K % 512 == 0 and (K < (1 << 28) if M <= 16 else (M <= 64 and K <= 8192)):
             return "gemm_decode.hip", "gemm_mxfp4_decode"
-        if K % 512 == 0 and K < (1 << 25) and M >= 256 and N >= 256:
-            return "gemm_mxfp4_ring.hip", "gemm_mxfp4_ring"
-        if K % 512 == 0 and K < (1 << 25) and M > 64 and N >= 1024:
-            return "gemm_mxfp4_ring.hip", "gemm_mxfp4_ring_skinny"
+        if ring:
+            return ("gemm_mxfp4_ring.hip", "gemm_mxfp4_ring" if M >= 256 else "gemm_mxfp4_ring_skinny")
         return "gemm_mxfp4.hip", "gemm_mxfp4_kernel"
     if M <= 64 and K % 512 == 0 and K <= 8192:
         return "gemm_decode.hip", "gemm_nvfp4_decode"
@@ -434,7 +434,7 @@ DECODE_TRAFFIC_KEY = {
     "decode_wide4": ("gemm_mxfp4_decode@decode_wide", "gemm_decode.hip"),
     "decode_wide16": ("gemm_mxfp4_decode@decode_wide", "gemm_decode.hip"),
     "decode_wide32": ("gemm_mxfp4_decode@decode_wide32", "gemm_decode.hip"),
-    "decode_wide64": ("gemm_mxfp4_decode@decode_wide64", "gemm_decode.hip"),
+    "decode_wide64": ("gemm_mxfp4_ring_skinny@decode_wide64", "gemm_mxfp4_ring.hip"),
     "decode_wide128": ("gemm_mxfp4_ring_skinny@decode_wide128", "gemm_mxfp4_ring.hip"),
     "decode_nv_wide1": ("gemm_nvfp4_decode@decode_nv_wide", "gemm_decode.hip"),
     "decode_nv_wide16": ("gemm_nvfp4_decode@decode_nv_wide", "gemm_decode.hip"),

@@ -37,7 +37,9 @@ SQ_PASSES = {
 }
 
 # (kernel name as rocprofv3 prints it, grid in work-items on the 256-CU MI355X, traffic key, source,
-#  workload) for every kernel launch the default bench run reports HBM traffic for
+#  workload[, (run, runs)]) for every kernel launch the default bench run reports HBM traffic for. With
+# (run, runs), the launches of that kernel and grid come from `runs` bench rows, one after the other,
+# and the entry takes row number `run` of them (split_runs).
 TRAFFIC_MAP = [
     ("gemm_mxfp4_ring<true>", 262144, "gemm_mxfp4_ring@prefill_mx", "gemm_mxfp4_ring.hip",
      "prefill_mx M=2048 K=4096 N=14336 bf16 Y"),
@@ -53,11 +55,12 @@ TRAFFIC_MAP = [
      "decode_wide M in {1,4,16} K=4096 N=14336 fp32 Y, two 16-row tiles per workgroup, W from HBM"),
     ("gemm_mxfp4_decode<false, 2, 2>", 229376, "gemm_mxfp4_decode@decode_wide32", "gemm_decode.hip",
      "decode_wide32 M=32 K=4096 N=14336 fp32 Y, two 16-row tiles and two X fragments per workgroup, W from HBM"),
-    ("gemm_mxfp4_decode<false, 2, 4>", 229376, "gemm_mxfp4_decode@decode_wide64", "gemm_decode.hip",
-     "decode_wide64 M=64 K=4096 N=14336 fp32 Y, two 16-row tiles and four X fragments per workgroup, W from HBM"),
-    ("gemm_mxfp4_ring_skinny<false, Tile<64, 4, 2, 128>>", 114688, "gemm_mxfp4_ring_skinny@decode_wide128",
-     "gemm_mxfp4_ring.hip", "decode_wide128 M=128 K=4096 N=14336 fp32 Y, 128x64 tiles, W from HBM"),
-    ("gemm_nvfp4_ring_skinny<false, Tile<64, 4, 2, 128>>", 114688, "gemm_nvfp4_ring_skinny@decode_nv_wide128",
+    ("gemm_mxfp4_ring_skinny<false, Tile<64, 4, 2, 128, 3>>", 114688, "gemm_mxfp4_ring_skinny@decode_wide64",
+     "gemm_mxfp4_ring.hip", "decode_wide64 M=64 K=4096 N=14336 fp32 Y, 128x64 tiles (rows past 64 repeat row 63), "
+     "W from HBM", (0, 2)),
+    ("gemm_mxfp4_ring_skinny<false, Tile<64, 4, 2, 128, 3>>", 114688, "gemm_mxfp4_ring_skinny@decode_wide128",
+     "gemm_mxfp4_ring.hip", "decode_wide128 M=128 K=4096 N=14336 fp32 Y, 128x64 tiles, W from HBM", (1, 2)),
+    ("gemm_nvfp4_ring_skinny<false, Tile<64, 4, 2, 128, 2>>", 114688, "gemm_nvfp4_ring_skinny@decode_nv_wide128",
      "gemm_nvfp4_ring.hip", "decode_nv_wide128 M=128 K=4096 N=14336 NVFP4 block 16 fp32 Y, 128x64 tiles, W from HBM"),
     ("gemm_nvfp4_decode<false, 2, 1>", 229376, "gemm_nvfp4_decode@decode_nv_wide", "gemm_decode.hip",
      "decode_nv_wide M in {1,16} K=4096 N=14336 NVFP4 block 16 fp32 Y, two 16-row tiles per workgroup, W from HBM"),
@@ -124,6 +127,22 @@ def _grid(r):
 def _name(r):
     n = r["Kernel_Name"].replace("void ", "").replace("fp4::(anonymous namespace)::", "")
     return n.split("(")[0].strip().replace("> >", ">>")
+
+
+def split_runs(d, counter, kern, runs):
+    """Means per dispatch of one counter for the launches of kern = (kernel, grid), split into `runs`
+    groups at the runs - 1 widest gaps between their dispatch ids (bench rows that use the same
+    kernel and grid run one after the other, with other launches between them); [(mean, count)]."""
+    per_dispatch = {}
+    for r in _rows(os.path.join(d, "**", "*counter_collection.csv")):
+        if r["Counter_Name"] != counter or (_name(r), _grid(r)) != kern:
+            continue
+        i = int(r.get("Dispatch_Id", r.get("Correlation_Id")))
+        per_dispatch[i] = per_dispatch.get(i, 0.0) + float(r["Counter_Value"])
+    ids = sorted(per_dispatch)
+    cuts = sorted(sorted(range(1, len(ids)), key=lambda j: ids[j] - ids[j - 1])[-(runs - 1):]) if runs > 1 else []
+    bounds = [0] + cuts + [len(ids)]
+    return [(statistics.fmean(per_dispatch[i] for i in ids[a:b]), b - a) for a, b in zip(bounds, bounds[1:])]
 
 
 def counter_means(d, counter):
@@ -199,14 +218,18 @@ def _summarize_trace_and_traffic(out, cmds):
                          "each scaled by the same counter's reading for a plain 256 MiB device copy; valid only while "
                          "the hash of the kernel source and the shared headers matches (bench_profiles.py)",
              "copy_scale_fetch": sf, "copy_scale_write": sw}
-    for n, g, key, src, wl in TRAFFIC_MAP:
+    for n, g, key, src, wl, *part in TRAFFIC_MAP:
         if (n, g) not in fetch or (n, g) not in write:
             print(f"warning: no counters for {n} grid {g} ({key})", file=sys.stderr)
             continue
-        rb, wb = fetch[(n, g)][0] * 1024 * sf, write[(n, g)][0] * 1024 * sw
+        (fv, fc), (wv, _) = fetch[(n, g)], write[(n, g)]
+        if part:
+            run, runs = part[0]
+            (fv, fc), (wv, _) = (split_runs(os.path.join(out, "fetch"), "FETCH_SIZE", (n, g), runs)[run],
+                                 split_runs(os.path.join(out, "write"), "WRITE_SIZE", (n, g), runs)[run])
+        rb, wb = fv * 1024 * sf, wv * 1024 * sw
         table[key] = {"workload": wl, "kernel": n, "grid": g, "source_sha": bench.source_sha(src),
-                      "bytes_per_launch": rb + wb, "read_bytes": rb, "write_bytes": wb,
-                      "dispatches": fetch[(n, g)][1]}
+                      "bytes_per_launch": rb + wb, "read_bytes": rb, "write_bytes": wb, "dispatches": fc}
     with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
         json.dump(table, f, indent=1)
         f.write("\n")

@@ -211,10 +211,10 @@ hipError_t fp4_launch_gemm_mxfp4(const uint8_t* Xq, const uint8_t* Xs, const uin
   // pointers aligned to 16 bytes (K % 512 == 0 keeps every row aligned then); the general kernel
   // below reads 4-byte words and takes any 4-byte-aligned pair.
   const bool scales16 = ((reinterpret_cast<uintptr_t>(Xs) | reinterpret_cast<uintptr_t>(Ws)) & 15) == 0;
-  if (scales16 && fp4_gemm_mxfp4_decode_fits(M, N, K))
+  const bool ring = scales16 && fp4_gemm_mxfp4_ring_fits(M, N, K);
+  if (scales16 && !(ring && M > 32) && fp4_gemm_mxfp4_decode_fits(M, N, K))
     return fp4_launch_gemm_mxfp4_decode(Xq, Xs, Wq, Ws, M, N, K, Y, out_bf16, st);
-  if (scales16 && fp4_gemm_mxfp4_ring_fits(M, N, K))
-    return fp4_launch_gemm_mxfp4_ring(Xq, Xs, Wq, Ws, M, N, K, Y, out_bf16, st);
+  if (ring) return fp4_launch_gemm_mxfp4_ring(Xq, Xs, Wq, Ws, M, N, K, Y, out_bf16, st);
   // 128x128 tiles on 4 waves; when they would give fewer than two workgroups per CU (as for 65 to
   // 255 tokens against one layer), 64x64 tiles on 4 waves: four times the workgroups streaming W
   // (at N = 14336, K = 4096: 1.3-1.5x faster from 65 to 192 tokens, 1.06x at 255).

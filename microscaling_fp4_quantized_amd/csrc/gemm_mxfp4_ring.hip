@@ -10,14 +10,15 @@
 //    elements (one MXFP4 group) of row l % 32 and that group's E8M0 byte.
 //  * 8 waves (2 per SIMD). The 256x256 tile uses a 2 x 4 wave layout, 128 x 64 outputs per
 //    wave (128 accumulators), so one wave's LDS reads overlap the other wave's MFMAs.
-//  * K advances in stages of 256 elements (128 bytes per row). A 2-deep LDS ring is filled
+//  * K advances in stages of 256 elements (128 bytes per row). A 2-deep LDS ring (3-deep for the
+//    one-row-tile grids below) is filled
 //    with buffer_load_dwordx4 ... lds (LDS DMA, no register staging; the stage's offset in the
 //    scalar offset field); 16-byte chunks of a row are XOR-swizzled by the row's low five bits
 //    so the 32 rows of a fragment read hit distinct banks. The buffer form, not
 //    global_load_lds: the compiler counts a pending FLAT-encoded DMA as a possible LDS access
 //    and so waits for every LDS read (lgkmcnt(0)) before each MFMA group while one is in
 //    flight; with the buffer form it waits only for the fragments the MFMAs use.
-//  * LDS holds the A rows of both stages, then the B rows, then the scales: every fragment
+//  * LDS holds the A rows of the ring's stages, then the B rows, then the scales: every fragment
 //    read is one of four per-lane offsets (per k-step) plus the stage's base and an immediate,
 //    and the loop carries about a dozen VALU instructions per stage (which compete with the
 //    MFMAs for issue cycles on gfx950).
@@ -36,8 +37,11 @@
 //    workgroups part-filled, the columns left after whole rounds of 256-wide tiles are
 //    covered by 256x192 tiles (4 x 2 waves of 64 x 96), each about 0.78 of a wide tile's
 //    time, so the last round is full of cheaper tiles.
-//  * Fewer than 256 rows of X (and N >= 1024): one row tile of 64-column tiles (128 x 64 up to
-//    128 rows, 256 x 64 above), so that enough workgroups stream W; rows past M repeat row M-1.
+//  * Fewer than 256 rows of X (and N >= 1024; 33-64 rows from N >= 8192): one row tile of
+//    64-column tiles (128 x 64 up to 128 rows, 256 x 64 above), so that enough workgroups stream
+//    W; rows past M repeat row M-1. A stage then holds few MFMAs per wave, so their ring is 3
+//    deep: the DMA of stage s + 2 is issued while stage s is multiplied (from HBM at N = 14336,
+//    K = 4096: 128 rows 13.8 against 17.4 us with 2 deep; 4 or 5 deep measured no faster).
 // Requires K % 512 == 0 (whole scale groups) and K < 2^25 (32-bit buffer offsets); other
 // shapes use the general kernel.
 #include <atomic>
@@ -55,13 +59,15 @@ constexpr int BM = 256;                  // workgroup tile rows (both widths)
 constexpr int WAVES = 8, NT = WAVES * 64;
 constexpr int BKB = 128;                 // bytes of K per row per stage (256 elements)
 constexpr int KSTEPS = 4;                // 32x32x64 steps per stage
-constexpr int NS = 2;                    // ring depth
-constexpr int LDS_BYTES = NS * (BM + 256) * BKB + 2 * (BM + 256) * 16;  // sized for the wide tile: 144 KB
+constexpr int LDS_BYTES = 2 * (BM + 256) * BKB + 2 * (BM + 256) * 16;  // the wide tile's 2-deep ring: 144 KB
 
-// One tile shape: BM_ rows, BN columns, WGM x WGN waves.
-template <int BN_, int WGM_, int WGN_, int BM_ = BM>
+// One tile shape: BM_ rows, BN columns, WGM x WGN waves, an NS_-deep ring of stages. The DMA of
+// stage s + NS - 1 is issued while stage s is multiplied; the scale bytes come 16 per row for a
+// pair of stages, in SCP pair buffers (pair j + SCP is fetched with stage 2 j + 2 SCP, during
+// stage 2 j + 2 SCP - NS + 1, which must come after every read of stage 2 j + 1).
+template <int BN_, int WGM_, int WGN_, int BM_ = BM, int NS_ = 2>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, NS = NS_, SCP = NS_ / 2 + 1;
   static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
   static constexpr int STAGE = (BM + BN) * BKB;
   static constexpr int A_WL = BM / 8 / WAVES, B_WL = BN / 8 / WAVES;  // 1 KB DMA wave-loads per wave
@@ -69,20 +75,24 @@ struct Tile {
   static constexpr int SC_LOADS = (BM + BN) / 64;                      // 64-row scale wave-loads
   static constexpr int SC_WL = (SC_LOADS + WAVES - 1) / WAVES;
   static constexpr int EP = WN * 4 + 16;                               // epilogue row pitch (bytes)
+  static constexpr int RING = NS * STAGE + SCP * SC_BYTES;
   static_assert(WGM * WGN == WAVES, "wave layout");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "whole 32x32 fragments");
   static_assert(A_WL * 8 * WAVES == BM && B_WL * 8 * WAVES == BN, "row split");
   static_assert(SC_LOADS * 64 == BM + BN, "scale split");
-  static_assert(NS * STAGE + 2 * SC_BYTES <= LDS_BYTES, "ring fits");
+  static_assert(NS >= 2 && 2 * SCP >= NS + 1, "scale pair buffers outlive their reads");
+  static_assert(NS == 2 || SC_WL == 1, "at most one scale wave-load per wave (the wait counts assume it)");
+  static_assert(RING <= LDS_BYTES, "ring fits");
   static_assert(WAVES * 32 * EP <= LDS_BYTES, "epilogue staging fits");
 };
 using Wide = Tile<256, 2, 4>;
 using Narrow = Tile<192, 4, 2>;
-using Skinny = Tile<64, 8, 1>;  // 129-255 rows: 256 x 64 tiles, 8 waves of 32 x 64
-using Skinny128 = Tile<64, 4, 2, 128>;  // 65-128 rows: 128 x 64 tiles, 8 waves of 32 x 32
+// Below 256 rows a stage holds few MFMAs per wave, so a deeper ring keeps more stages in flight.
+using Skinny = Tile<64, 8, 1, 256, 3>;     // 129-255 rows: 256 x 64 tiles, 8 waves of 32 x 64
+using Skinny128 = Tile<64, 4, 2, 128, 3>;  // 33-128 rows: 128 x 64 tiles, 8 waves of 32 x 32
 template <class C>
 constexpr int lds_need() {  // the ring and scale buffers, or the epilogue staging if larger
-  return NS * C::STAGE + 2 * C::SC_BYTES > WAVES * 32 * C::EP ? NS * C::STAGE + 2 * C::SC_BYTES : WAVES * 32 * C::EP;
+  return C::RING > WAVES * 32 * C::EP ? C::RING : WAVES * 32 * C::EP;
 }
 constexpr float kNarrowCost = 0.78f;  // measured time of a 256x192 tile over a 256x256 one (MXFP4)
 
@@ -127,8 +137,12 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
   constexpr int BM = C::BM;
   constexpr int WGN = C::WGN, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
   constexpr int STAGE = C::STAGE, A_WL = C::A_WL, B_WL = C::B_WL, SC_BYTES = C::SC_BYTES, SC_WL = C::SC_WL;
-  // LDS: the A rows of both stages, then the B rows of both stages, then the scale buffers,
-  // so that a fragment read is a per-lane offset of the stage plus an immediate.
+  constexpr int NS = C::NS, SCP = C::SCP, D = NS - 1;  // D: stages fetched ahead
+  // ring slot of stage s, and scale pair buffer of stage s
+  auto slot = [](int s) { return NS == 2 ? (s & 1) : (int)((unsigned)s % NS); };
+  auto pair = [](int s) { return SCP == 2 ? ((s >> 1) & 1) : (int)(((unsigned)s >> 1) % SCP); };
+  // LDS: the A rows of the NS stages, then their B rows, then the scale buffers, so that a
+  // fragment read is a per-lane offset of the stage plus an immediate.
   constexpr int A_ST = BM * BKB, B_ST = C::BN * BKB, B_BASE = NS * A_ST;
   uint8_t* scl = smem + NS * STAGE;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -170,7 +184,7 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
   // nine loads while it could be issuing MFMAs.
   auto issue_part = [&](int s, int p) {
     if (p == 0 && (s & 1) == 0) {
-      uint8_t* dst = scl + ((s >> 1) & 1) * SC_BYTES;
+      uint8_t* dst = scl + pair(s) * SC_BYTES;
 #pragma unroll
       for (int i = 0; i < SC_WL; ++i)
         if (wave * SC_WL + i < C::SC_LOADS)
@@ -178,8 +192,8 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
                                                    (lds_void*)(dst + (wave * SC_WL + i) * 1024), 16,
                                                    offS[i], (unsigned)(s >> 1) * 16, 0, 0);
     }
-    uint8_t* bufa = smem + (s & 1) * A_ST;
-    uint8_t* bufb = smem + B_BASE + (s & 1) * B_ST;
+    uint8_t* bufa = smem + slot(s) * A_ST;
+    uint8_t* bufb = smem + B_BASE + slot(s) * B_ST;
 #pragma unroll
     for (int i = 0; i < A_WL; ++i)
       if (i % KSTEPS == p)
@@ -209,20 +223,33 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
   for (int ks = 0; ks < KSTEPS; ++ks) cx[ks] = ((ks + 4 * fh) ^ swz(fr)) << 4;
 
   // Stage s: wait for its DMA (this wave's, then everyone's at the barrier), then multiply it
-  // while the parts of stage s+1 refill the buffer of stage s-1, which every wave has finished
-  // reading once past the barrier. The last stage is peeled off so that the loop body issues
+  // while the parts of stage s+D refill the buffer of stage s-1, which every wave has finished
+  // reading once past the barrier. The last D stages are peeled off so that the loop body issues
   // its DMA unconditionally (a per-k-step condition makes the compiler wait on the DMA before
   // every LDS read).
+  // This wave's loads still allowed in flight at the top of a stage s with s + D < nst: those of
+  // stages s+1 .. s+D-1, i.e. A_WL + B_WL each, plus the scale load on the even ones if the wave
+  // issues one (of D-1 consecutive stages from s+1, D/2 are even if s+1 is, else (D-1)/2).
+  auto wait_stage = [&](int s, auto with_dma) {
+    constexpr int L = (D - 1) * (A_WL + B_WL);
+    if constexpr (!decltype(with_dma)::value || D == 1) {
+      wait_vmcnt<0>();
+    } else {
+      if (wave >= C::SC_LOADS) wait_vmcnt<L>();
+      else if (s & 1) wait_vmcnt<L + D / 2>();
+      else wait_vmcnt<L + (D - 1) / 2>();
+    }
+  };
   auto run_stage = [&](int s, auto with_dma) {
-    wait_vmcnt<0>();
+    wait_stage(s, with_dma);
     ring_barrier();
-    const int sl = s & 1;
+    const int sl = slot(s);
     const int la = ra + sl * A_ST, lb = rb + sl * B_ST;
-    // the lane half's 4 scale bytes of the stage (pair buffer (s >> 1) & 1, bytes 8 sl + 4 h ..
-    // + 3 of the row's 16): byte ks goes with k-step ks
+    // the lane half's 4 scale bytes of the stage (pair buffer (s >> 1) % SCP, bytes 8 (s & 1) +
+    // 4 h .. + 3 of the row's 16): byte ks goes with k-step ks
     unsigned sg_a[FM], sg_b[FN];
     {
-      const uint8_t* sbuf = scl + ((s >> 1) & 1) * SC_BYTES + 8 * sl + 4 * fh;
+      const uint8_t* sbuf = scl + pair(s) * SC_BYTES + 8 * (s & 1) + 4 * fh;
 #pragma unroll
       for (int i = 0; i < FM; ++i) sg_a[i] = *reinterpret_cast<const unsigned*>(sbuf + (wm0 + i * 32 + fr) * 16);
 #pragma unroll
@@ -230,7 +257,7 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
     }
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      if constexpr (decltype(with_dma)::value) issue_part(s + 1, ks);
+      if constexpr (decltype(with_dma)::value) issue_part(s + D, ks);
       v4u a[FM], b[FN];
       const int oa = la + cx[ks], ob = lb + cx[ks];
 #pragma unroll
@@ -253,10 +280,19 @@ __device__ __forceinline__ void ring_tile(uint8_t* smem, const uint8_t* __restri
       }
     }
   };
+  if constexpr (D == 1) {
 #pragma unroll
-  for (int p = 0; p < KSTEPS; ++p) issue_part(0, p);
-  for (int s = 0; s + 1 < nst; ++s) run_stage(s, std::true_type{});
-  run_stage(nst - 1, std::false_type{});
+    for (int p = 0; p < KSTEPS; ++p) issue_part(0, p);
+    for (int s = 0; s + 1 < nst; ++s) run_stage(s, std::true_type{});
+    run_stage(nst - 1, std::false_type{});
+  } else {
+    for (int t = 0; t < D && t < nst; ++t)
+#pragma unroll
+      for (int p = 0; p < KSTEPS; ++p) issue_part(t, p);
+    int s = 0;
+    for (; s + D < nst; ++s) run_stage(s, std::true_type{});
+    for (; s < nst; ++s) run_stage(s, std::false_type{});
+  }
 
   // Epilogue: each wave stages one 32 x WN slab at a time in its own LDS region, then writes
   // whole 16-byte pieces of its rows, 64 per wave instruction: 4 float32 values per piece, or
@@ -422,8 +458,14 @@ hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const
 }  // namespace
 }  // namespace fp4
 
+// 33-64 rows take the 128-row tiles only on layers of at least this many columns: there the
+// one-row-tile grid has 128+ workgroups and beats the weight-streaming decode kernel (N = 8192,
+// 64 rows: 11.0 against 14.0 us; N = 14336: 11.7 against 16.2 us), while at N = 4096 its 64
+// workgroups lose (10.2 against 7.0 us at 40 rows).
+static constexpr int64_t kMidN = 8192;
 bool fp4_gemm_mxfp4_ring_fits(int64_t M, int64_t N, int64_t K) {
-  return K % 512 == 0 && K < ((int64_t)1 << 25) && ((M >= 256 && N >= 256) || (M > 64 && N >= 1024));
+  return K % 512 == 0 && K < ((int64_t)1 << 25) &&
+         ((M >= 256 && N >= 256) || (M > 64 && N >= 1024) || (M > 32 && N >= kMidN));
 }
 
 hipError_t fp4_launch_gemm_mxfp4_ring(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,

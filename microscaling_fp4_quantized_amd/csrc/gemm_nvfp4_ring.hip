@@ -55,13 +55,13 @@ constexpr int WAVES = 8, NT = WAVES * 64;
 constexpr int BKB = 128;                 // code bytes of a row per stage (256 elements)
 constexpr int SCB = 16;                  // E4M3 bytes of a row per stage (16 groups of 16)
 constexpr int KBLK = 4;                  // 64-element blocks per stage (one DMA part each)
-constexpr int NS = 2;                    // ring depth
-constexpr int LDS_BYTES = NS * (BM + 256) * (BKB + SCB);  // sized for the wide tile: 144 KB
+constexpr int LDS_BYTES = 2 * (BM + 256) * (BKB + SCB);  // the wide tile's 2-deep ring: 144 KB
 
-// One tile shape: BM_ rows, BN columns, WGM x WGN waves.
-template <int BN_, int WGM_, int WGN_, int BM_ = BM>
+// One tile shape: BM_ rows, BN columns, WGM x WGN waves, an NS_-deep ring of stages (the DMA of
+// stage s + NS - 1 is issued while stage s is multiplied).
+template <int BN_, int WGM_, int WGN_, int BM_ = BM, int NS_ = 2>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, NS = NS_;
   static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
   static constexpr int STAGE = (BM + BN) * BKB;                   // codes of one stage
   static constexpr int SC = (BM + BN) * SCB;                      // scales of one stage
@@ -73,7 +73,8 @@ struct Tile {
   static_assert(WM % 32 == 0 && WN % 32 == 0, "whole 32x32 fragments");
   static_assert(A_WL * 8 * WAVES == BM && B_WL * 8 * WAVES == BN, "row split");
   static_assert(SC_LOADS * 64 == BM + BN, "scale split");
-  static_assert(NS * (STAGE + SC) <= LDS_BYTES, "ring fits");
+  static_assert(NS >= 2 && NS * (STAGE + SC) <= LDS_BYTES, "ring fits");
+  static_assert(NS == 2 || SC_WL == 1, "at most one scale wave-load per wave (the wait counts assume it)");
   static_assert(WAVES * 32 * EP <= LDS_BYTES, "epilogue staging fits");
 };
 using Wide = Tile<256, 2, 4>;
@@ -82,7 +83,7 @@ using Skinny = Tile<64, 8, 1>;  // 129-255 rows: 256 x 64 tiles, 8 waves of 32 x
 using Skinny128 = Tile<64, 4, 2, 128>;  // 65-128 rows: 128 x 64 tiles, 8 waves of 32 x 32
 template <class C>
 constexpr int lds_need() {  // the ring and scale buffers, or the epilogue staging if larger
-  return NS * (C::STAGE + C::SC) > WAVES * 32 * C::EP ? NS * (C::STAGE + C::SC) : WAVES * 32 * C::EP;
+  return C::NS * (C::STAGE + C::SC) > WAVES * 32 * C::EP ? C::NS * (C::STAGE + C::SC) : WAVES * 32 * C::EP;
 }
 constexpr float kNvNarrowCost = 0.84f;  // measured time of a 256x192 tile over a 256x256 one
 
@@ -141,8 +142,9 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
   constexpr int BM = C::BM;
   constexpr int WGN = C::WGN, WM = C::WM, WN = C::WN, FM = C::FM, FN = C::FN;
   constexpr int STAGE = C::STAGE, SC = C::SC, A_WL = C::A_WL, B_WL = C::B_WL, SC_WL = C::SC_WL;
-  // LDS: the A rows of both stages, then the B rows of both stages, then the scale buffers,
-  // so that a fragment read is a per-lane offset of the stage plus an immediate.
+  constexpr int NS = C::NS, D = NS - 1;  // D: stages fetched ahead
+  // LDS: the A rows of the NS stages, then their B rows, then the scale buffers, so that a
+  // fragment read is a per-lane offset of the stage plus an immediate.
   constexpr int A_ST = BM * BKB, B_ST = C::BN * BKB, B_BASE = NS * A_ST;
   uint8_t* scl = smem + NS * STAGE;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -180,7 +182,7 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
   // stage's scales (16 bytes per row) with part 0.
   auto issue_part = [&](int s, int p) {
     if (p == 0) {
-      uint8_t* dst = scl + (s & 1) * SC;
+      uint8_t* dst = scl + ((unsigned)s % NS) * SC;
 #pragma unroll
       for (int i = 0; i < SC_WL; ++i)
         if (wave * SC_WL + i < C::SC_LOADS)
@@ -188,8 +190,8 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
                                                    (lds_void*)(dst + (wave * SC_WL + i) * 1024), 16,
                                                    offS[i], (unsigned)s * SCB, 0, 0);
     }
-    uint8_t* bufa = smem + (s & 1) * A_ST;
-    uint8_t* bufb = smem + B_BASE + (s & 1) * B_ST;
+    uint8_t* bufa = smem + ((unsigned)s % NS) * A_ST;
+    uint8_t* bufb = smem + B_BASE + ((unsigned)s % NS) * B_ST;
 #pragma unroll
     for (int i = 0; i < A_WL; ++i)
       if (i % KBLK == p)
@@ -220,14 +222,19 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
   const unsigned psel = fh ? 0x07060302u : 0x05040100u;  // bytes 2h, 2h + 1 of two dwords
 
   // Stage s: wait for its DMA (this wave's, then everyone's at the barrier), then multiply it
-  // while the parts of stage s+1 refill the buffers of stage s-1, which every wave has finished
-  // reading once past the barrier. The last stage is peeled off so that the loop body issues its
-  // DMA unconditionally.
+  // while the parts of stage s+D refill the buffers of stage s-1, which every wave has finished
+  // reading once past the barrier. The last D stages are peeled off so that the loop body issues
+  // its DMA unconditionally. At the top of a stage s with s + D < nst this wave may still have the
+  // loads of stages s+1 .. s+D-1 in flight: A_WL + B_WL each, plus its scale load if it has one.
+  constexpr int LW = A_WL + B_WL;
+  const bool has_sc = wave < C::SC_LOADS;
   auto run_stage = [&](int s, auto with_dma) {
-    wait_vmcnt<0>();
+    if constexpr (!decltype(with_dma)::value || D == 1) wait_vmcnt<0>();
+    else if (has_sc) wait_vmcnt<(D - 1) * (LW + 1)>();
+    else wait_vmcnt<(D - 1) * LW>();
     ring_barrier();
-    const int la = ra + (s & 1) * A_ST, lb = rb + (s & 1) * B_ST;
-    const uint8_t* sbuf = scl + (s & 1) * SC;
+    const int la = ra + ((unsigned)s % NS) * A_ST, lb = rb + ((unsigned)s % NS) * B_ST;
+    const uint8_t* sbuf = scl + ((unsigned)s % NS) * SC;
     // the lane's scale bytes of the stage: of each block's four (one dword), the two of its lane
     // half, gathered as word kb % 2 of dword kb / 2
     unsigned sg_a[FM][2], sg_b[FN][2];
@@ -245,7 +252,7 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
     }
 #pragma unroll
     for (int kb = 0; kb < KBLK; ++kb) {
-      if constexpr (decltype(with_dma)::value) issue_part(s + 1, kb);
+      if constexpr (decltype(with_dma)::value) issue_part(s + D, kb);
       // 16-byte chunk 2 kb + h of the row: elements 32h .. 32h + 31 of block kb
       v4u ca[FM], cb[FN];
       const int oa = la + cx[kb], ob = lb + cx[kb];
@@ -278,10 +285,19 @@ __device__ __forceinline__ void nv_tile(uint8_t* smem, const uint8_t* __restrict
       }
     }
   };
+  if constexpr (D == 1) {
 #pragma unroll
-  for (int p = 0; p < KBLK; ++p) issue_part(0, p);
-  for (int s = 0; s + 1 < nst; ++s) run_stage(s, std::true_type{});
-  run_stage(nst - 1, std::false_type{});
+    for (int p = 0; p < KBLK; ++p) issue_part(0, p);
+    for (int s = 0; s + 1 < nst; ++s) run_stage(s, std::true_type{});
+    run_stage(nst - 1, std::false_type{});
+  } else {
+    for (int t = 0; t < D && t < nst; ++t)
+#pragma unroll
+      for (int p = 0; p < KBLK; ++p) issue_part(t, p);
+    int s = 0;
+    for (; s + D < nst; ++s) run_stage(s, std::true_type{});
+    for (; s < nst; ++s) run_stage(s, std::false_type{});
+  }
 
   // acc[i][j][4q + r] = Y[m][n + r] with m = wm0 + 32 i + l % 32, n = wn0 + 32 j + 8 q + 4 (l / 32).
   // Epilogue: each wave stages one 32 x WN slab of float32 at a time in its own region of the

@@ -37,7 +37,7 @@ def test_committed_traffic_is_current():
 
     table = load("traffic.json")
     assert len(bench_profiles.TRAFFIC_MAP) >= 10
-    for kernel, grid, key, src, _ in bench_profiles.TRAFFIC_MAP:
+    for kernel, grid, key, src, *_ in bench_profiles.TRAFFIC_MAP:
         assert key in table, key
         e = table[key]
         assert (e["kernel"], e["grid"]) == (kernel, grid)
@@ -51,7 +51,7 @@ def test_bench_traffic_lookups_are_in_the_map():
     # the literal keys bench.py looks up are ones the profiling pipeline measures
     import bench_profiles
 
-    keys = {k for _, _, k, _, _ in bench_profiles.TRAFFIC_MAP}
+    keys = {e[2] for e in bench_profiles.TRAFFIC_MAP}
     with open(os.path.join(ROOT, "bench.py")) as f:
         lits = re.findall(r'measured_traffic\("([\w@]+)",', f.read())
     assert len(lits) >= 6
@@ -59,21 +59,22 @@ def test_bench_traffic_lookups_are_in_the_map():
     assert {"gemm_mxfp4_ring@prefill_mx", "rotate_quant_mx@stress_mx32", "gemm_mxfp4_decode@decode",
             "gemm_mxfp4_decode@decode_wide"} <= keys
     # the decode rows' table: every key measured, on the source it names
-    srcs = {k: src for _, _, k, src, _ in bench_profiles.TRAFFIC_MAP}
+    srcs = {e[2]: e[3] for e in bench_profiles.TRAFFIC_MAP}
     for name, (key, src) in bench.DECODE_TRAFFIC_KEY.items():
         assert srcs.get(key) == src, (name, key, src)
 
 
 def test_roofline_kernel_follows_the_library_dispatch():
     # the kernel fp4_linear runs for each workload (16-byte-aligned scales): decode kernel for M <= 16
-    # with K % 512 == 0 (up to 64 rows when K <= 8192), the 256-row-tile kernels for M, N >= 256, the
-    # general kernels otherwise
+    # with K % 512 == 0 (up to 64 rows when K <= 8192, except MXFP4 with 33-64 rows against N >= 8192,
+    # which takes the 128-row ring tiles), the 256-row-tile kernels for M, N >= 256, the general
+    # kernels otherwise
     from microscaling_fp4_quantized_amd import workloads as WL
 
     want = {"tiny": "gemm_mxfp4_kernel", "decode1": "gemm_mxfp4_decode", "decode4": "gemm_mxfp4_decode",
             "decode16": "gemm_mxfp4_decode", "decode_wide1": "gemm_mxfp4_decode",
             "decode_wide4": "gemm_mxfp4_decode", "decode_wide16": "gemm_mxfp4_decode",
-            "decode_wide32": "gemm_mxfp4_decode", "decode_wide64": "gemm_mxfp4_decode",
+            "decode_wide32": "gemm_mxfp4_decode", "decode_wide64": "gemm_mxfp4_ring_skinny",
             "decode_nv_wide1": "gemm_nvfp4_decode", "decode_nv_wide16": "gemm_nvfp4_decode",
             "decode_nv_wide64": "gemm_nvfp4_decode", "decode_wide128": "gemm_mxfp4_ring_skinny",
             "decode_nv_wide128": "gemm_nvfp4_ring_skinny",
@@ -88,6 +89,11 @@ def test_roofline_kernel_follows_the_library_dispatch():
     assert bench.gemm_kernel_for("mxfp4", 16, 4096, 4224)[1] == "gemm_mxfp4_kernel"   # K % 512 != 0
     assert bench.gemm_kernel_for("mxfp4", 17, 4096, 4096)[1] == "gemm_mxfp4_decode"   # up to 64 tokens
     assert bench.gemm_kernel_for("mxfp4", 64, 4096, 8192)[1] == "gemm_mxfp4_decode"
+    assert bench.gemm_kernel_for("mxfp4", 64, 8191, 4096)[1] == "gemm_mxfp4_decode"
+    assert bench.gemm_kernel_for("mxfp4", 33, 8192, 4096)[1] == "gemm_mxfp4_ring_skinny"  # 128 x 64 tiles
+    assert bench.gemm_kernel_for("mxfp4", 32, 14336, 4096)[1] == "gemm_mxfp4_decode"
+    assert bench.gemm_kernel_for("mxfp4", 48, 14336, 8704)[1] == "gemm_mxfp4_ring_skinny"
+    assert bench.gemm_kernel_for("nvfp4", 48, 14336, 4096)[1] == "gemm_nvfp4_decode"
     assert bench.gemm_kernel_for("mxfp4", 64, 4096, 8704)[1] == "gemm_mxfp4_kernel"   # K past the slices
     assert bench.gemm_kernel_for("mxfp4", 65, 4096, 4096)[1] == "gemm_mxfp4_ring_skinny"  # 256 x 64 tiles
     assert bench.gemm_kernel_for("mxfp4", 65, 1000, 4096)[1] == "gemm_mxfp4_kernel"   # too few columns
@@ -99,6 +105,23 @@ def test_roofline_kernel_follows_the_library_dispatch():
     assert bench.gemm_kernel_for("nvfp4", 256, 256, 256)[1] == "gemm_nvfp4_ring"
     assert bench.gemm_kernel_for("nvfp4", 256, 256, 384)[1] == "gemm_nvfp4_kernel"    # K % 256 != 0
     assert bench.gemm_kernel_for("mxfp4", 16, 4096, 1 << 28)[1] == "gemm_mxfp4_kernel"  # K past the decode bound
+
+
+def test_split_runs_separates_consecutive_rows(tmp_path):
+    # two bench rows launch the same kernel and grid one after the other, with other launches
+    # between them: the counter values of each row come back separately, in order
+    import bench_profiles
+
+    d = tmp_path / "fetch"
+    d.mkdir()
+    rows = [(i, "k<1>", 512, 10.0) for i in (3, 4, 6, 7)] + [(i, "k<1>", 512, 30.0) for i in (40, 41, 43)] + \
+        [(5, "other", 512, 99.0), (20, "k<1>", 1024, 7.0)]
+    with open(d / "run_counter_collection.csv", "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n")
+        for i, n, g, v in rows:
+            f.write(f"{i},{n},{g},FETCH_SIZE,{v}\n")
+    assert bench_profiles.split_runs(str(d), "FETCH_SIZE", ("k<1>", 512), 2) == [(10.0, 4), (30.0, 3)]
+    assert bench_profiles.split_runs(str(d), "FETCH_SIZE", ("k<1>", 512), 1) == [(pytest.approx(130 / 7), 7)]
 
 
 def test_committed_bench_line_contract():

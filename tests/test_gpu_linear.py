@@ -71,15 +71,16 @@ def test_decode_kernel_unit_scales_exact(M, N, K):
     assert np.array_equal(host(yb.float()).astype(np.float64), O.bf16_rne_f64(ref))
 
 
-@pytest.mark.parametrize("M,N,K", [(17, 300, 512), (32, 4096, 4096), (33, 12300, 1024), (48, 777, 8192),
-                                   (64, 12289, 4096), (63, 4100, 8192), (64, 16, 2560), (40, 20, 1536),
-                                   (65, 300, 1024)])
+@pytest.mark.parametrize("M,N,K", [(17, 300, 512), (32, 4096, 4096), (32, 12300, 1024), (33, 8000, 1024),
+                                   (48, 777, 8192), (64, 8191, 4096), (63, 4100, 8192), (64, 16, 2560),
+                                   (40, 20, 1536), (65, 300, 1024)])
 def test_decode_kernel_up_to_64_tokens_unit_scales_exact(M, N, K):
     # 16 < M <= 64 with K % 512 == 0 and K <= 8192 runs the decode kernel with ceil(M / 16) column
-    # fragments of X per W fragment (17, 33: one and two rows into the last fragment; 48, 63, 64:
-    # three and four fragments); N >= 3 * 16 * 256 with K <= 4096 puts two tiles in a workgroup
-    # (12300, 12289: ragged last workgroup), K = 8192 gives each wave two slices with one tile,
-    # K = 512 and 2560 leave waves idle. M = 65 takes the general kernel.
+    # fragments of X per W fragment (17, 33: one row into the last fragment; 48, 63, 64: three and
+    # four fragments), except 33-64 rows against N >= 8192, which take the 128-row ring tiles;
+    # N >= 3 * 16 * 256 with K <= 4096 puts two tiles in a workgroup (32 x 12300: ragged last
+    # workgroup), K = 8192 gives each wave two slices with one tile, K = 512 and 2560 leave waves
+    # idle. M = 65 takes the general kernel.
     rng = np.random.default_rng(5 * M + N + K)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
@@ -94,7 +95,7 @@ def test_decode_kernel_up_to_64_tokens_unit_scales_exact(M, N, K):
     assert np.array_equal(host(yb.float()).astype(np.float64), O.bf16_rne_f64(ref))
 
 
-@pytest.mark.parametrize("M,N,K", [(50, 1000, 2048), (64, 12300, 4096)])
+@pytest.mark.parametrize("M,N,K", [(50, 1000, 2048), (64, 8000, 4096), (32, 12300, 4096)])
 def test_decode_kernel_up_to_64_tokens_random_scales(M, N, K):
     rng = np.random.default_rng(M + N)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
@@ -111,12 +112,14 @@ def test_decode_kernel_up_to_64_tokens_random_scales(M, N, K):
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
 @pytest.mark.parametrize("M,N,K", [(65, 1024, 512), (100, 1100, 1536), (128, 2048, 512), (200, 3000, 4096),
-                                   (255, 14336, 1024), (129, 1030, 8192)])
+                                   (255, 14336, 1024), (129, 1030, 8192), (33, 12300, 1024), (64, 12289, 4096),
+                                   (48, 8192, 8192)])
 def test_skinny_tiles_unit_scales_exact(fmt, M, N, K):
     # 64 < M < 256 with N >= 1024 (and K % 512 == 0 for MXFP4, K % 256 == 0 for NVFP4) runs the
     # large-tile kernels on one row tile of 64-column tiles, 128 rows up to M = 128 and 256 above,
-    # whose rows past M repeat row M - 1 (N = 1100, 3000, 1030: a ragged last column tile). Unit
-    # scales make every sum exact.
+    # whose rows past M repeat row M - 1 (N = 1100, 3000, 1030, 12300, 12289: a ragged last column
+    # tile); for MXFP4 so do 33-64 rows against N >= 8192 (for NVFP4 those take the decode
+    # kernel). Unit scales make every sum exact.
     rng = np.random.default_rng(3 * M + N + K)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
@@ -134,9 +137,13 @@ def test_skinny_tiles_unit_scales_exact(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
-def test_skinny_tiles_random_scales(fmt):
-    M, N, K = 150, 2100, 2048
-    rng = np.random.default_rng(21 if fmt == "mxfp4" else 22)
+@pytest.mark.parametrize("M,N,K", [(150, 2100, 2048), (100, 1100, 4096), (128, 3000, 8192), (97, 1024, 1536),
+                                   (40, 8200, 4096)])
+def test_skinny_tiles_random_scales(fmt, M, N, K):
+    # random scales catch a stage multiplied with another stage's scale bytes, which unit scales
+    # hide: the MXFP4 tiles keep three stages in flight (K = 1536: six stages in all); 40 rows
+    # against N = 8200 take the 128-row MXFP4 tiles and the NVFP4 decode kernel
+    rng = np.random.default_rng((21 if fmt == "mxfp4" else 22) + M + K)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
     if fmt == "mxfp4":
