@@ -225,8 +225,14 @@ def _summarize_trace_and_traffic(out, cmds):
         (fv, fc), (wv, _) = fetch[(n, g)], write[(n, g)]
         if part:
             run, runs = part[0]
-            (fv, fc), (wv, _) = (split_runs(os.path.join(out, "fetch"), "FETCH_SIZE", (n, g), runs)[run],
-                                 split_runs(os.path.join(out, "write"), "WRITE_SIZE", (n, g), runs)[run])
+            fr = split_runs(os.path.join(out, "fetch"), "FETCH_SIZE", (n, g), runs)
+            wr = split_runs(os.path.join(out, "write"), "WRITE_SIZE", (n, g), runs)
+            # the rows sharing a kernel and grid launch it equally often; anything else means the
+            # widest gaps did not fall between rows (say, a row was left out of the run)
+            if len({c for _, c in fr}) != 1 or len({c for _, c in wr}) != 1:
+                print(f"warning: {key}: launches of {n} grid {g} do not split into {runs} equal rows", file=sys.stderr)
+                continue
+            (fv, fc), (wv, _) = fr[run], wr[run]
         rb, wb = fv * 1024 * sf, wv * 1024 * sw
         table[key] = {"workload": wl, "kernel": n, "grid": g, "source_sha": bench.source_sha(src),
                       "bytes_per_launch": rb + wb, "read_bytes": rb, "write_bytes": wb, "dispatches": fc}
