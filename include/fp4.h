@@ -190,8 +190,8 @@ FP4_API int fp4_quantize_weights_ex(const void *W, int64_t N, int64_t K, int64_t
  *  Xq, Wq 16-byte aligned; Xs, Ws 4-byte aligned. (With 16-byte-aligned Xs and Ws: MXFP4
  *  with K % 512 == 0 runs the weight-streaming decode kernel for M <= 16, and for M <= 64
  *  when K <= 8192, except 33 <= M <= 64 with N >= 8192, and the large-tile kernel for
- *  M, N >= 256 (K < 2^25), on one row tile of 64-column tiles for 64 < M < 256 with
- *  N >= 1024 and for those 33-64 rows; NVFP4 runs the decode kernel for M <= 64 when
+ *  M, N >= 256 (K < 2^25), on 64-column tiles (one or two row tiles) for 64 < M < 256
+ *  with N >= 1024 and for those 33-64 rows; NVFP4 runs the decode kernel for M <= 64 when
  *  K % 512 == 0 and K <= 8192, and the large-tile kernel for M, N >= 256, and for
  *  64 < M < 256 with N >= 1024, when K % 256 == 0. Other pointers or shapes run the general
  *  kernel, on 64 x 64 tiles when its 128 x 128 grid would be small.)

@@ -37,9 +37,9 @@
 //    workgroups part-filled, the columns left after whole rounds of 256-wide tiles are
 //    covered by 256x192 tiles (4 x 2 waves of 64 x 96), each about 0.78 of a wide tile's
 //    time, so the last round is full of cheaper tiles.
-//  * Fewer than 256 rows of X (and N >= 1024; 33-64 rows from N >= 8192): one row tile of
-//    64-column tiles (128 x 64 up to 128 rows, 256 x 64 above), so that enough workgroups stream
-//    W; rows past M repeat row M-1. A stage then holds few MFMAs per wave, so their ring is 3
+//  * Fewer than 256 rows of X (and N >= 1024; 33-64 rows from N >= 8192): 64-column tiles, 128 x 64
+//    up to 128 rows, 256 x 64 above (two 128 x 64 row tiles where the 256-row grid would fill at
+//    most half the CUs), so that enough workgroups stream W; rows past M repeat row M-1. A stage then holds few MFMAs per wave, so their ring is 3
 //    deep: the DMA of stage s + 2 is issued while stage s is multiplied (from HBM at N = 14336,
 //    K = 4096: 128 rows 13.8 against 17.4 us with 2 deep; 4 or 5 deep measured no faster).
 // Requires K % 512 == 0 (whole scale groups) and K < 2^25 (32-bit buffer offsets); other
@@ -446,7 +446,13 @@ hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const
     if (cached) g_cus[dev].store(cus, std::memory_order_release);
   }
   const int tiles_m = (M + BM - 1) / BM;
-  if (M <= 128) return launch_skinny<B, Skinny128>(Xq, Xs, Wq, Ws, M, N, K, Y, dev, 1, st);
+  // Below 256 rows: one 128-row tile per 64 columns up to 128 rows. Above, one 256-row tile per 64
+  // columns when that grid fills more than half the CUs, else two 128-row tiles per 64 columns
+  // (78 KB of LDS each, so two share a CU): at 129-255 rows and N = 4096 (K = 4096, W from HBM)
+  // 10.2-12.0 against 14.1-15.8 us, while at N = 14336 the 256-row tiles win (15.5-17.2 against
+  // 18.7-23.9 us).
+  if (M <= 128 || (M < BM && 2 * ((N + 63) / 64) <= cus))
+    return launch_skinny<B, Skinny128>(Xq, Xs, Wq, Ws, M, N, K, Y, dev, 1, st);
   if (M < BM) return launch_skinny<B, Skinny>(Xq, Xs, Wq, Ws, M, N, K, Y, dev, 0, st);
   int tn1, tn2;
   fp4_plan_tile_columns(tiles_m, N, cus, kNarrowCost, tn1, tn2);

@@ -113,13 +113,15 @@ def test_decode_kernel_up_to_64_tokens_random_scales(M, N, K):
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
 @pytest.mark.parametrize("M,N,K", [(65, 1024, 512), (100, 1100, 1536), (128, 2048, 512), (200, 3000, 4096),
                                    (255, 14336, 1024), (129, 1030, 8192), (33, 12300, 1024), (64, 12289, 4096),
-                                   (48, 8192, 8192)])
+                                   (48, 8192, 8192), (160, 8300, 1536), (129, 8192, 1024)])
 def test_skinny_tiles_unit_scales_exact(fmt, M, N, K):
     # 64 < M < 256 with N >= 1024 (and K % 512 == 0 for MXFP4, K % 256 == 0 for NVFP4) runs the
     # large-tile kernels on one row tile of 64-column tiles, 128 rows up to M = 128 and 256 above,
     # whose rows past M repeat row M - 1 (N = 1100, 3000, 1030, 12300, 12289: a ragged last column
     # tile); for MXFP4 so do 33-64 rows against N >= 8192 (for NVFP4 those take the decode
-    # kernel). Unit scales make every sum exact.
+    # kernel), and above 128 rows MXFP4 takes two 128-row tiles per column where the 256-row grid
+    # would fill at most half the CUs (N <= 8192 on 256 CUs; 8300 and 14336 keep 256-row tiles).
+    # Unit scales make every sum exact.
     rng = np.random.default_rng(3 * M + N + K)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
@@ -138,11 +140,12 @@ def test_skinny_tiles_unit_scales_exact(fmt, M, N, K):
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
 @pytest.mark.parametrize("M,N,K", [(150, 2100, 2048), (100, 1100, 4096), (128, 3000, 8192), (97, 1024, 1536),
-                                   (40, 8200, 4096)])
+                                   (40, 8200, 4096), (200, 9000, 2048)])
 def test_skinny_tiles_random_scales(fmt, M, N, K):
     # random scales catch a stage multiplied with another stage's scale bytes, which unit scales
     # hide: the MXFP4 tiles keep three stages in flight (K = 1536: six stages in all); 40 rows
-    # against N = 8200 take the 128-row MXFP4 tiles and the NVFP4 decode kernel
+    # against N = 8200 take the 128-row MXFP4 tiles and the NVFP4 decode kernel; 150 x 2100 two
+    # 128-row MXFP4 tiles per column, 200 x 9000 one 256-row tile
     rng = np.random.default_rng((21 if fmt == "mxfp4" else 22) + M + K)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
