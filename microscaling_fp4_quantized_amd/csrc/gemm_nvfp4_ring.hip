@@ -34,8 +34,9 @@
 //    M-fastest within groups of 8 tile rows. Two tile widths in one launch, as in the MXFP4
 //    kernel: when 256x256 tiles would leave the last round part-filled, the columns after
 //    whole rounds of them are covered by 256x192 tiles (4 x 2 waves of 64 x 96).
-//  * Fewer than 256 rows of X (and N >= 1024): one row tile of 64-column tiles (128 x 64 up to
-//    128 rows, 256 x 64 above), so that enough workgroups stream W; rows past M repeat row M-1.
+//  * Fewer than 256 rows of X (and N >= 1024): 64-column tiles, 128 x 64 up to 128 rows, 256 x 64
+//    above (two 128 x 64 row tiles where the 256-row grid would fill at most half the CUs), so
+//    that enough workgroups stream W; rows past M repeat row M-1.
 // Requires K % 256 == 0 and K < 2^25 (32-bit buffer offsets); other shapes use the general kernel.
 #include <atomic>
 #include <type_traits>
@@ -457,7 +458,11 @@ hipError_t launch(const uint8_t* Xq, const uint8_t* Xs, const float* x_ts, const
     if (cached) g_cus[dev].store(cus, std::memory_order_release);
   }
   const int tiles_m = (M + BM - 1) / BM;
-  if (M <= 128) return launch_skinny<B, Skinny128>(Xq, Xs, x_ts, Wq, Ws, w_ts, M, N, K, Y, dev, 1, st);
+  // Above 128 rows, two 128-row tiles per 64 columns where one 256-row tile per 64 columns would
+  // fill at most half the CUs: at 129-255 rows and N = 4096 (K = 4096) 25 against 35 us, while at
+  // N = 14336 the 256-row tiles win (36-38 against 44-50 us).
+  if (M <= 128 || (M < BM && 2 * ((N + 63) / 64) <= cus))
+    return launch_skinny<B, Skinny128>(Xq, Xs, x_ts, Wq, Ws, w_ts, M, N, K, Y, dev, 1, st);
   if (M < BM) return launch_skinny<B, Skinny>(Xq, Xs, x_ts, Wq, Ws, w_ts, M, N, K, Y, dev, 0, st);
   int tn1, tn2;
   fp4_plan_tile_columns(tiles_m, N, cus, kNvNarrowCost, tn1, tn2);

@@ -119,7 +119,7 @@ def test_skinny_tiles_unit_scales_exact(fmt, M, N, K):
     # large-tile kernels on one row tile of 64-column tiles, 128 rows up to M = 128 and 256 above,
     # whose rows past M repeat row M - 1 (N = 1100, 3000, 1030, 12300, 12289: a ragged last column
     # tile); for MXFP4 so do 33-64 rows against N >= 8192 (for NVFP4 those take the decode
-    # kernel), and above 128 rows MXFP4 takes two 128-row tiles per column where the 256-row grid
+    # kernel), and above 128 rows both take two 128-row tiles per column where the 256-row grid
     # would fill at most half the CUs (N <= 8192 on 256 CUs; 8300 and 14336 keep 256-row tiles).
     # Unit scales make every sum exact.
     rng = np.random.default_rng(3 * M + N + K)
@@ -145,7 +145,7 @@ def test_skinny_tiles_random_scales(fmt, M, N, K):
     # random scales catch a stage multiplied with another stage's scale bytes, which unit scales
     # hide: the MXFP4 tiles keep three stages in flight (K = 1536: six stages in all); 40 rows
     # against N = 8200 take the 128-row MXFP4 tiles and the NVFP4 decode kernel; 150 x 2100 two
-    # 128-row MXFP4 tiles per column, 200 x 9000 one 256-row tile
+    # 128-row tiles per column, 200 x 9000 one 256-row tile
     rng = np.random.default_rng((21 if fmt == "mxfp4" else 22) + M + K)
     c = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
     d = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
